@@ -1,0 +1,125 @@
+/*
+ * mxgemm.h -- C ABI of libmxgemm: small-row MXFP8 block-scaled GEMMs for the
+ * attention projections of a decode step, on AMD MI355X (gfx950).
+ *
+ * Sources ("pages") are the vLLM API documentation pages
+ *   [mxfp8]  vllm.models.deepseek_v41.nvidia.specialized_decode.attention.mxfp8
+ *   [step]   vllm.models.deepseek_v41.nvidia.specialized_decode.attention.step
+ *   [cute]   vllm.models.deepseek_v41.nvidia.ops.cute_dsl
+ *   [o_proj] vllm.models.deepseek_v41.nvidia.ops.o_proj
+ *
+ * Data formats
+ *   MXFP8 tensor  E4M3 ("FN": bias 7, max 448, no infinity) element codes, one
+ *                 byte each, row-major [rows, K], plus one UE8M0 scale byte
+ *                 (value 2^(byte-127)) per 32 consecutive K elements, row-major
+ *                 [rows, K/32].  ([mxfp8] compile_low_latency: Float8E4M3FN
+ *                 operands, Float8E8M0FNU scales, sf_vec_size 32.)
+ *   weights       "column-major [K, N]" in the pages' words ([mxfp8]
+ *                 launch_low_latency), i.e. N rows of K contiguous codes:
+ *                 w_q [N, K], w_s [N, K/32] here.
+ *   BF16          uint16_t bit patterns.  Outputs are BF16 [M, N] row-major,
+ *                 each element the FP32-accumulated sum rounded to nearest even,
+ *                 with no scale and no bias ([mxfp8] compile_low_latency).
+ *
+ * Conventions (all entry points)
+ *   - Every buffer is device memory owned by the caller; the library allocates
+ *     nothing and keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *     default stream) and the call returns without waiting for it.
+ *   - Arguments are validated on the host before anything is launched
+ *     ([cute] AllReduceMHC validates every buffer before its first launch):
+ *     on any error nothing is launched and no output is written.
+ *   - Device pointers must be 16-byte aligned, and row strides must keep every
+ *     row 16-byte aligned ([mxfp8] launch_low_latency passes 16-byte aligned
+ *     operand pointers).
+ *   - Row counts: 1 <= M <= MXG_MAX_ROWS for the GEMM entry points ([mxfp8]:
+ *     the low-latency kernel covers up to 48 rows with 16-, 32- or 48-row
+ *     activation tiles; more rows go to another kernel).
+ *   - K must be a multiple of 128 and N a multiple of 16 for the GEMMs
+ *     ([mxfp8] mxfp8_eligible requires the weight's K to be a multiple of 128).
+ *   - Inputs holding NaN/Inf (BF16), the E4M3 NaN codes 0x7F/0xFF or the
+ *     E8M0 NaN byte 0xFF are outside the contract: the results are unspecified
+ *     (the hardware propagates NaN).
+ */
+#ifndef MXGEMM_H
+#define MXGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+#define MXG_OK 0
+#define MXG_ERR_NULL 1      /* a required pointer is NULL                      */
+#define MXG_ERR_ALIGN 2     /* a pointer or row stride is not 16-byte aligned   */
+#define MXG_ERR_SHAPE 3     /* a size is out of range or sizes are inconsistent */
+#define MXG_ERR_WORKSPACE 4 /* workspace missing or smaller than required       */
+#define MXG_ERR_DEVICE 5    /* current device is not gfx950, or a launch failed */
+
+#define MXG_MAX_ROWS 48
+
+/* Human-readable text of a status code (static storage; never NULL). */
+const char *mxg_strerror(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int mxg_version(void);
+
+/*
+ * mxfp8_quantize -- BF16 -> MXFP8 ([mxfp8] pinned_mm and wide_mm quantize a
+ * BF16 input with mxfp8_e4m3_quantize; [cute] AllReduceMHC's mxfp8_out
+ * receives the layer input as MXFP8).
+ *
+ * For each row m and each 32-element block b of columns [0, K):
+ *   amax = max |x|;  e = clamp(floor(log2 amax) - 8, -127, 127), and e = -127
+ *   when amax = 0;  s[m, b] = e + 127;  q[m, k] = E4M3(x[m, k] * 2^-e), rounded
+ *   to nearest even and saturated to +-448, sign kept.
+ * (The pages do not print the scale rule; this is the benchmark's rule,
+ * 2^(floor(log2 amax) - 8), 8 being E4M3's largest exponent.)
+ *
+ *   x     BF16 [M, ld_x] (reads columns [0, K) of each row)
+ *   M     rows, >= 1 (any count: weights may be quantized with this too)
+ *   K     columns to quantize, multiple of 32
+ *   ld_x  row stride of x in elements, >= K, multiple of 8
+ *   q     out: E4M3 codes [M, K]
+ *   s     out: scale bytes [M, K/32]
+ * Codes and scales are a deterministic function of the BF16 bits.
+ */
+int mxfp8_quantize(const uint16_t *x, int64_t M, int64_t K, int64_t ld_x,
+                   uint8_t *q, uint8_t *s, void *stream);
+
+/*
+ * mxfp8_gemm -- out = dequant(a) . dequant(w)^T  ([mxfp8] launch_low_latency:
+ * out = a (rows x K) times the [K, N] weight; the kernel there computes out^T
+ * with the weight's N as its M, as this one does).  FP32 accumulation, BF16
+ * output, no scale, no bias.
+ *
+ *   M, N, K   1 <= M <= 48, N % 16 == 0, K % 128 == 0
+ *   x_bf16    NULL: a_q/a_s are inputs.  Non-NULL: BF16 [M, ld_x] activations
+ *             that the kernel quantizes itself (as mxfp8_quantize does) and
+ *             whose codes/scales it also WRITES to a_q/a_s (the pages'
+ *             wide_mm quantizes a BF16 x before its GEMM; here both run in
+ *             one launch).
+ *   ld_x      row stride of x_bf16 in elements (ignored when x_bf16 is NULL)
+ *   a_q, a_s  MXFP8 activations [M, K] / [M, K/32]
+ *   w_q, w_s  MXFP8 weights [N, K] / [N, K/32]
+ *   out       BF16 [M, N]
+ *   workspace, workspace_bytes
+ *             scratch for partial sums; mxg_gemm_workspace_bytes() gives the
+ *             size needed (0 means NULL is accepted).
+ */
+int mxfp8_gemm(int64_t M, int64_t N, int64_t K, const uint16_t *x_bf16,
+               int64_t ld_x, uint8_t *a_q, uint8_t *a_s, const uint8_t *w_q,
+               const uint8_t *w_s, uint16_t *out, void *workspace,
+               size_t workspace_bytes, void *stream);
+
+/* Workspace bytes mxfp8_gemm needs for these sizes (0: none). */
+size_t mxg_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXGEMM_H */

@@ -1,0 +1,131 @@
+"""Python binding of libmxgemm (small-row MXFP8 block-scaled GEMMs on MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libmxgemm.so``.  Tensors are torch device tensors (torch supplies memory and
+the current stream); BF16 data is ``torch.bfloat16``, E4M3 codes and UE8M0
+scale bytes are ``torch.uint8``.  The functions carry the C names of
+``include/mxgemm.h``; a non-zero status raises ``MxgError`` (a ValueError) with
+the library's message.  There is no fallback: if the shared library is missing
+the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxgemm.so")
+MAX_ROWS = 48
+
+_lib = None
+
+
+class MxgError(ValueError):
+    """A libmxgemm call returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libmxgemm status {status}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmxgemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m mxfp8_block_scaled_gemm_amd._build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        L.mxg_strerror.argtypes = [ctypes.c_int]
+        L.mxg_strerror.restype = ctypes.c_char_p
+        L.mxg_version.argtypes = []
+        L.mxg_version.restype = ctypes.c_int
+        L.mxfp8_quantize.argtypes = [vp, i64, i64, i64, vp, vp, vp]
+        L.mxfp8_quantize.restype = ctypes.c_int
+        L.mxfp8_gemm.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.mxfp8_gemm.restype = ctypes.c_int
+        L.mxg_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+        L.mxg_gemm_workspace_bytes.restype = sz
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().mxg_strerror(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise MxgError(status, strerror(status))
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _expect(t: torch.Tensor, dtype: torch.dtype, name: str, shape=None) -> None:
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda:
+        raise TypeError(f"{name} must be a {dtype} CUDA/HIP tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def mxfp8_quantize(x: torch.Tensor, K: int | None = None, q: torch.Tensor | None = None,
+                   s: torch.Tensor | None = None, stream=None):
+    """BF16 [M, >=K] (unit stride along K, any row stride) -> (codes [M, K],
+    scales [M, K/32]).  Columns [0, K) are quantized (default: all)."""
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or x.stride(1) != 1:
+        raise TypeError("x must be a 2-D bfloat16 tensor with unit stride along K")
+    M = x.shape[0]
+    K = x.shape[1] if K is None else int(K)
+    if q is None:
+        q = torch.empty(M, K, dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty(M, K // 32, dtype=torch.uint8, device=x.device)
+    _expect(q, torch.uint8, "q", (M, K))
+    _expect(s, torch.uint8, "s", (M, K // 32))
+    _check(lib().mxfp8_quantize(_ptr(x), M, K, x.stride(0), _ptr(q), _ptr(s), _stream(stream)))
+    return q, s
+
+
+def mxfp8_gemm(a_q: torch.Tensor, a_s: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor,
+               out: torch.Tensor | None = None, x: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """out[M, N] (BF16) = dequant(a) . dequant(w)^T.
+
+    With ``x`` (BF16 [M, >=K]) the kernel quantizes x itself and writes its
+    codes/scales into ``a_q``/``a_s`` (which must then be allocated by the
+    caller); otherwise ``a_q``/``a_s`` are the MXFP8 inputs."""
+    M, K = a_q.shape
+    N = w_q.shape[0]
+    _expect(a_q, torch.uint8, "a_q", (M, K))
+    _expect(a_s, torch.uint8, "a_s", (M, K // 32))
+    _expect(w_q, torch.uint8, "w_q", (N, K))
+    _expect(w_s, torch.uint8, "w_s", (N, K // 32))
+    if out is None:
+        out = torch.empty(M, N, dtype=torch.bfloat16, device=a_q.device)
+    _expect(out, torch.bfloat16, "out", (M, N))
+    ld_x = 0
+    if x is not None:
+        if x.dim() != 2 or x.dtype != torch.bfloat16 or x.stride(1) != 1 or x.shape[0] != M:
+            raise TypeError("x must be a bfloat16 [M, >=K] tensor with unit stride along K")
+        ld_x = x.stride(0)
+    ws_bytes = int(lib().mxg_gemm_workspace_bytes(M, N, K))
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=a_q.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().mxfp8_gemm(M, N, K, _ptr(x), ld_x, _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s),
+                            _ptr(out), _ptr(workspace), wsz, _stream(stream)))
+    return out

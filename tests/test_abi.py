@@ -1,0 +1,92 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/*.h declares, and rejects bad arguments with the
+documented status before anything touches a device.  Pointers passed here
+are never dereferenced: every call fails validation first."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "mxfp8_block_scaled_gemm_amd", "libmxgemm.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from mxfp8_block_scaled_gemm_amd import _build
+        _build.build()
+    import mxfp8_block_scaled_gemm_amd as mx
+    return mx.lib()
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\(", text, flags=re.M):
+            if not m.group(0).lstrip().startswith(("#", "typedef", "return")):
+                names.add(m.group(1))
+    return sorted(names)
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("mxfp8_quantize", "mxfp8_gemm", "mxg_strerror", "mxg_version"):
+        assert n in names, names
+
+
+@pytest.mark.parametrize("name", declared_functions())
+def test_every_declared_symbol_is_exported(lib, name):
+    assert hasattr(lib, name), f"{name} is declared in include/ but not exported"
+
+
+def test_strerror(lib):
+    for st in range(6):
+        assert lib.mxg_strerror(st)
+    assert b"unknown" in lib.mxg_strerror(99)
+
+
+A = 0x10000   # fake 16-byte-aligned addresses; never dereferenced
+P = lambda k: ctypes.c_void_p(A * (k + 1))
+
+
+def gemm(lib, M=4, N=1024, K=2048, x=None, ld_x=0, a_q=P(1), a_s=P(2), w_q=P(3), w_s=P(4),
+         out=P(5), ws=None, ws_bytes=0):
+    return lib.mxfp8_gemm(M, N, K, x, ld_x, a_q, a_s, w_q, w_s, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a_q=None), 1), (dict(w_s=None), 1), (dict(out=None), 1),
+    (dict(M=0), 3), (dict(M=49), 3), (dict(M=-1), 3),
+    (dict(K=100), 3), (dict(K=64), 3), (dict(K=0), 3), (dict(N=8), 3), (dict(N=1000), 3),
+    (dict(x=P(6), ld_x=1024), 3),
+    (dict(a_q=ctypes.c_void_p(A + 8)), 2), (dict(w_q=ctypes.c_void_p(A + 1)), 2),
+    (dict(out=ctypes.c_void_p(A + 4)), 2),
+    (dict(x=ctypes.c_void_p(A + 2), ld_x=2048), 2), (dict(x=P(6), ld_x=2052), 2),
+])
+def test_gemm_rejects(lib, kw, status):
+    assert gemm(lib, **kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 4, 64, 64, P(1), P(2)), 1),
+    ((P(0), 0, 64, 64, P(1), P(2)), 3),
+    ((P(0), 4, 48, 64, P(1), P(2)), 3),
+    ((P(0), 4, 64, 32, P(1), P(2)), 3),
+    ((ctypes.c_void_p(A + 2), 4, 64, 64, P(1), P(2)), 2),
+    ((P(0), 4, 64, 68, P(1), P(2)), 2),
+])
+def test_quantize_rejects(lib, args, status):
+    assert lib.mxfp8_quantize(*args, None) == status
+
+
+def test_forced_foreign_arch_is_rejected_before_launch(lib, monkeypatch):
+    # A fully valid call on a device that reports another architecture must
+    # return MXG_ERR_DEVICE without launching (the pointers are fake).
+    monkeypatch.setenv("MXG_FORCE_ARCH", "gfx942")
+    assert gemm(lib) == 5
+    assert lib.mxfp8_quantize(P(0), 4, 64, 64, P(1), P(2), None) == 5

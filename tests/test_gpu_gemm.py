@@ -1,0 +1,158 @@
+"""GPU parity of mxfp8_gemm against the oracle.
+
+Both sides start from the same seeded BF16 tensors (synth.py) and quantize
+them on their own; the codes must agree bit for bit, and every BF16 output
+element must lie within 2^-7 * sum|a_k w_k| + 1e-6 of the oracle's fp64 sum.
+Sizes span several workgroups, ragged row counts (every activation-tile
+bucket and its edges) and the benchmark's full shapes."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_block_scaled_gemm_amd as mx
+import oracle
+import synth
+from helpers import check_gemm, dev_bf16, dev_u8, host_bits, host_u8, say
+
+pytestmark = pytest.mark.gpu
+
+_wcache = {}
+
+
+def _weights(N, K, seed):
+    """Weight codes from the GPU quantizer and from the oracle (must agree)."""
+    key = (N, K, seed)
+    if key not in _wcache:
+        w_bits = synth.bits(synth.gemm_case(1, N, K, seed=seed)["w"])
+        ow = oracle.quantize(w_bits)
+        gq, gs = mx.mxfp8_quantize(dev_bf16(w_bits))
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u8(gq), ow[0]) and np.array_equal(host_u8(gs), ow[1])
+        _wcache.clear()
+        _wcache[key] = (gq, gs, ow)
+    return _wcache[key]
+
+
+def run_case(M, N, K, seed=0, outliers=False, fused=False):
+    case = synth.gemm_case(M, N, K, seed=seed, outliers=outliers)
+    x_bits = synth.bits(case["x"])
+    w_bits = synth.bits(case["w"])
+    ow_q, ow_s = oracle.quantize(w_bits)
+    oa_q, oa_s = oracle.quantize(x_bits)
+    ref = oracle.gemm(oa_q, oa_s, ow_q, ow_s)
+    say(f"gemm M={M} N={N} K={K} seed={seed} outliers={outliers} fused={fused}")
+    w_q, w_s = mx.mxfp8_quantize(dev_bf16(w_bits))
+    x = dev_bf16(x_bits)
+    if fused:
+        a_q = torch.full((M, K), 0x55, dtype=torch.uint8, device="cuda")
+        a_s = torch.full((M, K // 32), 0x55, dtype=torch.uint8, device="cuda")
+        out = mx.mxfp8_gemm(a_q, a_s, w_q, w_s, x=x)
+    else:
+        a_q, a_s = mx.mxfp8_quantize(x)
+        out = mx.mxfp8_gemm(a_q, a_s, w_q, w_s)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u8(w_q), ow_q) and np.array_equal(host_u8(w_s), ow_s)
+    assert np.array_equal(host_u8(a_q), oa_q) and np.array_equal(host_u8(a_s), oa_s)
+    return check_gemm(out, ref, f"M={M} N={N} K={K}")
+
+
+# small shapes: several workgroups, every row bucket and its edges
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 15, 16, 17, 31, 32, 33, 47, 48])
+@pytest.mark.parametrize("fused", [False, True])
+def test_rows_sweep(M, fused):
+    run_case(M, 256, 1024, seed=M, fused=fused)
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (1024, 128), (128, 8192), (2064, 1664)])
+@pytest.mark.parametrize("fused", [False, True])
+def test_shapes(N, K, fused):
+    for M in (1, 20, 48):
+        run_case(M, N, K, seed=N + K, fused=fused)
+
+
+def test_single_gemm_config():
+    # M=4, N=1024, K=2048, x ~ N(0,1), W ~ N(0,0.02), seed 0
+    run_case(4, 1024, 2048, seed=0)
+    run_case(4, 1024, 2048, seed=0, fused=True)
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_decode_bucket_full_size(M):
+    # N=4096, K=5120 with the activation quantize fused into the GEMM launch
+    run_case(M, 4096, 5120, seed=0, fused=True)
+
+
+@pytest.mark.parametrize("N,K", [(4096, 5120), (5120, 8192), (8192, 1536)])
+@pytest.mark.parametrize("M", [16, 32, 48])
+def test_wide_tiles_full_size_outliers(M, N, K):
+    run_case(M, N, K, seed=0, outliers=True)
+
+
+def test_one_hot_weights_bitwise():
+    M, N, K = 9, 256, 1024
+    rng = np.random.default_rng(0)
+    x_bits = oracle.bf16_round(rng.standard_normal((M, K)))
+    oa_q, oa_s = oracle.quantize(x_bits)
+    kn = rng.integers(0, K, N)
+    wq = np.zeros((N, K), np.uint8); wq[np.arange(N), kn] = 0x38
+    ws = np.full((N, K // 32), 127, np.uint8)
+    ref = oracle.gemm(oa_q, oa_s, wq, ws)
+    say("gemm one-hot")
+    out = mx.mxfp8_gemm(dev_u8(oa_q), dev_u8(oa_s), dev_u8(wq), dev_u8(ws))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out), ref.bf16)
+
+
+def test_weight_scale_plus_one_doubles_output_bitwise():
+    M, N, K = 6, 512, 2048
+    case = synth.gemm_case(M, N, K, seed=3)
+    say("gemm scale+1 metamorphic")
+    a_q, a_s = mx.mxfp8_quantize(case["x"].cuda())
+    w_q, w_s = mx.mxfp8_quantize(case["w"].cuda())
+    out1 = mx.mxfp8_gemm(a_q, a_s, w_q, w_s)
+    out2 = mx.mxfp8_gemm(a_q, a_s, w_q, w_s + 1)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.float(), out1.float() * 2)
+
+
+def test_zero_activations_give_positive_zero():
+    M, N, K = 3, 256, 512
+    w_q, w_s, _ = _weights(N, K, 0)
+    say("gemm zero input")
+    out = mx.mxfp8_gemm(torch.zeros(M, K, dtype=torch.uint8, device="cuda"),
+                        torch.zeros(M, K // 32, dtype=torch.uint8, device="cuda"), w_q, w_s)
+    torch.cuda.synchronize()
+    assert (out.view(torch.int16) == 0).all()
+
+
+def test_deterministic_repeats():
+    M, N, K = 8, 4096, 5120
+    w_q, w_s, _ = _weights(N, K, 0)
+    x = synth.gemm_case(M, 16, K, seed=1)["x"].cuda()
+    a_q = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+    a_s = torch.empty(M, K // 32, dtype=torch.uint8, device="cuda")
+    say("gemm determinism x100")
+    first = mx.mxfp8_gemm(a_q, a_s, w_q, w_s, x=x).clone()
+    for _ in range(100):
+        out = mx.mxfp8_gemm(a_q, a_s, w_q, w_s, x=x)
+        assert torch.equal(out.view(torch.int16), first.view(torch.int16))
+    torch.cuda.synchronize()
+
+
+def test_rejected_call_writes_nothing():
+    M, N, K = 4, 256, 512
+    w_q, w_s, _ = _weights(N, K, 0)
+    a_q = torch.zeros(M, K, dtype=torch.uint8, device="cuda")
+    a_s = torch.zeros(M, K // 32, dtype=torch.uint8, device="cuda")
+    out = torch.full((M, N), 0x1234, dtype=torch.int16, device="cuda")
+    say("gemm rejected call")
+    L = mx.lib()
+    for m, k in ((0, K), (49, K), (M, 500)):
+        st = L.mxfp8_gemm(m, N, k, None, 0, a_q.data_ptr(), a_s.data_ptr(), w_q.data_ptr(),
+                          w_s.data_ptr(), out.data_ptr(), None, 0, None)
+        assert st == 3
+    st = L.mxfp8_gemm(M, N, K, None, 0, a_q.data_ptr() + 8, a_s.data_ptr(), w_q.data_ptr(),
+                      w_s.data_ptr(), out.data_ptr(), None, 0, None)
+    assert st == 2
+    torch.cuda.synchronize()
+    assert (out == 0x1234).all()
