@@ -16,7 +16,10 @@
  *                 operands, Float8E8M0FNU scales, sf_vec_size 32.)
  *   weights       "column-major [K, N]" in the pages' words ([mxfp8]
  *                 launch_low_latency), i.e. N rows of K contiguous codes:
- *                 w_q [N, K], w_s [N, K/32] here.
+ *                 w_q [N, K], w_s [N, K/32] here.  The GEMM entry points take
+ *                 the weight once repacked by mxfp8_pack_weights into the
+ *                 order its kernels stream (see there), as a layer
+ *                 preprocesses its weights once for its GEMM backend.
  *   BF16          uint16_t bit patterns.  Outputs are BF16 [M, N] row-major,
  *                 each element the FP32-accumulated sum rounded to nearest even,
  *                 with no scale and no bias ([mxfp8] compile_low_latency).
@@ -91,6 +94,22 @@ int mxfp8_quantize(const uint16_t *x, int64_t M, int64_t K, int64_t ld_x,
                    uint8_t *q, uint8_t *s, void *stream);
 
 /*
+ * mxfp8_pack_weights -- one-time repack of an MXFP8 weight into the tile
+ * order the GEMM kernels stream.  A pure permutation of bytes:
+ *   wp_q[((t*S + s)*2 + h)*1024 + 16*l + b] = w_q[16t + l%16][128s + 64h + 16(l/16) + b]
+ *   wp_s[(t*S + s)*64 + l]                  = w_s[16t + l%16][4s + l/16]
+ * with S = K/128, tile t < N/16, step s < S, half h < 2, lane l < 64,
+ * byte b < 16: the 2 KiB of codes and 64 scale bytes that one 16-row x 128-K
+ * scaled MFMA consumes are contiguous, in the order its lanes hold them.
+ *
+ *   w_q, w_s    row-major MXFP8 weight, [N, K] codes and [N, K/32] scales
+ *   N, K        N % 16 == 0, K % 128 == 0
+ *   wp_q, wp_s  out: N*K and N*K/32 bytes (must not overlap the inputs)
+ */
+int mxfp8_pack_weights(const uint8_t *w_q, const uint8_t *w_s, int64_t N, int64_t K,
+                       uint8_t *wp_q, uint8_t *wp_s, void *stream);
+
+/*
  * mxfp8_gemm -- out = dequant(a) . dequant(w)^T  ([mxfp8] launch_low_latency:
  * out = a (rows x K) times the [K, N] weight; the kernel there computes out^T
  * with the weight's N as its M, as this one does).  FP32 accumulation, BF16
@@ -104,7 +123,7 @@ int mxfp8_quantize(const uint16_t *x, int64_t M, int64_t K, int64_t ld_x,
  *             one launch).
  *   ld_x      row stride of x_bf16 in elements (ignored when x_bf16 is NULL)
  *   a_q, a_s  MXFP8 activations [M, K] / [M, K/32]
- *   w_q, w_s  MXFP8 weights [N, K] / [N, K/32]
+ *   w_q, w_s  MXFP8 weight [N, K] / [N, K/32], packed by mxfp8_pack_weights
  *   out       BF16 [M, N]
  *   workspace, workspace_bytes
  *             scratch for partial sums; mxg_gemm_workspace_bytes() gives the

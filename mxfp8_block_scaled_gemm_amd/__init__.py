@@ -46,6 +46,8 @@ def lib() -> ctypes.CDLL:
         L.mxg_version.restype = ctypes.c_int
         L.mxfp8_quantize.argtypes = [vp, i64, i64, i64, vp, vp, vp]
         L.mxfp8_quantize.restype = ctypes.c_int
+        L.mxfp8_pack_weights.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+        L.mxfp8_pack_weights.restype = ctypes.c_int
         L.mxfp8_gemm.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
         L.mxfp8_gemm.restype = ctypes.c_int
         L.mxg_gemm_workspace_bytes.argtypes = [i64, i64, i64]
@@ -100,20 +102,61 @@ def mxfp8_quantize(x: torch.Tensor, K: int | None = None, q: torch.Tensor | None
     return q, s
 
 
-def mxfp8_gemm(a_q: torch.Tensor, a_s: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor,
+def mxfp8_pack_weights(w_q: torch.Tensor, w_s: torch.Tensor, wp_q: torch.Tensor | None = None,
+                       wp_s: torch.Tensor | None = None, stream=None):
+    """Repack a row-major MXFP8 weight ([N, K] codes, [N, K/32] scales) into
+    the GEMM's streaming order; returns (wp_q [N*K], wp_s [N*K/32]) uint8."""
+    N, K = w_q.shape
+    _expect(w_q, torch.uint8, "w_q", (N, K))
+    _expect(w_s, torch.uint8, "w_s", (N, K // 32))
+    if wp_q is None:
+        wp_q = torch.empty(N * K, dtype=torch.uint8, device=w_q.device)
+    if wp_s is None:
+        wp_s = torch.empty(N * K // 32, dtype=torch.uint8, device=w_q.device)
+    _expect(wp_q, torch.uint8, "wp_q", (N * K,))
+    _expect(wp_s, torch.uint8, "wp_s", (N * K // 32,))
+    _check(lib().mxfp8_pack_weights(_ptr(w_q), _ptr(w_s), N, K, _ptr(wp_q), _ptr(wp_s),
+                                    _stream(stream)))
+    return wp_q, wp_s
+
+
+class PackedWeight:
+    """An MXFP8 weight in the GEMM's streaming order, with its shape."""
+
+    def __init__(self, q: torch.Tensor, s: torch.Tensor, N: int, K: int):
+        self.q, self.s, self.N, self.K = q, s, N, K
+
+    @classmethod
+    def from_rows(cls, w_q: torch.Tensor, w_s: torch.Tensor, stream=None) -> "PackedWeight":
+        q, s = mxfp8_pack_weights(w_q, w_s, stream=stream)
+        return cls(q, s, w_q.shape[0], w_q.shape[1])
+
+    @classmethod
+    def from_bf16(cls, w: torch.Tensor, stream=None) -> "PackedWeight":
+        """Quantize a BF16 [N, K] weight (same rule as the activations) and pack it."""
+        q, s = mxfp8_quantize(w, stream=stream)
+        return cls.from_rows(q, s, stream=stream)
+
+    def clone(self) -> "PackedWeight":
+        return PackedWeight(self.q.clone(), self.s.clone(), self.N, self.K)
+
+
+def mxfp8_gemm(a_q: torch.Tensor, a_s: torch.Tensor, w: PackedWeight,
                out: torch.Tensor | None = None, x: torch.Tensor | None = None,
                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """out[M, N] (BF16) = dequant(a) . dequant(w)^T.
+    """out[M, N] (BF16) = dequant(a) . dequant(w)^T for a PackedWeight w.
 
     With ``x`` (BF16 [M, >=K]) the kernel quantizes x itself and writes its
     codes/scales into ``a_q``/``a_s`` (which must then be allocated by the
     caller); otherwise ``a_q``/``a_s`` are the MXFP8 inputs."""
     M, K = a_q.shape
-    N = w_q.shape[0]
+    N = w.N
+    if w.K != K:
+        raise ValueError(f"weight K {w.K} != activation K {K}")
     _expect(a_q, torch.uint8, "a_q", (M, K))
     _expect(a_s, torch.uint8, "a_s", (M, K // 32))
-    _expect(w_q, torch.uint8, "w_q", (N, K))
-    _expect(w_s, torch.uint8, "w_s", (N, K // 32))
+    _expect(w.q, torch.uint8, "w.q", (N * K,))
+    _expect(w.s, torch.uint8, "w.s", (N * K // 32,))
     if out is None:
         out = torch.empty(M, N, dtype=torch.bfloat16, device=a_q.device)
     _expect(out, torch.bfloat16, "out", (M, N))
@@ -126,6 +169,6 @@ def mxfp8_gemm(a_q: torch.Tensor, a_s: torch.Tensor, w_q: torch.Tensor, w_s: tor
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=a_q.device)
     wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().mxfp8_gemm(M, N, K, _ptr(x), ld_x, _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s),
+    _check(lib().mxfp8_gemm(M, N, K, _ptr(x), ld_x, _ptr(a_q), _ptr(a_s), _ptr(w.q), _ptr(w.s),
                             _ptr(out), _ptr(workspace), wsz, _stream(stream)))
     return out

@@ -56,12 +56,24 @@ int validate_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* x, int64_t ld
   if (M < 1 || M > MXG_MAX_ROWS || N < 16 || N % 16 != 0 || K < 128 || K % 128 != 0 ||
       N > (int64_t)1 << 24 || K > (int64_t)1 << 20)
     return MXG_ERR_SHAPE;
-  if (x && ld_x < K) return MXG_ERR_SHAPE;
+  if (N * K > ((int64_t)1 << 31) - 1) return MXG_ERR_SHAPE;
+  if (x && (ld_x < K || ld_x * M > ((int64_t)1 << 30))) return MXG_ERR_SHAPE;
   if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(w_q) || !aligned16(w_s) ||
       !aligned16(out) || (x && (!aligned16(x) || ld_x % 8 != 0)))
     return MXG_ERR_ALIGN;
   const size_t need = mxg_gemm_workspace_bytes(M, N, K);
   if (need > 0 && (!ws || ws_bytes < need)) return MXG_ERR_WORKSPACE;
+  return MXG_OK;
+}
+
+int validate_pack(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K,
+                  const uint8_t* wp_q, const uint8_t* wp_s) {
+  if (!w_q || !w_s || !wp_q || !wp_s) return MXG_ERR_NULL;
+  if (N < 16 || N % 16 != 0 || K < 128 || K % 128 != 0 || N > (int64_t)1 << 24 ||
+      K > (int64_t)1 << 20 || N * K > ((int64_t)1 << 31) - 1)
+    return MXG_ERR_SHAPE;
+  if (!aligned16(w_q) || !aligned16(w_s) || !aligned16(wp_q) || !aligned16(wp_s))
+    return MXG_ERR_ALIGN;
   return MXG_OK;
 }
 
@@ -91,6 +103,14 @@ int mxfp8_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_
   if (st != MXG_OK) return st;
   if ((st = check_device()) != MXG_OK) return st;
   return launched(mxg::launch_quantize(x, M, K, ld_x, q, s, (hipStream_t)stream));
+}
+
+int mxfp8_pack_weights(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K,
+                       uint8_t* wp_q, uint8_t* wp_s, void* stream) {
+  int st = validate_pack(w_q, w_s, N, K, wp_q, wp_s);
+  if (st != MXG_OK) return st;
+  if ((st = check_device()) != MXG_OK) return st;
+  return launched(mxg::launch_pack(w_q, w_s, N, K, wp_q, wp_s, (hipStream_t)stream));
 }
 
 int mxfp8_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* x_bf16, int64_t ld_x,

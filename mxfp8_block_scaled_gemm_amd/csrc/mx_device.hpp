@@ -27,12 +27,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
-// Larger of the two BF16 magnitudes of a packed pair, as magnitude bits.
-// For non-negative floats the bit patterns order like the values, so the
-// block maximum is an integer maximum.
-__device__ __forceinline__ uint32_t bf16_pair_absmax_bits(uint32_t w) {
-  uint32_t lo = w & 0x7FFFu, hi = (w >> 16) & 0x7FFFu;
-  return lo > hi ? lo : hi;
+// Maximum over the 4 lanes of each aligned lane quad (DPP quad permutes:
+// no LDS round trip).
+__device__ __forceinline__ uint32_t quad_max(uint32_t a) {
+  uint32_t b = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+  a = a > b ? a : b;
+  b = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x4E, 0xF, 0xF, false);           // [2,3,0,1]
+  return a > b ? a : b;
 }
 
 // ------------------------------------------------------- scale exponent
@@ -51,25 +52,54 @@ __device__ __forceinline__ int block_exponent(uint32_t amax_bits) {
 
 // --------------------------------------------------------------- E4M3
 
-// Scales two FP32 values by 2^-e (exact), saturates them to +-448 and
-// converts them to E4M3 with round-to-nearest-even; the two codes land in the
-// low (HI = false) or high (HI = true) 16 bits of `old`.  The hardware
-// conversion rounds to nearest even on the whole E4M3 grid, subnormals
-// included, but returns NaN above 464, hence the clamp first.
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+
+// Larger BF16 magnitude (as bits) over two packed pairs, per 16-bit half.
+// For non-negative floats the bit patterns order like the values, so a
+// block's amax is an integer maximum of its magnitude bits.
+__device__ __forceinline__ uint32_t bf16x2_absmax2(uint32_t a, uint32_t b) {
+  const v2u16 x = __builtin_bit_cast(v2u16, a & 0x7FFF7FFFu);
+  const v2u16 y = __builtin_bit_cast(v2u16, b & 0x7FFF7FFFu);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
+}
+__device__ __forceinline__ uint32_t halves_max(uint32_t m) {
+  const uint32_t lo = m & 0xFFFFu, hi = m >> 16;
+  return lo > hi ? lo : hi;
+}
+
+// The block's scale 2^e and saturation bound 448 * 2^e as FP32, built from
+// their bit fields (2^-127 is an FP32 subnormal; the bound is always normal).
+struct BlockScale {
+  float scale, bound;
+};
+__device__ __forceinline__ BlockScale block_scale(int e) {
+  BlockScale b;
+  b.scale = __uint_as_float(e > -127 ? (uint32_t)(e + 127) << 23 : 0x00400000u);
+  b.bound = __uint_as_float(((uint32_t)(e + 135) << 23) | 0x00600000u);
+  return b;
+}
+
+// Two FP32 values -> two E4M3 codes of x / 2^e, round to nearest even,
+// saturated to +-448: the hardware MX convert divides by the scale and
+// rounds to nearest even over the whole E4M3 grid (subnormals included) but
+// gives NaN above 464, so the inputs are first clamped to +-448 * 2^e (exact:
+// both are powers of two times representable values).  The codes land in the
+// low (HI = false) or high (HI = true) 16 bits of `old`.
 template <bool HI>
-__device__ __forceinline__ uint32_t enc2_e4m3(float a, float b, int neg_e, uint32_t old) {
-  float va = __builtin_amdgcn_ldexpf(a, neg_e);
-  float vb = __builtin_amdgcn_ldexpf(b, neg_e);
-  va = __builtin_fminf(__builtin_fmaxf(va, -448.0f), 448.0f);
-  vb = __builtin_fminf(__builtin_fmaxf(vb, -448.0f), 448.0f);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(va, vb, (int)old, HI);
+__device__ __forceinline__ uint32_t enc2_e4m3(float a, float b, BlockScale bs, uint32_t old) {
+  const float ca = __builtin_amdgcn_fmed3f(a, -bs.bound, bs.bound);
+  const float cb = __builtin_amdgcn_fmed3f(b, -bs.bound, bs.bound);
+  return __builtin_bit_cast(
+      uint32_t, __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s, old), ca, cb,
+                                                         bs.scale, HI));
 }
 
 // Four BF16 values (two packed pairs) -> four E4M3 codes in one dword,
 // element order preserved (lowest address in the lowest byte).
-__device__ __forceinline__ uint32_t enc4_e4m3(uint32_t w0, uint32_t w1, int neg_e) {
-  uint32_t r = enc2_e4m3<false>(bf16_lo(w0), bf16_hi(w0), neg_e, 0u);
-  return enc2_e4m3<true>(bf16_lo(w1), bf16_hi(w1), neg_e, r);
+__device__ __forceinline__ uint32_t enc4_e4m3(uint32_t w0, uint32_t w1, BlockScale bs) {
+  uint32_t r = enc2_e4m3<false>(bf16_lo(w0), bf16_hi(w0), bs, 0u);
+  return enc2_e4m3<true>(bf16_lo(w1), bf16_hi(w1), bs, r);
 }
 
 // ---------------------------------------------------------------- MFMA
@@ -94,5 +124,28 @@ __device__ __forceinline__ v8i cat8(v4i lo, v4i hi) {
 // 16-byte global load / store.
 __device__ __forceinline__ v4i ld16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
 __device__ __forceinline__ void st16(void* p, v4i v) { *reinterpret_cast<v4i*>(p) = v; }
+
+// ------------------------------------------------------- buffer loads
+//
+// Raw buffer loads with a byte range: an access at or beyond `bytes` returns
+// zero without touching memory, which predicates a load without a branch
+// (so the number of outstanding loads stays static for s_waitcnt).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ v4i buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+// Streaming variant for data read exactly once (the weights): non-temporal
+// cache policy, so the stream does not evict reused lines.
+__device__ __forceinline__ v4i buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
+}
+__device__ __forceinline__ uint32_t buf_ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
 
 }  // namespace mxg

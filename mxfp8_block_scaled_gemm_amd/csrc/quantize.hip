@@ -7,7 +7,7 @@
 // integer max over BF16 magnitude bits reduced with two lane shuffles, and
 // each lane writes its 8 codes as one 8-byte store.  Bit-exact by
 // construction: the exponent is integer arithmetic and the only rounding is
-// the hardware RNE convert of x * 2^-e.
+// the hardware RNE convert of x / 2^e.
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
 
@@ -25,17 +25,15 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
   for (int64_t row = blockIdx.y; row < M; row += gridDim.y) {
     v4i v = {0, 0, 0, 0};
     if (valid) v = ld16(x + row * ld_x + b * 32 + sub * 8);
-    uint32_t a = bf16_pair_absmax_bits((uint32_t)v[0]);
-    a = max(a, bf16_pair_absmax_bits((uint32_t)v[1]));
-    a = max(a, bf16_pair_absmax_bits((uint32_t)v[2]));
-    a = max(a, bf16_pair_absmax_bits((uint32_t)v[3]));
-    a = max(a, (uint32_t)__shfl_xor((int)a, 1));
-    a = max(a, (uint32_t)__shfl_xor((int)a, 2));
+    uint32_t a = halves_max(bf16x2_absmax2(bf16x2_absmax2((uint32_t)v[0], (uint32_t)v[1]),
+                                           bf16x2_absmax2((uint32_t)v[2], (uint32_t)v[3])));
+    a = quad_max(a);
     const int e = block_exponent(a);
+    const BlockScale bs = block_scale(e);
     if (valid) {
       uint2 c;
-      c.x = enc4_e4m3((uint32_t)v[0], (uint32_t)v[1], -e);
-      c.y = enc4_e4m3((uint32_t)v[2], (uint32_t)v[3], -e);
+      c.x = enc4_e4m3((uint32_t)v[0], (uint32_t)v[1], bs);
+      c.y = enc4_e4m3((uint32_t)v[2], (uint32_t)v[3], bs);
       *reinterpret_cast<uint2*>(q + row * K + b * 32 + sub * 8) = c;
       if (sub == 0) s[row * nb + b] = (uint8_t)(e + 127);
     }

@@ -29,7 +29,7 @@ def _weights(N, K, seed):
         torch.cuda.synchronize()
         assert np.array_equal(host_u8(gq), ow[0]) and np.array_equal(host_u8(gs), ow[1])
         _wcache.clear()
-        _wcache[key] = (gq, gs, ow)
+        _wcache[key] = (mx.PackedWeight.from_rows(gq, gs), ow)
     return _wcache[key]
 
 
@@ -42,14 +42,15 @@ def run_case(M, N, K, seed=0, outliers=False, fused=False):
     ref = oracle.gemm(oa_q, oa_s, ow_q, ow_s)
     say(f"gemm M={M} N={N} K={K} seed={seed} outliers={outliers} fused={fused}")
     w_q, w_s = mx.mxfp8_quantize(dev_bf16(w_bits))
+    w = mx.PackedWeight.from_rows(w_q, w_s)
     x = dev_bf16(x_bits)
     if fused:
         a_q = torch.full((M, K), 0x55, dtype=torch.uint8, device="cuda")
         a_s = torch.full((M, K // 32), 0x55, dtype=torch.uint8, device="cuda")
-        out = mx.mxfp8_gemm(a_q, a_s, w_q, w_s, x=x)
+        out = mx.mxfp8_gemm(a_q, a_s, w, x=x)
     else:
         a_q, a_s = mx.mxfp8_quantize(x)
-        out = mx.mxfp8_gemm(a_q, a_s, w_q, w_s)
+        out = mx.mxfp8_gemm(a_q, a_s, w)
     torch.cuda.synchronize()
     assert np.array_equal(host_u8(w_q), ow_q) and np.array_equal(host_u8(w_s), ow_s)
     assert np.array_equal(host_u8(a_q), oa_q) and np.array_equal(host_u8(a_s), oa_s)
@@ -98,7 +99,7 @@ def test_one_hot_weights_bitwise():
     ws = np.full((N, K // 32), 127, np.uint8)
     ref = oracle.gemm(oa_q, oa_s, wq, ws)
     say("gemm one-hot")
-    out = mx.mxfp8_gemm(dev_u8(oa_q), dev_u8(oa_s), dev_u8(wq), dev_u8(ws))
+    out = mx.mxfp8_gemm(dev_u8(oa_q), dev_u8(oa_s), mx.PackedWeight.from_rows(dev_u8(wq), dev_u8(ws)))
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(out), ref.bf16)
 
@@ -109,39 +110,40 @@ def test_weight_scale_plus_one_doubles_output_bitwise():
     say("gemm scale+1 metamorphic")
     a_q, a_s = mx.mxfp8_quantize(case["x"].cuda())
     w_q, w_s = mx.mxfp8_quantize(case["w"].cuda())
-    out1 = mx.mxfp8_gemm(a_q, a_s, w_q, w_s)
-    out2 = mx.mxfp8_gemm(a_q, a_s, w_q, w_s + 1)
+    out1 = mx.mxfp8_gemm(a_q, a_s, mx.PackedWeight.from_rows(w_q, w_s))
+    out2 = mx.mxfp8_gemm(a_q, a_s, mx.PackedWeight.from_rows(w_q, w_s + 1))
     torch.cuda.synchronize()
     assert torch.equal(out2.float(), out1.float() * 2)
 
 
 def test_zero_activations_give_positive_zero():
     M, N, K = 3, 256, 512
-    w_q, w_s, _ = _weights(N, K, 0)
+    w, _ = _weights(N, K, 0)
     say("gemm zero input")
     out = mx.mxfp8_gemm(torch.zeros(M, K, dtype=torch.uint8, device="cuda"),
-                        torch.zeros(M, K // 32, dtype=torch.uint8, device="cuda"), w_q, w_s)
+                        torch.zeros(M, K // 32, dtype=torch.uint8, device="cuda"), w)
     torch.cuda.synchronize()
     assert (out.view(torch.int16) == 0).all()
 
 
 def test_deterministic_repeats():
     M, N, K = 8, 4096, 5120
-    w_q, w_s, _ = _weights(N, K, 0)
+    w, _ = _weights(N, K, 0)
     x = synth.gemm_case(M, 16, K, seed=1)["x"].cuda()
     a_q = torch.empty(M, K, dtype=torch.uint8, device="cuda")
     a_s = torch.empty(M, K // 32, dtype=torch.uint8, device="cuda")
     say("gemm determinism x100")
-    first = mx.mxfp8_gemm(a_q, a_s, w_q, w_s, x=x).clone()
+    first = mx.mxfp8_gemm(a_q, a_s, w, x=x).clone()
     for _ in range(100):
-        out = mx.mxfp8_gemm(a_q, a_s, w_q, w_s, x=x)
+        out = mx.mxfp8_gemm(a_q, a_s, w, x=x)
         assert torch.equal(out.view(torch.int16), first.view(torch.int16))
     torch.cuda.synchronize()
 
 
 def test_rejected_call_writes_nothing():
     M, N, K = 4, 256, 512
-    w_q, w_s, _ = _weights(N, K, 0)
+    w, _ = _weights(N, K, 0)
+    w_q, w_s = w.q, w.s
     a_q = torch.zeros(M, K, dtype=torch.uint8, device="cuda")
     a_s = torch.zeros(M, K // 32, dtype=torch.uint8, device="cuda")
     out = torch.full((M, N), 0x1234, dtype=torch.int16, device="cuda")
@@ -156,3 +158,33 @@ def test_rejected_call_writes_nothing():
     assert st == 2
     torch.cuda.synchronize()
     assert (out == 0x1234).all()
+
+
+def _pack_reference(wq: np.ndarray, ws: np.ndarray) -> tuple:
+    """The packed order written out from its definition in include/mxgemm.h."""
+    N, K = wq.shape
+    S = K // 128
+    pq = np.empty(N * K, np.uint8)
+    ps = np.empty(N * K // 32, np.uint8)
+    for t in range(N // 16):
+        for s_ in range(S):
+            for h in range(2):
+                for l in range(64):
+                    off = ((t * S + s_) * 2 + h) * 1024 + 16 * l
+                    col = 128 * s_ + 64 * h + 16 * (l // 16)
+                    pq[off:off + 16] = wq[16 * t + l % 16, col:col + 16]
+            for l in range(64):
+                ps[(t * S + s_) * 64 + l] = ws[16 * t + l % 16, 4 * s_ + l // 16]
+    return pq, ps
+
+
+@pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (64, 1024)])
+def test_pack_is_the_documented_permutation(N, K):
+    rng = np.random.default_rng(N + K)
+    wq = rng.integers(0, 256, (N, K)).astype(np.uint8)
+    ws = rng.integers(0, 256, (N, K // 32)).astype(np.uint8)
+    say(f"pack N={N} K={K}")
+    pq, ps = mx.mxfp8_pack_weights(dev_u8(wq), dev_u8(ws))
+    torch.cuda.synchronize()
+    rq, rs = _pack_reference(wq, ws)
+    assert np.array_equal(host_u8(pq), rq) and np.array_equal(host_u8(ps), rs)
