@@ -126,16 +126,74 @@ int mxfp8_pack_weights(const uint8_t *w_q, const uint8_t *w_s, int64_t N, int64_
  *   w_q, w_s  MXFP8 weight [N, K] / [N, K/32], packed by mxfp8_pack_weights
  *   out       BF16 [M, N]
  *   workspace, workspace_bytes
- *             scratch for partial sums; mxg_gemm_workspace_bytes() gives the
- *             size needed (0 means NULL is accepted).
+ *             caller-owned device scratch of at least mxg_gemm_workspace_bytes()
+ *             bytes: cross-workgroup counters and K-split partial sums.  It
+ *             must be zero-filled once when allocated; every call leaves its
+ *             counters (the first 64 KiB) at zero again, and the partial
+ *             sums after them need no clearing, so calls of any shape can
+ *             share one workspace in turn.
+ *             Byte offset 20 holds an error word that an in-kernel wait sets
+ *             if it ever expires (it cannot in a correct launch).  Calls that
+ *             share a workspace must not overlap (issue them on one stream).
+ *
+ * Small-row GEMMs are bound by the weight stream from HBM; the library picks
+ * the kernel and the K split per shape.  Results do not depend on the choice
+ * beyond FP32 summation order, and are deterministic for a given shape.
  */
 int mxfp8_gemm(int64_t M, int64_t N, int64_t K, const uint16_t *x_bf16,
                int64_t ld_x, uint8_t *a_q, uint8_t *a_s, const uint8_t *w_q,
                const uint8_t *w_s, uint16_t *out, void *workspace,
                size_t workspace_bytes, void *stream);
 
-/* Workspace bytes mxfp8_gemm needs for these sizes (0: none). */
+/* Workspace bytes mxfp8_gemm needs for these sizes. */
 size_t mxg_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * A packed MXFP8 weight (mxfp8_pack_weights order) and its shape [N, K].
+ */
+typedef struct {
+  const uint8_t *q; /* N*K packed codes   */
+  const uint8_t *s; /* N*K/32 packed scales */
+  int64_t N, K;
+} mxg_weight;
+
+/*
+ * mxfp8_proj_chain -- three projections back to back in one launch, in the
+ * order of a decode step's attention ([step] page, AttentionStep.run:
+ * fused_wqa_wkv on the MXFP8 layer input, the leading columns of its output
+ * requantized to MXFP8 for wq_b, and wo_b on its own MXFP8 input):
+ *   A:  out_a = a . wA^T                       (a: MXFP8 [M, wA.K])
+ *   requantize out_a[:, 0:wB.K] to MXFP8 -> (b_q, b_s), as mxfp8_quantize does
+ *   B:  out_b = b . wB^T
+ *   C:  out_c = c . wC^T                       (c: MXFP8 [M, wC.K])
+ * Each stage reads its activations only once the previous stage has finished
+ * (C included), but every stage's weight stream starts as early as the
+ * hardware allows: weights never depend on the previous stage ([mxfp8] page:
+ * the low-latency kernel loads its weights before its grid dependency wait
+ * so the weight read overlaps the previous kernel).
+ *
+ * Shapes: 1 <= M <= 48; each weight N % 16 == 0, K % 128 == 0; wB.K <= wA.N,
+ * wB.K % 128 == 0.  out_a/out_b/out_c are BF16 [M, N] row-major, b_q/b_s
+ * [M, wB.K] / [M, wB.K/32] (written).  The workspace rules of mxfp8_gemm
+ * apply, with mxg_chain_workspace_bytes() as the size.
+ */
+typedef struct {
+  int64_t M;
+  const uint8_t *a_q, *a_s;
+  mxg_weight wA, wB, wC;
+  uint16_t *out_a;
+  uint8_t *b_q, *b_s;
+  uint16_t *out_b;
+  const uint8_t *c_q, *c_s;
+  uint16_t *out_c;
+  void *workspace;
+  size_t workspace_bytes;
+} mxg_chain;
+
+int mxfp8_proj_chain(const mxg_chain *chain, void *stream);
+
+/* Workspace bytes mxfp8_proj_chain needs (pointers in *chain are not read). */
+size_t mxg_chain_workspace_bytes(const mxg_chain *chain);
 
 #ifdef __cplusplus
 }

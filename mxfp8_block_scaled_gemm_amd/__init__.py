@@ -22,6 +22,23 @@ MAX_ROWS = 48
 _lib = None
 
 
+class MxgWeight(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("s", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class MxgChain(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64),
+                ("a_q", ctypes.c_void_p), ("a_s", ctypes.c_void_p),
+                ("wA", MxgWeight), ("wB", MxgWeight), ("wC", MxgWeight),
+                ("out_a", ctypes.c_void_p),
+                ("b_q", ctypes.c_void_p), ("b_s", ctypes.c_void_p),
+                ("out_b", ctypes.c_void_p),
+                ("c_q", ctypes.c_void_p), ("c_s", ctypes.c_void_p),
+                ("out_c", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 class MxgError(ValueError):
     """A libmxgemm call returned a non-zero status."""
 
@@ -52,6 +69,10 @@ def lib() -> ctypes.CDLL:
         L.mxfp8_gemm.restype = ctypes.c_int
         L.mxg_gemm_workspace_bytes.argtypes = [i64, i64, i64]
         L.mxg_gemm_workspace_bytes.restype = sz
+        L.mxfp8_proj_chain.argtypes = [ctypes.POINTER(MxgChain), vp]
+        L.mxfp8_proj_chain.restype = ctypes.c_int
+        L.mxg_chain_workspace_bytes.argtypes = [ctypes.POINTER(MxgChain)]
+        L.mxg_chain_workspace_bytes.restype = sz
         _lib = L
     return _lib
 
@@ -82,6 +103,29 @@ def _expect(t: torch.Tensor, dtype: torch.dtype, name: str, shape=None) -> None:
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+_workspaces: dict = {}
+
+
+def get_workspace(device, nbytes: int) -> torch.Tensor:
+    """A zero-filled, per-device workspace of at least ``nbytes`` bytes.
+
+    The library leaves a workspace zeroed after every call, so one buffer
+    serves all calls issued on one stream; calls on different streams need
+    workspaces of their own (pass ``workspace=``)."""
+    dev = torch.device(device)
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    t = _workspaces.get(key)
+    if t is None or t.numel() < nbytes:
+        t = torch.zeros(max(int(nbytes), 1 << 20), dtype=torch.uint8, device=dev)
+        _workspaces[key] = t
+    return t
+
+
+def workspace_error(ws: torch.Tensor) -> int:
+    """The error word of a workspace (non-zero: an in-kernel wait expired)."""
+    return int(ws[20:24].view(torch.int32).item())
 
 
 def mxfp8_quantize(x: torch.Tensor, K: int | None = None, q: torch.Tensor | None = None,
@@ -166,9 +210,49 @@ def mxfp8_gemm(a_q: torch.Tensor, a_s: torch.Tensor, w: PackedWeight,
             raise TypeError("x must be a bfloat16 [M, >=K] tensor with unit stride along K")
         ld_x = x.stride(0)
     ws_bytes = int(lib().mxg_gemm_workspace_bytes(M, N, K))
-    if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=a_q.device)
-    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is None:
+        workspace = get_workspace(a_q.device, ws_bytes)
+    wsz = workspace.numel() * workspace.element_size()
     _check(lib().mxfp8_gemm(M, N, K, _ptr(x), ld_x, _ptr(a_q), _ptr(a_s), _ptr(w.q), _ptr(w.s),
                             _ptr(out), _ptr(workspace), wsz, _stream(stream)))
     return out
+
+
+def _w(w: PackedWeight) -> MxgWeight:
+    return MxgWeight(w.q.data_ptr(), w.s.data_ptr(), w.N, w.K)
+
+
+def mxfp8_proj_chain(a_q: torch.Tensor, a_s: torch.Tensor, wA: PackedWeight, wB: PackedWeight,
+                     c_q: torch.Tensor, c_s: torch.Tensor, wC: PackedWeight, outs=None,
+                     workspace: torch.Tensor | None = None, stream=None):
+    """Three projections in one launch: A on (a_q, a_s); the leading wB.K
+    columns of A's output requantized to MXFP8 as B's input; C on (c_q, c_s).
+    Returns (out_a, b_q, b_s, out_b, out_c)."""
+    M = a_q.shape[0]
+    dev = a_q.device
+    _expect(a_q, torch.uint8, "a_q", (M, wA.K))
+    _expect(a_s, torch.uint8, "a_s", (M, wA.K // 32))
+    _expect(c_q, torch.uint8, "c_q", (M, wC.K))
+    _expect(c_s, torch.uint8, "c_s", (M, wC.K // 32))
+    if outs is None:
+        outs = (torch.empty(M, wA.N, dtype=torch.bfloat16, device=dev),
+                torch.empty(M, wB.K, dtype=torch.uint8, device=dev),
+                torch.empty(M, wB.K // 32, dtype=torch.uint8, device=dev),
+                torch.empty(M, wB.N, dtype=torch.bfloat16, device=dev),
+                torch.empty(M, wC.N, dtype=torch.bfloat16, device=dev))
+    out_a, b_q, b_s, out_b, out_c = outs
+    _expect(out_a, torch.bfloat16, "out_a", (M, wA.N))
+    _expect(b_q, torch.uint8, "b_q", (M, wB.K))
+    _expect(b_s, torch.uint8, "b_s", (M, wB.K // 32))
+    _expect(out_b, torch.bfloat16, "out_b", (M, wB.N))
+    _expect(out_c, torch.bfloat16, "out_c", (M, wC.N))
+    c = MxgChain(M, a_q.data_ptr(), a_s.data_ptr(), _w(wA), _w(wB), _w(wC), out_a.data_ptr(),
+                 b_q.data_ptr(), b_s.data_ptr(), out_b.data_ptr(), c_q.data_ptr(), c_s.data_ptr(),
+                 out_c.data_ptr(), None, 0)
+    need = int(lib().mxg_chain_workspace_bytes(ctypes.byref(c)))
+    if workspace is None:
+        workspace = get_workspace(dev, need)
+    c.workspace = workspace.data_ptr()
+    c.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().mxfp8_proj_chain(ctypes.byref(c), _stream(stream)))
+    return out_a, b_q, b_s, out_b, out_c

@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "mx_launch.hpp"
+#include "mx_stages.hpp"
 #include "mxgemm.h"
 
 namespace {
@@ -63,7 +64,71 @@ int validate_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* x, int64_t ld
     return MXG_ERR_ALIGN;
   const size_t need = mxg_gemm_workspace_bytes(M, N, K);
   if (need > 0 && (!ws || ws_bytes < need)) return MXG_ERR_WORKSPACE;
+  if (ws && !aligned16(ws)) return MXG_ERR_ALIGN;
   return MXG_OK;
+}
+
+bool weight_ok(const mxg_weight& w) {
+  return w.N >= 16 && w.N % 16 == 0 && w.K >= 128 && w.K % 128 == 0 && w.N <= ((int64_t)1 << 24) &&
+         w.K <= ((int64_t)1 << 20) && w.N * w.K <= ((int64_t)1 << 31) - 1;
+}
+
+int validate_chain(const mxg_chain* c, size_t need) {
+  if (!c) return MXG_ERR_NULL;
+  if (!c->a_q || !c->a_s || !c->wA.q || !c->wA.s || !c->wB.q || !c->wB.s || !c->wC.q ||
+      !c->wC.s || !c->out_a || !c->b_q || !c->b_s || !c->out_b || !c->c_q || !c->c_s ||
+      !c->out_c)
+    return MXG_ERR_NULL;
+  if (c->M < 1 || c->M > MXG_MAX_ROWS || !weight_ok(c->wA) || !weight_ok(c->wB) ||
+      !weight_ok(c->wC) || c->wB.K > c->wA.N)
+    return MXG_ERR_SHAPE;
+  const void* ptrs[] = {c->a_q, c->a_s, c->wA.q, c->wA.s, c->wB.q, c->wB.s, c->wC.q, c->wC.s,
+                        c->out_a, c->b_q, c->b_s, c->out_b, c->c_q, c->c_s, c->out_c};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MXG_ERR_ALIGN;
+  if (!c->workspace || c->workspace_bytes < need) return MXG_ERR_WORKSPACE;
+  if (!aligned16(c->workspace)) return MXG_ERR_ALIGN;
+  return MXG_OK;
+}
+
+// Kernel choice for a plain GEMM: the stage kernel when the activations come
+// as BF16 (distributed quantize), when the tiles need a K split to balance
+// the grid, or when forced; the direct kernels otherwise.  MXG_GEMM_PATH
+// ("stage" / "direct") forces a choice (tests use it to cover both).
+bool use_stage_kernel(int M, int N, int K, bool fq) {
+  const char* force = std::getenv("MXG_GEMM_PATH");
+  if (force && std::strcmp(force, "stage") == 0) return true;
+  if (force && std::strcmp(force, "direct") == 0) return false;
+  if (fq) return true;
+  const int G = mxg::stage_grid();
+  return G > 0 && mxg::choose_kparts(M, N, K, G) > 1;
+}
+
+mxg::ProgramBuilder gemm_program(int M, int N, int K, const uint16_t* x, int ld_x, uint8_t* a_q,
+                                 uint8_t* a_s, const uint8_t* w_q, const uint8_t* w_s,
+                                 uint16_t* out, uint8_t* ws, int G) {
+  mxg::ProgramBuilder pb(M, G, ws);
+  int dep = -1;
+  if (x) dep = pb.add_quant(x, ld_x, K, a_q, a_s, -1);
+  pb.add_gemm(N, K, w_q, w_s, a_q, a_s, 1, 0, 0, out, N, dep);
+  return pb;
+}
+
+mxg::ProgramBuilder chain_program(const mxg_chain& c, int G) {
+  mxg::ProgramBuilder pb((int)c.M, G, reinterpret_cast<uint8_t*>(c.workspace));
+  const int a = pb.add_gemm((int)c.wA.N, (int)c.wA.K, c.wA.q, c.wA.s, c.a_q, c.a_s, 1, 0, 0,
+                            c.out_a, (int)c.wA.N, -1);
+  const int rq = pb.add_quant(c.out_a, (int)c.wA.N, (int)c.wB.K, c.b_q, c.b_s, a);
+  const int b = pb.add_gemm((int)c.wB.N, (int)c.wB.K, c.wB.q, c.wB.s, c.b_q, c.b_s, 1, 0, 0,
+                            c.out_b, (int)c.wB.N, rq);
+  pb.add_gemm((int)c.wC.N, (int)c.wC.K, c.wC.q, c.wC.s, c.c_q, c.c_s, 1, 0, 0, c.out_c,
+              (int)c.wC.N, b);
+  return pb;
+}
+
+int run_program(mxg::ProgramBuilder& pb, hipStream_t stream) {
+  if (!pb.finish()) return MXG_ERR_SHAPE;
+  return launched(mxg::launch_program(pb.program(), pb.mb(), stream));
 }
 
 int validate_pack(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K,
@@ -95,7 +160,24 @@ const char* mxg_strerror(int status) {
 
 int mxg_version(void) { return 100; }
 
-size_t mxg_gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+size_t mxg_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || M > MXG_MAX_ROWS || N < 16 || K < 128) return mxg::kCtrBytes;
+  const int G = mxg::stage_grid();
+  if (G <= 0) return mxg::kCtrBytes;
+  mxg::ProgramBuilder pb = gemm_program((int)M, (int)N, (int)K, nullptr, 0, nullptr, nullptr,
+                                        nullptr, nullptr, nullptr, nullptr, G);
+  return pb.workspace_bytes();
+}
+
+size_t mxg_chain_workspace_bytes(const mxg_chain* c) {
+  if (!c || c->M < 1 || c->M > MXG_MAX_ROWS) return mxg::kCtrBytes;
+  const int G = mxg::stage_grid();
+  if (G <= 0) return mxg::kCtrBytes;
+  mxg_chain probe = *c;
+  probe.workspace = nullptr;
+  mxg::ProgramBuilder pb = chain_program(probe, G);
+  return pb.workspace_bytes();
+}
 
 int mxfp8_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* q, uint8_t* s,
                    void* stream) {
@@ -120,8 +202,26 @@ int mxfp8_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* x_bf16, int64_t 
                          workspace);
   if (st != MXG_OK) return st;
   if ((st = check_device()) != MXG_OK) return st;
+  if (use_stage_kernel((int)M, (int)N, (int)K, x_bf16 != nullptr)) {
+    const int G = mxg::stage_grid();
+    if (G <= 0) return MXG_ERR_DEVICE;
+    mxg::ProgramBuilder pb = gemm_program((int)M, (int)N, (int)K, x_bf16, (int)ld_x, a_q, a_s,
+                                          w_q, w_s, out, reinterpret_cast<uint8_t*>(workspace), G);
+    return run_program(pb, (hipStream_t)stream);
+  }
   GemmArgs a{x_bf16, ld_x, a_q, a_s, w_q, w_s, out, (int)M, (int)N, (int)K};
   return launched(mxg::launch_gemm(a, (hipStream_t)stream));
+}
+
+int mxfp8_proj_chain(const mxg_chain* c, void* stream) {
+  if (!c) return MXG_ERR_NULL;
+  int st = validate_chain(c, mxg_chain_workspace_bytes(c));
+  if (st != MXG_OK) return st;
+  if ((st = check_device()) != MXG_OK) return st;
+  const int G = mxg::stage_grid();
+  if (G <= 0) return MXG_ERR_DEVICE;
+  mxg::ProgramBuilder pb = chain_program(*c, G);
+  return run_program(pb, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -55,7 +55,7 @@ P = lambda k: ctypes.c_void_p(A * (k + 1))
 
 
 def gemm(lib, M=4, N=1024, K=2048, x=None, ld_x=0, a_q=P(1), a_s=P(2), w_q=P(3), w_s=P(4),
-         out=P(5), ws=None, ws_bytes=0):
+         out=P(5), ws=P(7), ws_bytes=1 << 30):
     return lib.mxfp8_gemm(M, N, K, x, ld_x, a_q, a_s, w_q, w_s, out, ws, ws_bytes, None)
 
 
@@ -67,6 +67,7 @@ def gemm(lib, M=4, N=1024, K=2048, x=None, ld_x=0, a_q=P(1), a_s=P(2), w_q=P(3),
     (dict(a_q=ctypes.c_void_p(A + 8)), 2), (dict(w_q=ctypes.c_void_p(A + 1)), 2),
     (dict(out=ctypes.c_void_p(A + 4)), 2),
     (dict(x=ctypes.c_void_p(A + 2), ld_x=2048), 2), (dict(x=P(6), ld_x=2052), 2),
+    (dict(ws=None), 4), (dict(ws_bytes=16), 4), (dict(ws=ctypes.c_void_p(A + 4)), 2),
 ])
 def test_gemm_rejects(lib, kw, status):
     assert gemm(lib, **kw) == status
@@ -90,3 +91,29 @@ def test_forced_foreign_arch_is_rejected_before_launch(lib, monkeypatch):
     monkeypatch.setenv("MXG_FORCE_ARCH", "gfx942")
     assert gemm(lib) == 5
     assert lib.mxfp8_quantize(P(0), 4, 64, 64, P(1), P(2), None) == 5
+
+
+def test_workspace_size_is_positive(lib):
+    assert lib.mxg_gemm_workspace_bytes(4, 1024, 2048) >= 256
+
+
+def test_chain_rejects_before_launch(lib):
+    # Every call below fails validation; the valid base chain is never passed.
+    import mxfp8_block_scaled_gemm_amd as mx
+    w = lambda k, N, K: mx.MxgWeight(A * k, A * (k + 1), N, K)
+    c = mx.MxgChain(8, A, A, w(2, 2048, 5120), w(4, 8192, 1536), w(6, 5120, 8192), A * 8, A * 9,
+                    A * 10, A * 11, A * 12, A * 13, A * 14, A * 15, 1 << 30)
+    for field, value, status in (("M", 0, 3), ("M", 49, 3), ("out_b", None, 1),
+                                 ("workspace", None, 4), ("workspace_bytes", 8, 4)):
+        bad = mx.MxgChain.from_buffer_copy(c)
+        setattr(bad, field, value)
+        assert lib.mxfp8_proj_chain(ctypes.byref(bad), None) == status, field
+    bad = mx.MxgChain.from_buffer_copy(c)
+    bad.wB = w(4, 8192, 100)                  # K % 128 != 0
+    assert lib.mxfp8_proj_chain(ctypes.byref(bad), None) == 3
+    bad = mx.MxgChain.from_buffer_copy(c)
+    bad.wB = w(4, 8192, 4096)                 # requantized width beyond A's output
+    assert lib.mxfp8_proj_chain(ctypes.byref(bad), None) == 3
+    bad = mx.MxgChain.from_buffer_copy(c)
+    bad.a_q = A + 8
+    assert lib.mxfp8_proj_chain(ctypes.byref(bad), None) == 2

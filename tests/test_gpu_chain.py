@@ -1,0 +1,112 @@
+"""GPU parity of mxfp8_proj_chain (three projections in one launch) against
+the oracle's chain, in the decode step's order: A on the MXFP8 layer input,
+the leading columns of A's output requantized for B, C on its own input.
+
+Unique results are compared with the oracle directly (A's and C's outputs,
+every code from a BF16 input).  A's BF16 output is only determined to within
+the GEMM tolerance, so the requantized codes are checked for validity (they
+must be exactly the quantization of the GPU's own A output), and B's output
+is compared end to end with the oracle on every row whose requantized codes
+match the oracle's, and stage-wise on the others."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_block_scaled_gemm_amd as mx
+import oracle
+import synth
+from helpers import check_gemm, dev_bf16, host_bits, host_u8, say
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {"A": (256, 512), "B": (384, 128), "C": (320, 640)}
+
+
+def _prep(case):
+    """GPU and oracle quantization of every input (must agree bit for bit)."""
+    g, o = {}, {}
+    for name in ("x_a", "x_c", "w_a", "w_b", "w_c"):
+        bits = synth.bits(case[name])
+        o[name] = oracle.quantize(bits)
+        q, s = mx.mxfp8_quantize(dev_bf16(bits))
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u8(q), o[name][0]) and np.array_equal(host_u8(s), o[name][1]), name
+        g[name] = (q, s) if name.startswith("x") else mx.PackedWeight.from_rows(q, s)
+    return g, o
+
+
+def run_chain(M, dims=None, seed=0):
+    case = synth.chain_case(M, seed=seed, dims=dims)
+    d = case["dims"]
+    b_cols = d["B"][1]
+    g, o = _prep(case)
+    ref = oracle.chain(*o["x_a"], o["w_a"], b_cols, o["w_b"], *o["x_c"], o["w_c"])
+    say(f"chain M={M} dims={d} seed={seed}")
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    out_a, b_q, b_s, out_b, out_c = mx.mxfp8_proj_chain(*g["x_a"], g["w_a"], g["w_b"], *g["x_c"],
+                                                         g["w_c"], workspace=ws)
+    torch.cuda.synchronize()
+    assert mx.workspace_error(ws) == 0
+    assert not ws[:65536].any(), "counters must be back to zero"
+    check_gemm(out_a, ref.A, "A")
+    check_gemm(out_c, ref.C, "C")
+    a_bits = host_bits(out_a)
+    vq, vs = oracle.quantize(np.ascontiguousarray(a_bits[:, :b_cols]))
+    gq, gs = host_u8(b_q), host_u8(b_s)
+    assert np.array_equal(gq, vq) and np.array_equal(gs, vs), "requant must quantize A's output"
+    same = np.all(gq == ref.b_q, axis=1) & np.all(gs == ref.b_s, axis=1)
+    out_b_bits = host_bits(out_b)
+    if same.any():
+        got = oracle.bf16_value(out_b_bits[same])
+        assert np.all(np.abs(got - ref.B.ref[same]) <= ref.B.tolerance()[same])
+    stage = oracle.gemm(gq, gs, o["w_b"][0], o["w_b"][1])
+    check_gemm(out_b, stage, "B (stage-wise)")
+    frac = 1.0 - np.mean(gq == ref.b_q)
+    assert frac < 0.02, f"{frac:.4f} of requantized codes differ from the end-to-end oracle"
+    return g, (out_a, b_q, b_s, out_b, out_c), ws
+
+
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 32, 48])
+def test_chain_small(M):
+    run_chain(M, dims=SMALL, seed=M)
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_chain_full_size(M):
+    run_chain(M)
+
+
+def test_chain_deterministic_and_equal_to_separate_calls(monkeypatch):
+    monkeypatch.setenv("MXG_GEMM_PATH", "stage")
+    g, outs, ws = run_chain(8)
+    first = [t.clone() for t in outs]
+    for _ in range(20):
+        again = mx.mxfp8_proj_chain(*g["x_a"], g["w_a"], g["w_b"], *g["x_c"], g["w_c"], workspace=ws)
+        for a, b in zip(first, again):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    # the same GEMMs issued one by one through the stage kernel give the same bits
+    out_a = mx.mxfp8_gemm(*g["x_a"], g["w_a"], workspace=ws)
+    b_q, b_s = mx.mxfp8_quantize(out_a, K=g["w_b"].K)
+    out_b = mx.mxfp8_gemm(b_q, b_s, g["w_b"], workspace=ws)
+    out_c = mx.mxfp8_gemm(*g["x_c"], g["w_c"], workspace=ws)
+    torch.cuda.synchronize()
+    names = ("out_a", "b_q", "b_s", "out_b", "out_c")
+    for name, a, b in zip(names, first, (out_a, b_q, b_s, out_b, out_c)):
+        diff = (a.view(torch.uint8) != b.view(torch.uint8))
+        if diff.any():
+            idx = torch.nonzero(diff)[:8].tolist()
+            say(f"{name}: {int(diff.sum())} bytes differ, first {idx}, "
+                f"max |d| {(a.float() - b.float()).abs().max().item() if a.dtype == torch.bfloat16 else -1}")
+        assert not diff.any(), name
+
+
+def test_chain_rejects_bad_shapes():
+    g, _ = _prep(synth.chain_case(2, dims=SMALL))
+    bad = mx.PackedWeight(g["w_b"].q, g["w_b"].s, g["w_b"].N, 100)   # K not a multiple of 128
+    with pytest.raises(ValueError):
+        mx.mxfp8_proj_chain(*g["x_a"], g["w_a"], bad, *g["x_c"], g["w_c"],
+                            outs=(torch.empty(2, 256, dtype=torch.bfloat16, device="cuda"),
+                                  torch.empty(2, 100, dtype=torch.uint8, device="cuda"),
+                                  torch.empty(2, 3, dtype=torch.uint8, device="cuda"),
+                                  torch.empty(2, 384, dtype=torch.bfloat16, device="cuda"),
+                                  torch.empty(2, 320, dtype=torch.bfloat16, device="cuda")))

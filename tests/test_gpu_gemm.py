@@ -16,6 +16,13 @@ from helpers import check_gemm, dev_bf16, dev_u8, host_bits, host_u8, say
 
 pytestmark = pytest.mark.gpu
 
+
+@pytest.fixture(params=["stage", "direct"])
+def path(request, monkeypatch):
+    """Run a test through the persistent stage kernel and the direct kernels."""
+    monkeypatch.setenv("MXG_GEMM_PATH", request.param)
+    return request.param
+
 _wcache = {}
 
 
@@ -60,32 +67,32 @@ def run_case(M, N, K, seed=0, outliers=False, fused=False):
 # small shapes: several workgroups, every row bucket and its edges
 @pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 15, 16, 17, 31, 32, 33, 47, 48])
 @pytest.mark.parametrize("fused", [False, True])
-def test_rows_sweep(M, fused):
+def test_rows_sweep(M, fused, path):
     run_case(M, 256, 1024, seed=M, fused=fused)
 
 
 @pytest.mark.parametrize("N,K", [(16, 128), (48, 384), (1024, 128), (128, 8192), (2064, 1664)])
 @pytest.mark.parametrize("fused", [False, True])
-def test_shapes(N, K, fused):
+def test_shapes(N, K, fused, path):
     for M in (1, 20, 48):
         run_case(M, N, K, seed=N + K, fused=fused)
 
 
-def test_single_gemm_config():
+def test_single_gemm_config(path):
     # M=4, N=1024, K=2048, x ~ N(0,1), W ~ N(0,0.02), seed 0
     run_case(4, 1024, 2048, seed=0)
     run_case(4, 1024, 2048, seed=0, fused=True)
 
 
 @pytest.mark.parametrize("M", [1, 2, 4, 8])
-def test_decode_bucket_full_size(M):
+def test_decode_bucket_full_size(M, path):
     # N=4096, K=5120 with the activation quantize fused into the GEMM launch
     run_case(M, 4096, 5120, seed=0, fused=True)
 
 
 @pytest.mark.parametrize("N,K", [(4096, 5120), (5120, 8192), (8192, 1536)])
 @pytest.mark.parametrize("M", [16, 32, 48])
-def test_wide_tiles_full_size_outliers(M, N, K):
+def test_wide_tiles_full_size_outliers(M, N, K, path):
     run_case(M, N, K, seed=0, outliers=True)
 
 
@@ -126,7 +133,7 @@ def test_zero_activations_give_positive_zero():
     assert (out.view(torch.int16) == 0).all()
 
 
-def test_deterministic_repeats():
+def test_deterministic_repeats(path):
     M, N, K = 8, 4096, 5120
     w, _ = _weights(N, K, 0)
     x = synth.gemm_case(M, 16, K, seed=1)["x"].cuda()
@@ -188,3 +195,28 @@ def test_pack_is_the_documented_permutation(N, K):
     torch.cuda.synchronize()
     rq, rs = _pack_reference(wq, ws)
     assert np.array_equal(host_u8(pq), rq) and np.array_equal(host_u8(ps), rs)
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 4096, 5120), (4, 5120, 8192), (33, 2048, 5120)])
+def test_workspace_left_clean(M, N, K, monkeypatch):
+    """Repeated stage-kernel calls (distributed quantize, K-split tiles) on one
+    workspace keep working: every counter is reset by the call that used it
+    (a stale tile counter would make the next call's wait expire and set the
+    error word), and the results stay bitwise identical."""
+    monkeypatch.setenv("MXG_GEMM_PATH", "stage")
+    w, _ = _weights(N, K, 0)
+    ws = torch.zeros(int(mx.lib().mxg_gemm_workspace_bytes(M, N, K)) + 4096, dtype=torch.uint8,
+                     device="cuda")
+    x = synth.gemm_case(M, 16, K, seed=2)["x"].cuda()
+    a_q = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+    a_s = torch.empty(M, K // 32, dtype=torch.uint8, device="cuda")
+    say(f"workspace hygiene M={M} N={N} K={K}")
+    first = mx.mxfp8_gemm(a_q, a_s, w, x=x, workspace=ws).clone()
+    for _ in range(3):
+        o1 = mx.mxfp8_gemm(a_q, a_s, w, x=x, workspace=ws)
+        assert torch.equal(o1.view(torch.int16), first.view(torch.int16))
+        o2 = mx.mxfp8_gemm(a_q, a_s, w, workspace=ws)
+        assert torch.equal(o2.view(torch.int16), first.view(torch.int16))
+    torch.cuda.synchronize()
+    assert mx.workspace_error(ws) == 0
+    assert not ws[:65536].any(), "counters must be back to zero"
