@@ -125,6 +125,56 @@ def decode_bucket(dev, steps: int, warmup: int, stream):
     }
 
 
+def roofline_kernel(dev, stream, reps: int = 600):
+    """The dominant kernel alone: the M=8 GEMM on MXFP8 activations (what the
+    M=8 step runs after its quantize launch), rotated weights, one HIP graph
+    of `reps` launches timed with HIP events on its launch stream."""
+    N, K, M = 4096, 5120, 8
+    copies = weight_copies(N, K, dev)
+    x = synth.gemm_case(8, N, K, seed=0)["x"].to(dev)
+    aq, as_ = mx.mxfp8_quantize(x)
+    out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+
+    def call(i):
+        mx.mxfp8_gemm(aq, as_, copies[i % len(copies)], out=out)
+    with torch.cuda.stream(stream):
+        for i in range(20):
+            call(i)
+    us = time_graph(call, reps, stream) * 1e3 / reps
+    b = gemm_bytes(M, N, K, False)
+    return {"us": us, "bytes": b, "GBs": b / (us * 1e-6) / 1e9, "reps": reps}
+
+
+def chain_case(dev, stream, M: int, reps: int = 200):
+    """The three-projection chain in one launch (A 2048x5120, requantize 1536
+    columns, B 8192x1536, C 5120x8192), weights rotated over copies."""
+    case = synth.chain_case(M, seed=0)
+    w = {k: mx.PackedWeight.from_bf16(case[k].to(dev)) for k in ("w_a", "w_b", "w_c")}
+    per = sum(mx_bytes(v.N, v.K) for v in w.values())
+    n = max(2, math.ceil(ROTATE_BYTES / per))
+    cop = [{k: v.clone() for k, v in w.items()} for _ in range(n)]
+    a = mx.mxfp8_quantize(case["x_a"].to(dev))
+    c = mx.mxfp8_quantize(case["x_c"].to(dev))
+    outs = (torch.empty(M, 2048, dtype=torch.bfloat16, device=dev),
+            torch.empty(M, 1536, dtype=torch.uint8, device=dev),
+            torch.empty(M, 48, dtype=torch.uint8, device=dev),
+            torch.empty(M, 8192, dtype=torch.bfloat16, device=dev),
+            torch.empty(M, 5120, dtype=torch.bfloat16, device=dev))
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
+
+    def call(i):
+        cw = cop[i % n]
+        mx.mxfp8_proj_chain(*a, cw["w_a"], cw["w_b"], *c, cw["w_c"], outs=outs, workspace=ws)
+    with torch.cuda.stream(stream):
+        for i in range(10):
+            call(i)
+    us = time_graph(call, reps, stream) * 1e3 / reps
+    b = per + mx_bytes(M, 5120) + mx_bytes(M, 8192) + 2 * M * (2048 + 8192 + 5120) \
+        + 2 * M * 1536 + mx_bytes(M, 1536)
+    return {"us": round(us, 3), "GBs": round(b / (us * 1e-6) / 1e9, 1),
+            "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def extra_cases(dev, stream):
     """Latency of the other single-GEMM configurations (MXFP8 inputs)."""
     out = {}
@@ -151,6 +201,8 @@ def extra_cases(dev, stream):
                                      "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         del copies
         torch.cuda.empty_cache()
+    for M in (1, 8, 32):
+        out[f"chain M{M}"] = chain_case(dev, stream, M)
     return out
 
 
@@ -187,6 +239,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cases", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="only the dominant kernel's timing (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); the "
@@ -196,7 +250,19 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream()
+    if args.roofline_only:
+        # Calibration for the HBM byte counters: an elementwise kernel that
+        # reads and writes exactly 64 MiB each (float32 add), then the kernel.
+        src = torch.ones(16 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.add(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"roofline_kernel_us": roofline_kernel(dev, stream)["us"],
+                          "calibration_bytes_each_way": 64 << 20}), flush=True)
+        return
     rec = decode_bucket(dev, args.steps, args.warmup, stream)
+    roof = roofline_kernel(dev, stream)
     cases = {} if args.no_cases else extra_cases(dev, stream)
     cpu = None if args.no_cpu else cpu_baseline()
     line = {
@@ -217,12 +283,13 @@ def main():
                    "M": [1, 2, 4, 8], "N": 4096, "K": 5120,
                    "weight_copies": rec["copies"], "timing": "HIP graph of K steps, HIP events"},
         "us_per_gemm": rec["per_m"],
-        "roofline": {"bound": "hbm", "kernel": "gemm_m16_kernel<8,16,true>",
-                     "achieved": round(rec["kernel_GBs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(rec["kernel_GBs"] / HBM_PEAK_GBS, 4),
-                     "avg_launch_us": round(rec["kernel_us"], 3),
-                     "bytes_per_launch": int(rec["per_launch_bytes"]),
+        "roofline": {"bound": "hbm", "kernel": "gemm_m16_kernel<16,3,4,false> (M=8 N=4096 K=5120)",
+                     "achieved": round(roof["GBs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(roof["GBs"] / HBM_PEAK_GBS, 4),
+                     "avg_launch_us": round(roof["us"], 3),
+                     "bytes_per_launch": int(roof["bytes"]),
                      "traffic": None},
+        "step_avg_launch_us": round(rec["kernel_us"], 3),
         "cases": cases,
         "cpu_baseline": cpu,
     }

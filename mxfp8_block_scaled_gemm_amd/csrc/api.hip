@@ -91,17 +91,14 @@ int validate_chain(const mxg_chain* c, size_t need) {
   return MXG_OK;
 }
 
-// Kernel choice for a plain GEMM: the stage kernel when the activations come
-// as BF16 (distributed quantize), when the tiles need a K split to balance
-// the grid, or when forced; the direct kernels otherwise.  MXG_GEMM_PATH
-// ("stage" / "direct") forces a choice (tests use it to cover both).
-bool use_stage_kernel(int M, int N, int K, bool fq) {
+// Kernel choice for a single GEMM: the direct kernels (one 16-row weight
+// tile per workgroup, the whole weight stream issued at once) measure faster
+// than the stage kernel for every single-GEMM shape; the stage kernel serves
+// the multi-stage programs.  MXG_GEMM_PATH ("stage" / "direct") forces a
+// choice (tests use it to cover both).
+bool use_stage_kernel(int, int, int, bool) {
   const char* force = std::getenv("MXG_GEMM_PATH");
-  if (force && std::strcmp(force, "stage") == 0) return true;
-  if (force && std::strcmp(force, "direct") == 0) return false;
-  if (fq) return true;
-  const int G = mxg::stage_grid();
-  return G > 0 && mxg::choose_kparts(M, N, K, G) > 1;
+  return force && std::strcmp(force, "stage") == 0;
 }
 
 mxg::ProgramBuilder gemm_program(int M, int N, int K, const uint16_t* x, int ld_x, uint8_t* a_q,

@@ -377,11 +377,12 @@ static hipError_t launch_m16(const GemmArgs& a, hipStream_t stream) {
 
 template <int SPW, bool FQ>
 static hipError_t launch_m16_ch(const GemmArgs& a, int ch, hipStream_t stream) {
-  if (ch <= 2) return launch_m16<SPW, 2, FQ>(a, stream);
-  if (ch <= 4) return launch_m16<SPW, 4, FQ>(a, stream);
   if constexpr (FQ) {
-    return launch_m16<SPW, 8, FQ>(a, stream);
+    if (ch <= 2) return launch_m16<SPW, 2, FQ>(a, stream);
+    return launch_m16<SPW, 4, FQ>(a, stream);
   } else {
+    if (ch <= 2) return launch_m16<SPW, 2, FQ>(a, stream);
+    if (ch <= 4) return launch_m16<SPW, 4, FQ>(a, stream);
     if (ch <= 8) return launch_m16<SPW, 8, FQ>(a, stream);
     return launch_m16<SPW, 16, FQ>(a, stream);
   }
@@ -413,10 +414,11 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   const int ch = (per + kM16Waves * 64 - 1) / (kM16Waves * 64);
   if (gemm_m16_fits(a.M, a.K) && steps <= 4) {
     if (!fq && ch <= 16) return launch_m16_spw<false>(a, steps, ch, stream);
-    // In-kernel quantize while the weight stream is in flight, as long as
-    // the BF16 staging fits the registers (8 chunks per thread); larger
+    // In-kernel quantize while the weight stream is in flight when the
+    // activation is small (every workgroup quantizes all of it, which costs
+    // more than a separate launch from about 8 rows of 5120); larger
     // activations are quantized by their own launch first.
-    if (fq && ch <= 8) return launch_m16_spw<true>(a, steps, ch, stream);
+    if (fq && ch <= 4) return launch_m16_spw<true>(a, steps, ch, stream);
     if (fq) {
       hipError_t e = launch_quantize(a.x, a.M, a.K, a.ld_x, a.a_q, a.a_s, stream);
       if (e != hipSuccess) return e;

@@ -13,25 +13,34 @@ constexpr int kStageIoWaves = 4;        // dependency / activation / output wave
 constexpr int kStageThreads = (kStageStreamWaves + kStageIoWaves) * 64;
 constexpr int kStageStepsPerWave = 4;   // 128-K steps a stream wave holds per unit
 constexpr int kMaxStages = 4;
-constexpr int kStageLdsMax = 160 * 1024;
+constexpr int kStageLdsMax = 160 * 1024 - 64;   // dynamic LDS; a few static words follow
 
 constexpr int kStageQuant = 1;          // BF16 -> MXFP8 of a row range
 constexpr int kStageGemm = 2;           // (grouped) MXFP8 GEMM, BF16 out
 
 // Workspace layout: a fixed counter region, then K-split partial sums.
-// Counter words [0, kMaxStages) count stage completion, then the exit count
-// and the error word; K-split tile counters follow up to kCtrRegionBytes.
-// Every counter is back at zero when a call ends, and no program ever puts
-// partial sums in the counter region, so programs of any shape can share a
-// workspace one after another.
-constexpr int kCtrExit = kMaxStages;
-constexpr int kCtrError = kMaxStages + 1;
-constexpr size_t kCtrBytes = 256;
+//   word 5 (byte 20)          error word (an expired wait sets it)
+//   kArriveBase + (s*8+x)*128 arrivals of workgroup group x (b mod 8) that
+//                             finished stage s, one 128-byte line each
+//   kExitBase + x*128         exits of group x;  kExitTop: groups done
+//   kTileCtrBase ..           K-split tile counters
+// Arrivals are spread over 8 lines because same-address device atomics
+// serialize.  Every counter is back at zero when a call ends, and no program
+// puts partial sums in the counter region, so programs of any shape can
+// share a workspace one after another.
+constexpr int kGroups = 8;
+constexpr int kCtrError = 5;
+constexpr size_t kArriveBase = 256;
+constexpr size_t kExitBase = kArriveBase + (size_t)kMaxStages * kGroups * 128;
+constexpr size_t kExitTop = kExitBase + (size_t)kGroups * 128;
+constexpr size_t kTileCtrBase = 8192;
+constexpr size_t kCtrBytes = kTileCtrBase;
 constexpr size_t kCtrRegionBytes = 64 * 1024;
 
 struct StageDesc {
   int kind, dep, units, rot;
-  uint32_t done_target;        // completion count of this stage (4 per tile / unit)
+  int consumed;                // a later stage reads this stage's output
+  uint16_t arrive_target[kGroups];  // workgroups of each group with units here
   // GEMM
   int M, N, K, P, Sp, tiles, group_tiles;
   const uint8_t* wq;           // packed weight codes (all groups, N rows)
@@ -52,8 +61,9 @@ struct StageDesc {
 
 struct Program {
   int nstages, G;
+  int synced;                  // some stage is consumed: arrivals and exit counting run
   int lds_act_bytes, lds_scl_bytes;
-  uint32_t* ctr;               // workspace counters (kCtrBytes)
+  uint8_t* ws;                 // workspace (counter region first)
   StageDesc st[kMaxStages];
 };
 

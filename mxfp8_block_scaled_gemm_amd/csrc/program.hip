@@ -54,10 +54,10 @@ int stage_grid() {
 }
 
 ProgramBuilder::ProgramBuilder(int M, int G, uint8_t* ws)
-    : M_(M), ws_(ws), ctr_off_(kCtrBytes), off_(kCtrRegionBytes) {
+    : M_(M), ws_(ws), ctr_off_(kTileCtrBase), off_(kCtrRegionBytes) {
   pg_ = Program{};
   pg_.G = G;
-  pg_.ctr = reinterpret_cast<uint32_t*>(ws);
+  pg_.ws = ws;
 }
 
 uint32_t* ProgramBuilder::carve_counters(size_t n) {
@@ -87,7 +87,6 @@ int ProgramBuilder::add_quant(const uint16_t* x, int ld_x, int K, uint8_t* q, ui
   d.q = q;
   d.s = s;
   d.units = ceil_div(M_ * (K / 32), 64);
-  d.done_target = (uint32_t)(kStageIoWaves * d.units);
   return pg_.nstages++;
 }
 
@@ -114,7 +113,6 @@ int ProgramBuilder::add_gemm(int N, int K, const uint8_t* wq, const uint8_t* wsc
   d.P = std::max(1, choose_kparts(M_, N, K, pg_.G));
   d.Sp = ceil_div(K / 128, d.P);
   d.units = d.tiles * d.P;
-  d.done_target = (uint32_t)(kStageIoWaves * d.tiles);
   if (d.P > 1) {
     d.tile_ctr = carve_counters((size_t)d.tiles);
     d.part = reinterpret_cast<float*>(carve((size_t)d.tiles * d.P * mb() * 64 * 16));
@@ -137,6 +135,16 @@ bool ProgramBuilder::finish() {
     // more in one stage are not the same ones in the next.
     d.rot = rot;
     rot = (rot + d.units) % pg_.G;
+    // Workgroups b with units in this stage: (b - rot) mod G < units.
+    for (int x = 0; x < kGroups; ++x) d.arrive_target[x] = 0;
+    for (int b = 0; b < pg_.G; ++b) {
+      const int f = ((b - d.rot) % pg_.G + pg_.G) % pg_.G;
+      if (f < d.units) ++d.arrive_target[b % kGroups];
+    }
+    if (d.dep >= 0) {
+      pg_.st[d.dep].consumed = 1;
+      pg_.synced = 1;
+    }
   }
   pg_.lds_act_bytes = (int)((act + 15) & ~(size_t)15);
   pg_.lds_scl_bytes = (int)scl;
