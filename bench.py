@@ -38,6 +38,26 @@ MALL_BYTES = 256 << 20         # Infinity Cache
 ROTATE_BYTES = 512 << 20       # weight bytes cycled through before a copy is reused
 
 
+ROOFLINE_PROFILE = os.path.join(ROOT, "profiles", "gemm_m16_kernel_M8_N4096_K5120.md")
+ROOFLINE_SOURCES = [os.path.join(ROOT, "mxfp8_block_scaled_gemm_amd", "csrc", f)
+                    for f in ("gemm.hip", "mx_device.hpp")]
+
+
+def profiled_traffic():
+    """HBM bytes per launch of the roofline kernel from its committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated), or None when the kernel's
+    sources changed since the counters were taken."""
+    import hashlib
+    try:
+        fields = dict(l.split(":", 1) for l in open(ROOFLINE_PROFILE).read().splitlines()
+                      if l.startswith(("traffic_bytes_per_launch:", "sources_sha256:")))
+        want = fields["sources_sha256"].split()
+        have = [hashlib.sha256(open(f, "rb").read()).hexdigest() for f in ROOFLINE_SOURCES]
+        return int(fields["traffic_bytes_per_launch"]) if want == have else None
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def mx_bytes(rows: int, K: int) -> int:
     return rows * K + rows * (K // 32)
 
@@ -288,7 +308,7 @@ def main():
                      "frac": round(roof["GBs"] / HBM_PEAK_GBS, 4),
                      "avg_launch_us": round(roof["us"], 3),
                      "bytes_per_launch": int(roof["bytes"]),
-                     "traffic": None},
+                     "traffic": profiled_traffic()},
         "step_avg_launch_us": round(rec["kernel_us"], 3),
         "cases": cases,
         "cpu_baseline": cpu,
