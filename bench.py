@@ -166,8 +166,9 @@ def roofline_kernel(dev, stream, reps: int = 600):
 
 
 def chain_case(dev, stream, M: int, reps: int = 200):
-    """The three-projection chain in one launch (A 2048x5120, requantize 1536
-    columns, B 8192x1536, C 5120x8192), weights rotated over copies."""
+    """The three-projection chain (A 2048x5120, requantize 1536 columns, B
+    8192x1536, C 5120x8192), weights rotated over copies; the library's
+    default chain path unless MXG_CHAIN_PATH says otherwise."""
     case = synth.chain_case(M, seed=0)
     w = {k: mx.PackedWeight.from_bf16(case[k].to(dev)) for k in ("w_a", "w_b", "w_c")}
     per = sum(mx_bytes(v.N, v.K) for v in w.values())
@@ -223,7 +224,48 @@ def extra_cases(dev, stream):
         torch.cuda.empty_cache()
     for M in (1, 8, 32):
         out[f"chain M{M}"] = chain_case(dev, stream, M)
+    os.environ["MXG_CHAIN_PATH"] = "stage"
+    try:
+        for M in (1, 8, 32):
+            out[f"chain M{M} (one stage-kernel launch)"] = chain_case(dev, stream, M)
+    finally:
+        del os.environ["MXG_CHAIN_PATH"]
+    for M in (1, 4, 16):
+        out[f"wo_a+wo_b M{M}"] = wo_a_case(dev, stream, M)
     return out
+
+
+def wo_a_case(dev, stream, M: int, reps: int = 200):
+    """Rotary + grouped WO-A (8 groups of 8 heads x 512 dims, rank 1024) +
+    MXFP8 of z + wo_b 5120x8192, weights rotated over copies."""
+    case = synth.wo_a_case(M, seed=0)
+    d = case["dims"]
+    G, R = d["n_groups"], d["rank"]
+    wa = mx.PackedWeight.from_bf16(case["w_a"].reshape(G * R, -1).to(dev))
+    wb = mx.PackedWeight.from_bf16(case["w_b"].to(dev))
+    per = mx_bytes(wa.N, wa.K) + mx_bytes(wb.N, wb.K)
+    n = max(2, math.ceil(ROTATE_BYTES / per))
+    cop = [(wa.clone(), wb.clone()) for _ in range(n)]
+    o = case["o"].to(dev)
+    pos = case["positions"].to(dev)
+    cs = torch.from_numpy(case["cos_sin"]).to(dev)
+    outs = (None, torch.empty(M, G * R, dtype=torch.uint8, device=dev),
+            torch.empty(M, G * R // 32, dtype=torch.uint8, device=dev),
+            torch.empty(M, wb.N, dtype=torch.bfloat16, device=dev))
+    ws = torch.zeros(16 << 20, dtype=torch.uint8, device=dev)
+
+    def call(i):
+        a, b = cop[i % n]
+        mx.wo_a_fused_quantize(o, pos, cs, a, n_groups=G, nope_dim=d["nope"], wb=b, outs=outs,
+                               workspace=ws)
+    with torch.cuda.stream(stream):
+        for i in range(10):
+            call(i)
+    us = time_graph(call, reps, stream) * 1e3 / reps
+    H, D = d["n_heads"], d["head_dim"]
+    b = per + 2 * M * H * D + 8 * M + 4 * M * (D - d["nope"]) + mx_bytes(M, G * R) + 2 * M * wb.N
+    return {"us": round(us, 3), "GBs": round(b / (us * 1e-6) / 1e9, 1),
+            "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def cpu_baseline(min_seconds: float = 10.0):

@@ -158,7 +158,7 @@ typedef struct {
 } mxg_weight;
 
 /*
- * mxfp8_proj_chain -- three projections back to back in one launch, in the
+ * mxfp8_proj_chain -- three projections back to back, in the
  * order of a decode step's attention ([step] page, AttentionStep.run:
  * fused_wqa_wkv on the MXFP8 layer input, the leading columns of its output
  * requantized to MXFP8 for wq_b, and wo_b on its own MXFP8 input):
@@ -194,6 +194,81 @@ int mxfp8_proj_chain(const mxg_chain *chain, void *stream);
 
 /* Workspace bytes mxfp8_proj_chain needs (pointers in *chain are not read). */
 size_t mxg_chain_workspace_bytes(const mxg_chain *chain);
+
+/*
+ * wo_a_fused_quantize -- the grouped WO-A projection with rotary embedding in
+ * front and MXFP8 of its output behind, optionally followed by wo_b ([o_proj]
+ * page, dsv41_o_proj: the fused WO-A kernel returns the MXFP8 codes and
+ * scales that wo_b takes as its input; _can_fuse_wo_a: FP8 WO-A with per-32
+ * scales, at most 8 heads per group, 448 + 64 head dims, o_lora_rank a
+ * multiple of 128).  For each row m (token):
+ *   1. y = o[m] with the last rope = D - nope dims of every head rotated by
+ *      positions[m]: pair i = dims (nope + 2i, nope + 2i + 1), angle row
+ *      cos_sin[positions[m]] = [cos theta_0 .. cos theta_{rope/2-1},
+ *      sin theta_0 .. sin theta_{rope/2-1}], y1 = x1 cos - x2 sin,
+ *      y2 = x2 cos + x1 sin in FP32 without fused multiply-add, rounded to
+ *      BF16; the nope dims pass through.
+ *   2. group g (heads g*hpg .. g*hpg + hpg - 1, hpg = H/G) is the hpg*D
+ *      values of those heads, concatenated, quantized to MXFP8 as
+ *      mxfp8_quantize does;
+ *   3. z[m, g*R + r] = BF16 of that group input times row g*R + r of wa
+ *      (R = wa.N / G), i.e. the G group outputs concatenated;
+ *   4. (z_q, z_s) = MXFP8 of z, as mxfp8_quantize does;
+ *   5. if wb.q != NULL: out = dequant(z_q, z_s) . dequant(wb)^T, BF16.
+ * Every intermediate is rounded to BF16 before it is quantized, as in the
+ * unfused path (rotary output, z).
+ *
+ *   M           1 <= M <= MXG_MAX_ROWS
+ *   o           BF16 attention output; head h of row m starts at
+ *               o + m*ld_row + h*ld_head, its D values contiguous
+ *   ld_row, ld_head
+ *               strides in elements: ld_head >= D, ld_row >= (H-1)*ld_head + D,
+ *               both multiples of 8
+ *   positions   int64 [M] token positions, each in [0, max_pos)
+ *   cos_sin     FP32 [max_pos, rope] angle table as above (16-byte aligned)
+ *   n_heads H, head_dim D, nope_dim, n_groups G
+ *               H % G == 0, H/G <= 8, D and nope multiples of 32,
+ *               0 < nope < D (rope = D - nope)
+ *   wa          packed MXFP8 weight (mxfp8_pack_weights) with N = G*R rows,
+ *               group g = rows [g*R, g*R + R), and K = hpg*D; R % 128 == 0
+ *   z           optional out: BF16 [M, G*R] (NULL: kept in the workspace)
+ *   z_q, z_s    out: MXFP8 of z, [M, G*R] codes, [M, G*R/32] scale bytes
+ *   wb, out     optional wo_b: packed weight with K = G*R, N % 16 == 0, and
+ *               its BF16 output [M, wb.N]; wb.q == NULL skips step 5
+ *   workspace, workspace_bytes
+ *               at least mxg_wo_a_workspace_bytes() bytes, zero-filled once
+ *               when allocated.  After a call, bytes [65536, 65536 + M*H*D)
+ *               hold the MXFP8 codes of the rotated input [M, H*D] (step 2)
+ *               and its scale bytes [M, H*D/32] follow at the next multiple
+ *               of 256; without z, z follows them.  Byte offset 20 is an error word: bit 1
+ *               is set when a position is outside [0, max_pos); that row then
+ *               uses angle row 0 and its results are not meaningful.  The
+ *               word is never cleared by the library.  Calls sharing a
+ *               workspace must not overlap.
+ * Validation happens before any launch; positions are device data, so their
+ * range is the one check made on the device.
+ */
+typedef struct {
+  int64_t M;
+  const uint16_t *o;
+  int64_t ld_row, ld_head;
+  const int64_t *positions;
+  const float *cos_sin;
+  int64_t max_pos;
+  int32_t n_heads, head_dim, nope_dim, n_groups;
+  mxg_weight wa;
+  uint16_t *z;
+  uint8_t *z_q, *z_s;
+  mxg_weight wb;
+  uint16_t *out;
+  void *workspace;
+  size_t workspace_bytes;
+} mxg_wo_a;
+
+int wo_a_fused_quantize(const mxg_wo_a *p, void *stream);
+
+/* Workspace bytes wo_a_fused_quantize needs (pointers in *p are not read). */
+size_t mxg_wo_a_workspace_bytes(const mxg_wo_a *p);
 
 #ifdef __cplusplus
 }

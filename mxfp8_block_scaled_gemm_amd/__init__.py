@@ -39,6 +39,19 @@ class MxgChain(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class MxgWoA(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("o", ctypes.c_void_p),
+                ("ld_row", ctypes.c_int64), ("ld_head", ctypes.c_int64),
+                ("positions", ctypes.c_void_p), ("cos_sin", ctypes.c_void_p),
+                ("max_pos", ctypes.c_int64),
+                ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("nope_dim", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("wa", MxgWeight), ("z", ctypes.c_void_p),
+                ("z_q", ctypes.c_void_p), ("z_s", ctypes.c_void_p),
+                ("wb", MxgWeight), ("out", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 class MxgError(ValueError):
     """A libmxgemm call returned a non-zero status."""
 
@@ -73,6 +86,10 @@ def lib() -> ctypes.CDLL:
         L.mxfp8_proj_chain.restype = ctypes.c_int
         L.mxg_chain_workspace_bytes.argtypes = [ctypes.POINTER(MxgChain)]
         L.mxg_chain_workspace_bytes.restype = sz
+        L.wo_a_fused_quantize.argtypes = [ctypes.POINTER(MxgWoA), vp]
+        L.wo_a_fused_quantize.restype = ctypes.c_int
+        L.mxg_wo_a_workspace_bytes.argtypes = [ctypes.POINTER(MxgWoA)]
+        L.mxg_wo_a_workspace_bytes.restype = sz
         _lib = L
     return _lib
 
@@ -124,7 +141,8 @@ def get_workspace(device, nbytes: int) -> torch.Tensor:
 
 
 def workspace_error(ws: torch.Tensor) -> int:
-    """The error word of a workspace (non-zero: an in-kernel wait expired)."""
+    """The error word of a workspace (non-zero: an in-kernel wait expired, or
+    for wo_a_fused_quantize bit 1: a position outside the angle table)."""
     return int(ws[20:24].view(torch.int32).item())
 
 
@@ -256,3 +274,58 @@ def mxfp8_proj_chain(a_q: torch.Tensor, a_s: torch.Tensor, wA: PackedWeight, wB:
     c.workspace_bytes = workspace.numel() * workspace.element_size()
     _check(lib().mxfp8_proj_chain(ctypes.byref(c), _stream(stream)))
     return out_a, b_q, b_s, out_b, out_c
+
+
+WO_A_ROTARY_OFFSET = 65536    # workspace byte offset of the rotated input's codes
+
+
+def wo_a_rotary_codes(workspace: torch.Tensor, M: int, HD: int):
+    """Views of the MXFP8 rotated input that wo_a_fused_quantize leaves in its
+    workspace: codes [M, HD] and scale bytes [M, HD/32]."""
+    q0 = WO_A_ROTARY_OFFSET
+    s0 = (q0 + M * HD + 255) // 256 * 256
+    return (workspace[q0:q0 + M * HD].view(M, HD),
+            workspace[s0:s0 + M * HD // 32].view(M, HD // 32))
+
+
+def wo_a_fused_quantize(o: torch.Tensor, positions: torch.Tensor, cos_sin: torch.Tensor,
+                        wa: PackedWeight, *, n_groups: int, nope_dim: int,
+                        wb: PackedWeight | None = None, outs=None, keep_z: bool = True,
+                        workspace: torch.Tensor | None = None, stream=None):
+    """Grouped WO-A with rotary in front and MXFP8 of its output behind,
+    optionally followed by wo_b.
+
+    ``o``: BF16 [M, H, D] (any row and head strides, D contiguous);
+    ``positions``: int64 [M]; ``cos_sin``: float32 [max_pos, D - nope_dim];
+    ``wa``: packed [G*R, (H/G)*D].  Returns (z or None, z_q, z_s, out or None)."""
+    if o.dim() != 3 or o.dtype != torch.bfloat16 or not o.is_cuda or o.stride(2) != 1:
+        raise ValueError("o must be a BF16 [M, H, D] device tensor with contiguous last dim")
+    M, H, D = o.shape
+    dev = o.device
+    GR = wa.N
+    _expect(positions, torch.int64, "positions", (M,))
+    _expect(cos_sin, torch.float32, "cos_sin")
+    if outs is None:
+        outs = (torch.empty(M, GR, dtype=torch.bfloat16, device=dev) if keep_z else None,
+                torch.empty(M, GR, dtype=torch.uint8, device=dev),
+                torch.empty(M, GR // 32, dtype=torch.uint8, device=dev),
+                torch.empty(M, wb.N, dtype=torch.bfloat16, device=dev) if wb is not None else None)
+    z, z_q, z_s, out = outs
+    if z is not None:
+        _expect(z, torch.bfloat16, "z", (M, GR))
+    _expect(z_q, torch.uint8, "z_q", (M, GR))
+    _expect(z_s, torch.uint8, "z_s", (M, GR // 32))
+    if wb is not None:
+        _expect(out, torch.bfloat16, "out", (M, wb.N))
+    p = MxgWoA(M, o.data_ptr(), o.stride(0), o.stride(1), positions.data_ptr(),
+               cos_sin.data_ptr(), cos_sin.shape[0], H, D, nope_dim, n_groups, _w(wa),
+               z.data_ptr() if z is not None else None, z_q.data_ptr(), z_s.data_ptr(),
+               _w(wb) if wb is not None else MxgWeight(None, None, 0, 0),
+               out.data_ptr() if wb is not None else None, None, 0)
+    need = int(lib().mxg_wo_a_workspace_bytes(ctypes.byref(p)))
+    if workspace is None:
+        workspace = get_workspace(dev, need)
+    p.workspace = workspace.data_ptr()
+    p.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().wo_a_fused_quantize(ctypes.byref(p), _stream(stream)))
+    return z, z_q, z_s, out

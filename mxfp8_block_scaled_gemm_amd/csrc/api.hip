@@ -123,6 +123,106 @@ mxg::ProgramBuilder chain_program(const mxg_chain& c, int G) {
   return pb;
 }
 
+// Chain kernel choice: by default three direct launches in stream order (B
+// quantizes A's output while staging it); MXG_CHAIN_PATH=stage runs the
+// whole chain as one stage-kernel launch.
+bool chain_on_stage_kernel() {
+  const char* force = std::getenv("MXG_CHAIN_PATH");
+  return force && std::strcmp(force, "stage") == 0;
+}
+
+int chain_direct(const mxg_chain& c, hipStream_t stream) {
+  const int M = (int)c.M;
+  GemmArgs a{nullptr, 0, const_cast<uint8_t*>(c.a_q), const_cast<uint8_t*>(c.a_s), c.wA.q, c.wA.s,
+             c.out_a, M, (int)c.wA.N, (int)c.wA.K};
+  hipError_t e = mxg::launch_gemm(a, stream);
+  if (e != hipSuccess) return MXG_ERR_DEVICE;
+  GemmArgs b{c.out_a, c.wA.N, c.b_q, c.b_s, c.wB.q, c.wB.s, c.out_b, M, (int)c.wB.N, (int)c.wB.K};
+  if ((e = mxg::launch_gemm(b, stream)) != hipSuccess) return MXG_ERR_DEVICE;
+  GemmArgs cc{nullptr, 0, const_cast<uint8_t*>(c.c_q), const_cast<uint8_t*>(c.c_s), c.wC.q,
+              c.wC.s, c.out_c, M, (int)c.wC.N, (int)c.wC.K};
+  return launched(mxg::launch_gemm(cc, stream));
+}
+
+// ------------------------------------------------------------------ WO-A
+
+struct WoALayout {
+  size_t xq, xs, z, end;   // workspace offsets
+};
+
+WoALayout wo_a_layout(const mxg_wo_a& p) {
+  const size_t M = (size_t)p.M, HD = (size_t)p.n_heads * (size_t)p.head_dim;
+  const size_t GR = (size_t)p.wa.N;
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  WoALayout l;
+  l.xq = mxg::kCtrRegionBytes;
+  l.xs = up(l.xq + M * HD);
+  l.z = up(l.xs + M * HD / 32);
+  l.end = up(l.z + (p.z ? 0 : 2 * M * GR));
+  return l;
+}
+
+bool wo_a_shape_ok(const mxg_wo_a& p) {
+  const int64_t H = p.n_heads, D = p.head_dim, nope = p.nope_dim, G = p.n_groups;
+  if (p.M < 1 || p.M > MXG_MAX_ROWS || H < 1 || G < 1 || H % G != 0 || H / G > 8) return false;
+  if (D < 64 || D % 32 != 0 || nope < 32 || nope >= D || nope % 32 != 0 || D > 4096) return false;
+  if (H * D > ((int64_t)1 << 20) || p.max_pos < 1 || p.max_pos > ((int64_t)1 << 31) / (D - nope))
+    return false;
+  if (p.ld_head < D || p.ld_row < (H - 1) * p.ld_head + D) return false;
+  if ((p.M - 1) * p.ld_row + H * p.ld_head > ((int64_t)1 << 40)) return false;
+  if (!weight_ok(p.wa) || p.wa.N % G != 0 || (p.wa.N / G) % 128 != 0 || p.wa.K != (H / G) * D)
+    return false;
+  if (p.wb.q && (!weight_ok(p.wb) || p.wb.K != p.wa.N)) return false;
+  return true;
+}
+
+int validate_wo_a(const mxg_wo_a* p) {
+  if (!p) return MXG_ERR_NULL;
+  if (!p->o || !p->positions || !p->cos_sin || !p->wa.q || !p->wa.s || !p->z_q || !p->z_s)
+    return MXG_ERR_NULL;
+  if (p->wb.q && (!p->wb.s || !p->out)) return MXG_ERR_NULL;
+  if (!wo_a_shape_ok(*p)) return MXG_ERR_SHAPE;
+  const void* ptrs[] = {p->o, p->cos_sin, p->wa.q, p->wa.s, p->z_q, p->z_s};
+  for (const void* q : ptrs)
+    if (!aligned16(q)) return MXG_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(p->positions) & 7u) || p->ld_row % 8 || p->ld_head % 8)
+    return MXG_ERR_ALIGN;
+  if (p->z && !aligned16(p->z)) return MXG_ERR_ALIGN;
+  if (p->wb.q && (!aligned16(p->wb.q) || !aligned16(p->wb.s) || !aligned16(p->out)))
+    return MXG_ERR_ALIGN;
+  if (!p->workspace || p->workspace_bytes < wo_a_layout(*p).end) return MXG_ERR_WORKSPACE;
+  if (!aligned16(p->workspace)) return MXG_ERR_ALIGN;
+  return MXG_OK;
+}
+
+int wo_a_run(const mxg_wo_a& p, hipStream_t stream) {
+  uint8_t* ws = reinterpret_cast<uint8_t*>(p.workspace);
+  const WoALayout l = wo_a_layout(p);
+  const int M = (int)p.M, H = p.n_heads, D = p.head_dim, G = p.n_groups;
+  const int HD = H * D, GR = (int)p.wa.N, R = GR / G, Kg = (int)p.wa.K;
+  uint8_t* xq = ws + l.xq;
+  uint8_t* xs = ws + l.xs;
+  uint16_t* z = p.z ? p.z : reinterpret_cast<uint16_t*>(ws + l.z);
+  // 1-2. rotary + MXFP8 of every head, groups side by side in each row.
+  mxg::RopeQuantArgs rq{p.o, p.ld_row, p.ld_head, p.positions, p.cos_sin, p.max_pos, xq, xs,
+                        reinterpret_cast<uint32_t*>(ws + 4 * mxg::kCtrError), M, H, D,
+                        p.nope_dim};
+  hipError_t e = mxg::launch_rope_quant(rq, stream);
+  if (e != hipSuccess) return MXG_ERR_DEVICE;
+  // 3. grouped projection: weight tile t reads group t / (R/16)'s columns.
+  GemmArgs ga{nullptr, 0, xq, xs, p.wa.q, p.wa.s, z, M, GR, Kg};
+  ga.lda = HD;
+  ga.group_tiles = R / 16;
+  ga.a_group = Kg;
+  if ((e = mxg::launch_gemm(ga, stream)) != hipSuccess) return MXG_ERR_DEVICE;
+  // 4-5. MXFP8 of z, written by wo_b's GEMM when there is one.
+  if (p.wb.q) {
+    GemmArgs gb{z, GR, p.z_q, p.z_s, p.wb.q, p.wb.s, p.out, M, (int)p.wb.N, (int)p.wb.K};
+    return launched(mxg::launch_gemm(gb, stream));
+  }
+  return launched(mxg::launch_quantize(z, M, GR, GR, p.z_q, p.z_s, stream));
+}
+
 int run_program(mxg::ProgramBuilder& pb, hipStream_t stream) {
   if (!pb.finish()) return MXG_ERR_SHAPE;
   return launched(mxg::launch_program(pb.program(), pb.mb(), stream));
@@ -215,10 +315,23 @@ int mxfp8_proj_chain(const mxg_chain* c, void* stream) {
   int st = validate_chain(c, mxg_chain_workspace_bytes(c));
   if (st != MXG_OK) return st;
   if ((st = check_device()) != MXG_OK) return st;
+  if (!chain_on_stage_kernel()) return chain_direct(*c, (hipStream_t)stream);
   const int G = mxg::stage_grid();
   if (G <= 0) return MXG_ERR_DEVICE;
   mxg::ProgramBuilder pb = chain_program(*c, G);
   return run_program(pb, (hipStream_t)stream);
+}
+
+size_t mxg_wo_a_workspace_bytes(const mxg_wo_a* p) {
+  if (!p || !wo_a_shape_ok(*p)) return mxg::kCtrRegionBytes;
+  return wo_a_layout(*p).end;
+}
+
+int wo_a_fused_quantize(const mxg_wo_a* p, void* stream) {
+  int st = validate_wo_a(p);
+  if (st != MXG_OK) return st;
+  if ((st = check_device()) != MXG_OK) return st;
+  return wo_a_run(*p, (hipStream_t)stream);
 }
 
 }  // extern "C"

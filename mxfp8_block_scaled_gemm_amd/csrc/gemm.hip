@@ -78,18 +78,26 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
     return c < nck ? c : -1;
   };
   if constexpr (!FQ) {
-    const auto ra = make_rsrc(p.a_q, (uint32_t)(M * K));
+    // Rows of K codes at stride lda (and K/32 scale bytes at stride lda/32),
+    // starting at this tile's group.
+    const int64_t grp = p.group_tiles ? (int64_t)(t / p.group_tiles) * p.a_group : 0;
+    const int lda = (int)p.lda, ldas = lda >> 5;
+    const auto ra = make_rsrc(p.a_q + grp, (uint32_t)((M - 1) * lda + K));
+    const int cpr = K >> 4;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = chunk(i);
-      st[i] = buf_ld16(ra, c >= 0 ? (uint32_t)c * 16u : kOutOfRange);
+      const int row = c / cpr, col = (c - row * cpr) * 16;
+      st[i] = buf_ld16(ra, c >= 0 ? (uint32_t)(row * lda + col) : kOutOfRange);
     }
-    const auto rs = make_rsrc(p.a_s, (uint32_t)(M * KB));
-    const int nsc = (M * KB) >> 2;
+    const auto rs = make_rsrc(p.a_s + (grp >> 5), (uint32_t)((M - 1) * ldas + KB));
+    const int nsc = (M * KB) >> 2, spr = KB >> 2;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = tid + i * kThreads;
-      sc[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, c < nsc ? c * 4 : (int)kOutOfRange, 0, 0);
+      const int row = c / spr, col = (c - row * spr) * 4;
+      sc[i] = __builtin_amdgcn_raw_buffer_load_b32(
+          rs, c < nsc ? row * ldas + col : (int)kOutOfRange, 0, 0);
     }
   } else {
     const auto rx = make_rsrc(p.x, (uint32_t)(((M - 1) * p.ld_x + K) * 2));
@@ -215,6 +223,7 @@ __global__ __launch_bounds__(kThreads) void gemm_wide_kernel(GemmArgs p) {
   const int my = S > wave ? (S - wave + kWaves - 1) / kWaves : 0;
   const auto rw = make_rsrc(p.w_q + (int64_t)t * S * 2048, (uint32_t)(S * 2048));
   const auto rws = make_rsrc(p.w_s + (int64_t)t * S * 64, (uint32_t)(S * 64));
+  const int64_t grp = p.group_tiles ? (int64_t)(t / p.group_tiles) * p.a_group : 0;
 
   v4f acc[MB];
 #pragma unroll
@@ -241,10 +250,10 @@ __global__ __launch_bounds__(kThreads) void gemm_wide_kernel(GemmArgs p) {
         for (int mb = 0; mb < MB; ++mb) {
           const int m = 16 * mb + r;
           if (m < p.M && c0 + j < my) {
-            const uint8_t* ap = p.a_q + (int64_t)m * K + s * 128 + 16 * g;
+            const uint8_t* ap = p.a_q + grp + (int64_t)m * p.lda + s * 128 + 16 * g;
             alo[j][mb] = ld16(ap);
             ahi[j][mb] = ld16(ap + 64);
-            asc[j][mb] = p.a_s[(int64_t)m * KB + 4 * s + g];
+            asc[j][mb] = p.a_s[(grp >> 5) + (int64_t)m * (p.lda >> 5) + 4 * s + g];
           } else {
             alo[j][mb] = ahi[j][mb] = v4i{0, 0, 0, 0};
             asc[j][mb] = 0;
@@ -406,8 +415,11 @@ static hipError_t launch_wide(const GemmArgs& a, hipStream_t stream) {
 // Whether the M <= 16 kernel can stage this activation in LDS.
 bool gemm_m16_fits(int M, int K) { return M <= 16 && gemm_m16_lds_bytes(M, K) <= 160 * 1024; }
 
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
+  GemmArgs a = args;
+  if (a.lda == 0) a.lda = a.K;
   const bool fq = a.x != nullptr;
+  if (fq && (a.group_tiles != 0 || a.lda != a.K)) return hipErrorInvalidValue;
   const int S = a.K / 128;
   const int steps = (S + kM16Waves - 1) / kM16Waves;       // weight steps per wave
   const int per = fq ? a.M * a.K / 8 : a.M * a.K / 16;     // 16-byte staging chunks

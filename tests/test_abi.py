@@ -91,6 +91,7 @@ def test_forced_foreign_arch_is_rejected_before_launch(lib, monkeypatch):
     monkeypatch.setenv("MXG_FORCE_ARCH", "gfx942")
     assert gemm(lib) == 5
     assert lib.mxfp8_quantize(P(0), 4, 64, 64, P(1), P(2), None) == 5
+    assert lib.wo_a_fused_quantize(ctypes.byref(_wo_a()), None) == 5
 
 
 def test_workspace_size_is_positive(lib):
@@ -117,3 +118,77 @@ def test_chain_rejects_before_launch(lib):
     bad = mx.MxgChain.from_buffer_copy(c)
     bad.a_q = A + 8
     assert lib.mxfp8_proj_chain(ctypes.byref(bad), None) == 2
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    # The binding's ctypes structures must have the C layout of include/mxgemm.h:
+    # compile a probe with the host C compiler and compare every field offset.
+    import shutil
+    import subprocess
+    import mxfp8_block_scaled_gemm_amd as mx
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    structs = {"mxg_weight": mx.MxgWeight, "mxg_chain": mx.MxgChain, "mxg_wo_a": mx.MxgWoA}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "mxgemm.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    c = {tuple(l.split()[:2]): int(l.split()[2]) for l in got if l}
+    for cname, py in structs.items():
+        assert c[(cname, "size")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert c[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
+
+
+def _wo_a(**kw):
+    import mxfp8_block_scaled_gemm_amd as mx
+    w = lambda k, N, K: mx.MxgWeight(A * k, A * (k + 1), N, K)
+    base = dict(M=4, o=A, ld_row=64 * 512, ld_head=512, positions=A * 2, cos_sin=A * 3,
+                max_pos=65536, n_heads=64, head_dim=512, nope_dim=448, n_groups=8,
+                wa=w(4, 8192, 4096), z=A * 6, z_q=A * 7, z_s=A * 8, wb=w(9, 5120, 8192),
+                out=A * 11, workspace=A * 12, workspace_bytes=1 << 30)
+    base.update(kw)
+    return mx.MxgWoA(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), 1), (dict(positions=None), 1), (dict(z_q=None), 1), (dict(out=None), 1),
+    (dict(M=0), 3), (dict(M=49), 3), (dict(n_groups=7), 3), (dict(n_groups=4), 3),
+    (dict(nope_dim=450), 3), (dict(nope_dim=512), 3), (dict(head_dim=500), 3),
+    (dict(ld_head=256), 3), (dict(ld_row=1000), 3),
+    (dict(max_pos=0), 3),
+    (dict(o=A + 8), 2), (dict(positions=A + 4), 2), (dict(ld_head=516, ld_row=64 * 516), 2),
+    (dict(cos_sin=A + 4), 2), (dict(z=A + 2), 2),
+    (dict(workspace=None), 4), (dict(workspace_bytes=1024), 4),
+])
+def test_wo_a_rejects(lib, kw, status):
+    import mxfp8_block_scaled_gemm_amd as mx
+    p = _wo_a(**kw)
+    assert lib.wo_a_fused_quantize(ctypes.byref(p), None) == status
+
+
+def test_wo_a_rejects_weight_shapes(lib):
+    import mxfp8_block_scaled_gemm_amd as mx
+    w = lambda k, N, K: mx.MxgWeight(A * k, A * (k + 1), N, K)
+    for wa, wb in ((w(4, 8192, 2048), w(9, 5120, 8192)),     # K != hpg * D
+                   (w(4, 8 * 1040, 4096), w(9, 5120, 8320)),  # R % 128 != 0
+                   (w(4, 8192, 4096), w(9, 5120, 4096))):     # wb.K != G * R
+        p = _wo_a(wa=wa, wb=wb)
+        assert lib.wo_a_fused_quantize(ctypes.byref(p), None) == 3
+
+
+def test_wo_a_workspace_size(lib):
+    import mxfp8_block_scaled_gemm_amd as mx
+    p = _wo_a(z=None)
+    with_z = lib.mxg_wo_a_workspace_bytes(ctypes.byref(_wo_a()))
+    without = lib.mxg_wo_a_workspace_bytes(ctypes.byref(p))
+    assert with_z >= 65536 + 4 * 32768 + 4 * 1024
+    assert without >= with_z + 2 * 4 * 8192

@@ -1,5 +1,6 @@
-"""GPU parity of mxfp8_proj_chain (three projections in one launch) against
-the oracle's chain, in the decode step's order: A on the MXFP8 layer input,
+"""GPU parity of mxfp8_proj_chain (three projections back to back: three
+direct-kernel launches, or one stage-kernel launch with MXG_CHAIN_PATH=stage)
+against the oracle's chain, in the decode step's order: A on the MXFP8 layer input,
 the leading columns of A's output requantized for B, C on its own input.
 
 Unique results are compared with the oracle directly (A's and C's outputs,
@@ -8,6 +9,8 @@ the GEMM tolerance, so the requantized codes are checked for validity (they
 must be exactly the quantization of the GPU's own A output), and B's output
 is compared end to end with the oracle on every row whose requantized codes
 match the oracle's, and stage-wise on the others."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -20,6 +23,14 @@ from helpers import check_gemm, dev_bf16, host_bits, host_u8, say
 pytestmark = pytest.mark.gpu
 
 SMALL = {"A": (256, 512), "B": (384, 128), "C": (320, 640)}
+
+
+@pytest.fixture(params=["direct", "stage"])
+def chain_path(request, monkeypatch):
+    """Both chain implementations; single GEMMs follow the same choice."""
+    monkeypatch.setenv("MXG_CHAIN_PATH", request.param)
+    monkeypatch.setenv("MXG_GEMM_PATH", request.param)
+    return request.param
 
 
 def _prep(case):
@@ -41,7 +52,7 @@ def run_chain(M, dims=None, seed=0):
     b_cols = d["B"][1]
     g, o = _prep(case)
     ref = oracle.chain(*o["x_a"], o["w_a"], b_cols, o["w_b"], *o["x_c"], o["w_c"])
-    say(f"chain M={M} dims={d} seed={seed}")
+    say(f"chain M={M} dims={d} seed={seed} path={os.environ.get('MXG_CHAIN_PATH')}")
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
     out_a, b_q, b_s, out_b, out_c = mx.mxfp8_proj_chain(*g["x_a"], g["w_a"], g["w_b"], *g["x_c"],
                                                          g["w_c"], workspace=ws)
@@ -67,18 +78,18 @@ def run_chain(M, dims=None, seed=0):
 
 
 @pytest.mark.parametrize("M", [1, 5, 16, 17, 32, 48])
-def test_chain_small(M):
+def test_chain_small(M, chain_path):
     run_chain(M, dims=SMALL, seed=M)
 
 
 @pytest.mark.parametrize("M", [1, 8, 32])
-def test_chain_full_size(M):
+def test_chain_full_size(M, chain_path):
     run_chain(M)
 
 
-def test_chain_deterministic_and_equal_to_separate_calls(monkeypatch):
-    monkeypatch.setenv("MXG_GEMM_PATH", "stage")
-    g, outs, ws = run_chain(8)
+@pytest.mark.parametrize("M", [8, 32])
+def test_chain_deterministic_and_equal_to_separate_calls(M, chain_path):
+    g, outs, ws = run_chain(M)
     first = [t.clone() for t in outs]
     for _ in range(20):
         again = mx.mxfp8_proj_chain(*g["x_a"], g["w_a"], g["w_b"], *g["x_c"], g["w_c"], workspace=ws)
