@@ -14,8 +14,8 @@
  *                 (value 2^(byte-127)) per 32 consecutive K elements, row-major
  *                 [rows, K/32].  ([mxfp8] compile_low_latency: Float8E4M3FN
  *                 operands, Float8E8M0FNU scales, sf_vec_size 32.)
- *   weights       "column-major [K, N]" in the pages' words ([mxfp8]
- *                 launch_low_latency), i.e. N rows of K contiguous codes:
+ *   weights       a column-major K x N matrix on the [mxfp8] page
+ *                 (launch_low_latency), i.e. N rows of K contiguous codes:
  *                 w_q [N, K], w_s [N, K/32] here.  The GEMM entry points take
  *                 the weight once repacked by mxfp8_pack_weights into the
  *                 order its kernels stream (see there), as a layer
