@@ -35,6 +35,17 @@ constexpr int kThreads = kWaves * 64;
 __host__ __device__ constexpr int act_ld(int K) { return K + 16; }          // LDS bytes per code row
 __host__ __device__ constexpr int scale_ld(int K) { return (K >> 5) + 4; }  // LDS bytes per scale row
 
+// Weight tile of workgroup b.  Workgroups are dispatched to the 8 XCDs round
+// robin (b mod 8), and each XCD has its own L2.  Four consecutive tiles share
+// every 128-byte line of the BF16 output rows, so when the tile count allows,
+// those four tiles go to workgroups of one XCD: their partial-line writes then
+// merge in one L2 instead of four.
+__device__ __forceinline__ int xcd_tile(int b, int tiles) {
+  if (tiles & 31) return b;
+  const int xcd = b & 7, k = b >> 3;
+  return 4 * (xcd + 8 * (k >> 2)) + (k & 3);
+}
+
 // Quantize one 8-element BF16 chunk (16 bytes) whose block of 32 is spread
 // over the 4 lanes tid & ~3 .. (tid & ~3) + 3; returns the 8 codes and the
 // block's exponent.  All 64 lanes must call it (it shuffles).
@@ -62,7 +73,7 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r = lane & 15;
   const int M = p.M, K = p.K, KB = K >> 5, S = K >> 7;
-  const int t = blockIdx.x;
+  const int t = xcd_tile(blockIdx.x, p.N >> 4);
   const int ldA = act_ld(K), ldS = scale_ld(K);
   uint8_t* s_act = smem;                                   // [M][ldA] codes
   uint8_t* s_scl = smem + M * ldA;                         // [M][ldS] scale bytes
@@ -154,7 +165,7 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
     }
   } else {
     const int cpr = K >> 3;
-    const bool writer = blockIdx.x == 0;
+    const bool writer = blockIdx.x == 0;   // one workgroup writes the codes out
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = chunk(i);
@@ -219,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void gemm_wide_kernel(GemmArgs p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r = lane & 15;
   const int K = p.K, KB = K >> 5, S = K >> 7;
-  const int t = blockIdx.x;
+  const int t = xcd_tile(blockIdx.x, p.N >> 4);
   const int my = S > wave ? (S - wave + kWaves - 1) / kWaves : 0;
   const auto rw = make_rsrc(p.w_q + (int64_t)t * S * 2048, (uint32_t)(S * 2048));
   const auto rws = make_rsrc(p.w_s + (int64_t)t * S * 64, (uint32_t)(S * 64));
