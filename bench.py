@@ -232,6 +232,12 @@ def extra_cases(dev, stream):
         del os.environ["MXG_CHAIN_PATH"]
     for M in (1, 4, 16):
         out[f"wo_a+wo_b M{M}"] = wo_a_case(dev, stream, M)
+    os.environ["MXG_WOA_PATH"] = "stage"
+    try:
+        for M in (1, 4, 16):
+            out[f"wo_a+wo_b M{M} (one stage-kernel launch)"] = wo_a_case(dev, stream, M)
+    finally:
+        del os.environ["MXG_WOA_PATH"]
     return out
 
 

@@ -3,6 +3,7 @@
 // and runs before anything is enqueued ([cute] page, AllReduceMHC checks every
 // buffer before its first launch), so a rejected call launches nothing and
 // writes nothing.
+#include <algorithm>
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
@@ -105,21 +106,38 @@ mxg::ProgramBuilder gemm_program(int M, int N, int K, const uint16_t* x, int ld_
                                  uint8_t* a_s, const uint8_t* w_q, const uint8_t* w_s,
                                  uint16_t* out, uint8_t* ws, int G) {
   mxg::ProgramBuilder pb(M, G, ws);
-  int dep = -1;
-  if (x) dep = pb.add_quant(x, ld_x, K, a_q, a_s, -1);
-  pb.add_gemm(N, K, w_q, w_s, a_q, a_s, 1, 0, 0, out, N, dep);
+  const int i = pb.add_gemm(N, K, w_q, w_s, -1, out, N, x ? mxg::kActBf16 : mxg::kActMx);
+  mxg::StageDesc& d = pb.stage(i);
+  if (x) {
+    d.x = x;
+    d.ld_x = ld_x;
+    d.q = a_q;
+    d.s = a_s;
+    d.ldq = K;
+  } else {
+    d.aq = a_q;
+    d.as = a_s;
+  }
   return pb;
 }
 
 mxg::ProgramBuilder chain_program(const mxg_chain& c, int G) {
   mxg::ProgramBuilder pb((int)c.M, G, reinterpret_cast<uint8_t*>(c.workspace));
-  const int a = pb.add_gemm((int)c.wA.N, (int)c.wA.K, c.wA.q, c.wA.s, c.a_q, c.a_s, 1, 0, 0,
-                            c.out_a, (int)c.wA.N, -1);
-  const int rq = pb.add_quant(c.out_a, (int)c.wA.N, (int)c.wB.K, c.b_q, c.b_s, a);
-  const int b = pb.add_gemm((int)c.wB.N, (int)c.wB.K, c.wB.q, c.wB.s, c.b_q, c.b_s, 1, 0, 0,
-                            c.out_b, (int)c.wB.N, rq);
-  pb.add_gemm((int)c.wC.N, (int)c.wC.K, c.wC.q, c.wC.s, c.c_q, c.c_s, 1, 0, 0, c.out_c,
-              (int)c.wC.N, b);
+  const int a = pb.add_gemm((int)c.wA.N, (int)c.wA.K, c.wA.q, c.wA.s, -1, c.out_a, (int)c.wA.N);
+  pb.stage(a).aq = c.a_q;
+  pb.stage(a).as = c.a_s;
+  // B quantizes the leading wB.K columns of A's output while staging them.
+  const int b = pb.add_gemm((int)c.wB.N, (int)c.wB.K, c.wB.q, c.wB.s, a, c.out_b, (int)c.wB.N,
+                            mxg::kActBf16);
+  mxg::StageDesc& sb = pb.stage(b);
+  sb.x = c.out_a;
+  sb.ld_x = c.wA.N;
+  sb.q = c.b_q;
+  sb.s = c.b_s;
+  sb.ldq = c.wB.K;
+  const int cc = pb.add_gemm((int)c.wC.N, (int)c.wC.K, c.wC.q, c.wC.s, b, c.out_c, (int)c.wC.N);
+  pb.stage(cc).aq = c.c_q;
+  pb.stage(cc).as = c.c_s;
   return pb;
 }
 
@@ -169,12 +187,14 @@ bool wo_a_shape_ok(const mxg_wo_a& p) {
   if (H * D > ((int64_t)1 << 20) || p.max_pos < 1 || p.max_pos > ((int64_t)1 << 31) / (D - nope))
     return false;
   if (p.ld_head < D || p.ld_row < (H - 1) * p.ld_head + D) return false;
-  if ((p.M - 1) * p.ld_row + H * p.ld_head > ((int64_t)1 << 40)) return false;
+  if (((p.M - 1) * p.ld_row + H * p.ld_head) * 2 >= ((int64_t)1 << 31)) return false;
   if (!weight_ok(p.wa) || p.wa.N % G != 0 || (p.wa.N / G) % 128 != 0 || p.wa.K != (H / G) * D)
     return false;
   if (p.wb.q && (!weight_ok(p.wb) || p.wb.K != p.wa.N)) return false;
   return true;
 }
+
+size_t wo_a_need(const mxg_wo_a& p);
 
 int validate_wo_a(const mxg_wo_a* p) {
   if (!p) return MXG_ERR_NULL;
@@ -190,12 +210,76 @@ int validate_wo_a(const mxg_wo_a* p) {
   if (p->z && !aligned16(p->z)) return MXG_ERR_ALIGN;
   if (p->wb.q && (!aligned16(p->wb.q) || !aligned16(p->wb.s) || !aligned16(p->out)))
     return MXG_ERR_ALIGN;
-  if (!p->workspace || p->workspace_bytes < wo_a_layout(*p).end) return MXG_ERR_WORKSPACE;
+  if (!p->workspace || p->workspace_bytes < wo_a_need(*p)) return MXG_ERR_WORKSPACE;
   if (!aligned16(p->workspace)) return MXG_ERR_ALIGN;
   return MXG_OK;
 }
 
+// WO-A kernel choice: MXG_WOA_PATH=stage runs the rotary + grouped
+// projection (and wo_b) as one stage-kernel launch; otherwise three direct
+// launches.
+bool wo_a_on_stage_kernel() {
+  const char* force = std::getenv("MXG_WOA_PATH");
+  return force && std::strcmp(force, "stage") == 0;
+}
+
+mxg::ProgramBuilder wo_a_program(const mxg_wo_a& p, int G) {
+  uint8_t* ws = reinterpret_cast<uint8_t*>(p.workspace);
+  const WoALayout l = wo_a_layout(p);
+  const int M = (int)p.M, H = p.n_heads, D = p.head_dim, Gr = p.n_groups;
+  const int GR = (int)p.wa.N, R = GR / Gr, Kg = (int)p.wa.K;
+  uint16_t* z = p.z ? p.z : (ws ? reinterpret_cast<uint16_t*>(ws + l.z) : nullptr);
+  mxg::ProgramBuilder pb(M, G, ws, l.end);
+  const int a = pb.add_gemm(GR, Kg, p.wa.q, p.wa.s, -1, z, GR, mxg::kActRope, D, p.nope_dim);
+  mxg::StageDesc& sa = pb.stage(a);
+  sa.group_tiles = R / 16;
+  sa.x = p.o;
+  sa.ld_x = p.ld_row;
+  sa.ld_head = p.ld_head;
+  sa.positions = p.positions;
+  sa.cos_sin = p.cos_sin;
+  sa.max_pos = p.max_pos;
+  sa.q = ws ? ws + l.xq : nullptr;
+  sa.s = ws ? ws + l.xs : nullptr;
+  sa.ldq = (int64_t)H * D;
+  if (p.wb.q) {
+    const int b = pb.add_gemm((int)p.wb.N, (int)p.wb.K, p.wb.q, p.wb.s, a, p.out, (int)p.wb.N,
+                              mxg::kActBf16);
+    mxg::StageDesc& sb = pb.stage(b);
+    sb.x = z;
+    sb.ld_x = GR;
+    sb.q = p.z_q;
+    sb.s = p.z_s;
+    sb.ldq = GR;
+  }
+  return pb;
+}
+
+// Workspace bytes of WO-A on either path.
+size_t wo_a_need(const mxg_wo_a& p) {
+  size_t need = wo_a_layout(p).end;
+  const int G = mxg::stage_grid();
+  if (G > 0) {
+    mxg_wo_a probe = p;
+    probe.workspace = nullptr;
+    need = std::max(need, wo_a_program(probe, G).workspace_bytes());
+  }
+  return need;
+}
+
+int run_program(mxg::ProgramBuilder& pb, hipStream_t stream);
+
 int wo_a_run(const mxg_wo_a& p, hipStream_t stream) {
+  if (wo_a_on_stage_kernel()) {
+    const int G = mxg::stage_grid();
+    if (G <= 0) return MXG_ERR_DEVICE;
+    mxg::ProgramBuilder pb = wo_a_program(p, G);
+    const int st = run_program(pb, stream);
+    if (st != MXG_OK || p.wb.q) return st;
+    const WoALayout l = wo_a_layout(p);
+    uint16_t* z = p.z ? p.z : reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(p.workspace) + l.z);
+    return launched(mxg::launch_quantize(z, p.M, p.wa.N, p.wa.N, p.z_q, p.z_s, stream));
+  }
   uint8_t* ws = reinterpret_cast<uint8_t*>(p.workspace);
   const WoALayout l = wo_a_layout(p);
   const int M = (int)p.M, H = p.n_heads, D = p.head_dim, G = p.n_groups;
@@ -324,7 +408,7 @@ int mxfp8_proj_chain(const mxg_chain* c, void* stream) {
 
 size_t mxg_wo_a_workspace_bytes(const mxg_wo_a* p) {
   if (!p || !wo_a_shape_ok(*p)) return mxg::kCtrRegionBytes;
-  return wo_a_layout(*p).end;
+  return wo_a_need(*p);
 }
 
 int wo_a_fused_quantize(const mxg_wo_a* p, void* stream) {

@@ -12,24 +12,25 @@ namespace {
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// LDS bytes of a GEMM unit's staged activations (codes, scales) for Sp steps.
-size_t act_lds(int M, int Sp) { return (size_t)M * (Sp * 128 + 16); }
-size_t scl_lds(int M, int Sp) { return ((size_t)M * (Sp * 4 + 4) + 15) & ~(size_t)15; }
-size_t red_lds(int MB) { return (size_t)kStageStreamWaves * MB * 64 * 16; }
+// LDS bytes of a stage whose segments are Sp steps long: one activation
+// buffer (codes, scales) plus the two alternating partial-tile buffers.
+size_t stage_lds(int M, int Sp, int MB) {
+  return (size_t)M * (Sp * 128 + 16) + (((size_t)M * (Sp * 4 + 4) + 15) & ~(size_t)15) +
+         (size_t)2 * kStageStreamWaves * MB * 64 * 16;
+}
 
-}  // namespace
-
-int choose_kparts(int M, int N, int K, int G) {
+// K parts per 16-row tile: the split whose busiest workgroup streams the
+// fewest weight steps, counting a small cost per unit and the latency of
+// the cross-workgroup partial sum when P > 1.  -1 if nothing fits in LDS.
+int choose_kparts(int M, int N, int K, int G, size_t extra_lds) {
   const int S = K / 128, tiles = N / 16, MB = (M + 15) / 16;
   int best = -1;
   long best_cost = 0;
-  for (int P = 1; P <= 16; P *= 2) {
+  for (int P = 1; P <= 64; P *= 2) {
     if (P > S) break;
     const int Sp = ceil_div(S, P);
-    if (Sp > kStageStreamWaves * kStageStepsPerWave) continue;
-    if (act_lds(M, Sp) + scl_lds(M, Sp) + red_lds(MB) > (size_t)kStageLdsMax) continue;
-    // weight steps the busiest workgroup streams, plus a per-unit overhead
-    const long cost = (long)ceil_div(tiles * P, G) * (Sp + 2);
+    if (stage_lds(M, Sp, MB) + extra_lds > (size_t)kStageLdsMax) continue;
+    const long cost = (long)ceil_div(tiles * P, G) * (Sp + 2) + (P > 1 ? 8 : 0);
     if (best < 0 || cost < best_cost) {
       best = P;
       best_cost = cost;
@@ -37,6 +38,8 @@ int choose_kparts(int M, int N, int K, int G) {
   }
   return best;
 }
+
+}  // namespace
 
 int stage_grid() {
   static std::atomic<int> cached[64];
@@ -53,8 +56,8 @@ int stage_grid() {
   return g;
 }
 
-ProgramBuilder::ProgramBuilder(int M, int G, uint8_t* ws)
-    : M_(M), ws_(ws), ctr_off_(kTileCtrBase), off_(kCtrRegionBytes) {
+ProgramBuilder::ProgramBuilder(int M, int G, uint8_t* ws, size_t data_start)
+    : M_(M), ws_(ws), ctr_off_(kTileCtrBase), off_(std::max(data_start, kCtrRegionBytes)) {
   pg_ = Program{};
   pg_.G = G;
   pg_.ws = ws;
@@ -74,44 +77,32 @@ uint8_t* ProgramBuilder::carve(size_t bytes) {
   return p;
 }
 
-int ProgramBuilder::add_quant(const uint16_t* x, int ld_x, int K, uint8_t* q, uint8_t* s,
-                              int dep) {
+int ProgramBuilder::add_gemm(int N, int K, const uint8_t* wq, const uint8_t* wsc, int dep,
+                             uint16_t* out, int ld_out, int act, int D, int nope) {
   StageDesc& d = pg_.st[pg_.nstages];
   d = StageDesc{};
-  d.kind = kStageQuant;
-  d.dep = dep;
-  d.M = M_;
-  d.x = x;
-  d.ld_x = ld_x;
-  d.qK = K;
-  d.q = q;
-  d.s = s;
-  d.units = ceil_div(M_ * (K / 32), 64);
-  return pg_.nstages++;
-}
-
-int ProgramBuilder::add_gemm(int N, int K, const uint8_t* wq, const uint8_t* wsc,
-                             const uint8_t* aq, const uint8_t* as, int groups, int64_t a_gs_q,
-                             int64_t a_gs_s, uint16_t* out, int ld_out, int dep) {
-  StageDesc& d = pg_.st[pg_.nstages];
-  d = StageDesc{};
-  d.kind = kStageGemm;
   d.dep = dep;
   d.M = M_;
   d.N = N;
   d.K = K;
+  d.S = K / 128;
   d.tiles = N / 16;
-  d.group_tiles = d.tiles / groups;
+  d.group_tiles = d.tiles;
   d.wq = wq;
   d.ws = wsc;
-  d.aq = aq;
-  d.as = as;
-  d.a_gs_q = a_gs_q;
-  d.a_gs_s = a_gs_s;
+  d.act = act;
+  d.lda = K;
+  d.D = D;
+  d.nope = nope;
   d.out = out;
   d.ld_out = ld_out;
-  d.P = std::max(1, choose_kparts(M_, N, K, pg_.G));
-  d.Sp = ceil_div(K / 128, d.P);
+  const size_t extra = act == kActRope ? (size_t)M_ * (D - nope) * 4 : 0;
+  d.P = choose_kparts(M_, N, K, pg_.G, extra);
+  if (d.P < 0) {
+    bad_ = true;
+    d.P = 1;
+  }
+  d.Sp = (d.S + d.P - 1) / d.P;
   d.units = d.tiles * d.P;
   if (d.P > 1) {
     d.tile_ctr = carve_counters((size_t)d.tiles);
@@ -121,34 +112,33 @@ int ProgramBuilder::add_gemm(int N, int K, const uint8_t* wq, const uint8_t* wsc
 }
 
 bool ProgramBuilder::finish() {
-  if (ctr_overflow_) return false;
-  size_t act = 0, scl = 0;
-  int rot = 0;
+  if (ctr_overflow_ || bad_ || pg_.nstages == 0) return false;
+  int rot = 0, act_ld = 0, scl_ld = 0;
   for (int i = 0; i < pg_.nstages; ++i) {
     StageDesc& d = pg_.st[i];
-    if (d.kind == kStageGemm) {
-      if (choose_kparts(M_, d.N, d.K, pg_.G) < 0) return false;
-      act = std::max(act, act_lds(M_, d.Sp));
-      scl = std::max(scl, scl_lds(M_, d.Sp));
-    }
-    // Rotate each stage's start so that the workgroups left with one unit
+    if (d.tiles % d.group_tiles != 0) return false;
+    act_ld = std::max(act_ld, d.Sp * 128 + 16);
+    scl_ld = std::max(scl_ld, d.Sp * 4 + 4);
+    // Rotate each stage's ranges so that the workgroups holding one unit
     // more in one stage are not the same ones in the next.
     d.rot = rot;
     rot = (rot + d.units) % pg_.G;
-    // Workgroups b with units in this stage: (b - rot) mod G < units.
+    // Workgroups b with units in this stage: f = (b - rot) mod G has a
+    // non-empty range [f*U/G, (f+1)*U/G).
     for (int x = 0; x < kGroups; ++x) d.arrive_target[x] = 0;
     for (int b = 0; b < pg_.G; ++b) {
       const int f = ((b - d.rot) % pg_.G + pg_.G) % pg_.G;
-      if (f < d.units) ++d.arrive_target[b % kGroups];
+      const long lo = (long)f * d.units / pg_.G, hi = (long)(f + 1) * d.units / pg_.G;
+      if (hi > lo) ++d.arrive_target[b % kGroups];
     }
     if (d.dep >= 0) {
       pg_.st[d.dep].consumed = 1;
       pg_.synced = 1;
     }
   }
-  pg_.lds_act_bytes = (int)((act + 15) & ~(size_t)15);
-  pg_.lds_scl_bytes = (int)scl;
-  return (size_t)pg_.lds_act_bytes + pg_.lds_scl_bytes + red_lds(mb()) <= (size_t)kStageLdsMax;
+  pg_.act_ld = act_ld;
+  pg_.scl_ld = scl_ld;
+  return stage_lds_bytes(pg_, mb()) <= (size_t)kStageLdsMax;
 }
 
 }  // namespace mxg

@@ -1,45 +1,49 @@
-// Persistent stage-program kernel: a short program of dependent stages
-// (activation quantize, MXFP8 GEMM, grouped GEMM, requantize) run by one
-// launch of one workgroup per CU.
+// Persistent stage-program kernel: a short program of dependent GEMM stages
+// (a projection chain, or grouped WO-A followed by wo_b) run by one launch of
+// one workgroup per CU.
 //
 // Why: a single small-row GEMM streams 2-40 MB of weights and a launch costs
 // about as much as streaming a few MB, and the decode step runs several
 // projections back to back ([step] page, AttentionStep: fused_wqa_wkv, wq_b,
-// wo_b; [mxfp8] page: the low-latency kernel loads its weights before its
-// grid dependency wait so the weight read overlaps the previous kernel).
-// Here every stage's weight stream is independent of the data, so the weight
-// loads of the next unit are always in flight while the current unit waits
-// for its input; only the activations wait for the previous stage.
+// wo_b; [o_proj] page, dsv41_o_proj: WO-A then wo_b).  The pages overlap the
+// next kernel's weight read with the previous kernel ([mxfp8] page: the
+// low-latency kernel loads its weights before its grid dependency wait).
+// Here the weight stream of the whole program is one sequence per wave that
+// never waits for data: only activations wait for the previous stage.
 //
 // Workgroup = 16 waves:
-//   waves 0..11  "stream" waves: weight loads (packed tile order, predicated
-//                by buffer ranges, non-temporal) for the current and the next
-//                unit, and the scaled MFMAs;
+//   waves 0..11  "stream" waves.  Each walks its share of the workgroup's
+//                weight steps (a step = 16 weight rows x 128 K: 2 KiB of
+//                codes, 64 scale bytes) across units and stages, holding a
+//                ring of R steps of loads in flight, and issues one scaled
+//                MFMA per step.
 //   waves 12..15 "io" waves: dependency waits, activation staging into LDS
-//                (or quantizing a BF16 input), the reduction of the 12 partial
-//                tiles, the BF16 output or the K-split partial, and
-//                publishing completion.
+//                (quantizing BF16 inputs, with rotary for attention heads),
+//                the sum of the 12 partial tiles of each unit, and the BF16
+//                output or K-split partial.
 // Splitting the roles keeps each wave's in-order load counter free of the
-// other role's loads, so no stream wave ever waits for an activation and no
-// activation waits behind a weight.
+// other role's loads: no weight load waits for an activation and the
+// activations never wait behind the weight ring.
 //
-// Work units: a GEMM stage is cut into (16-row weight tile) x (K part) units;
-// a quantize stage into 64-block chunks.  Unit u of stage s runs on
-// workgroup (u + rot_s) mod G, every workgroup taking its units stage by
-// stage.  A tile cut into P > 1 K parts is finished by whichever part
-// arrives last, which sums the P FP32 partials in part order (the result
-// does not depend on arrival order).
+// Work units: a stage is cut into (16-row weight tile) x (K part) units in
+// part-major order; workgroup b takes a contiguous, balanced range of them,
+// so it stages the activations of one (part, group) segment once for a run
+// of units.  Per unit there is one workgroup barrier (partials of the unit
+// written; their LDS buffers alternate), plus one when the unit starts a new
+// segment (activations staged).  A tile cut into P > 1 K parts is finished
+// by whichever part arrives last, which sums the P FP32 partials in part
+// order (the result does not depend on arrival order).
 //
-// Cross-workgroup data (quantized activations, outputs read by a later
-// stage, K-split partials) is written and read device-coherent (sc1), and a
-// workgroup counts one arrival per stage on one of 8 counters (same-address
-// device atomics serialize, so arrivals are spread over 8 lines); a
-// dependent stage's io wave polls the 8 counters.  Every spin is bounded (an
-// expired wait sets the workspace's error word and lets the kernel finish).
-// The last workgroup out resets the counters, so a zeroed workspace stays
-// valid for the next call.  Dependencies only point to earlier stages and
-// the grid never exceeds the number of co-resident workgroups, so every wait
-// is satisfied.
+// Cross-workgroup data (outputs read by a later stage, K-split partials) is
+// written and read device-coherent (sc1); a workgroup counts one arrival per
+// consumed stage on one of 8 counters, which a dependent stage's io wave
+// polls.  Every spin is bounded (an expired wait sets the workspace's error
+// word and lets the kernel finish).  The last workgroup out resets the
+// counters, so a zeroed workspace stays valid for the next call.
+// Dependencies only point to earlier stages and the grid never exceeds the
+// number of co-resident workgroups, so every wait is satisfied.
+#include <algorithm>
+
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
 #include "mx_stages.hpp"
@@ -51,21 +55,30 @@ namespace {
 constexpr int kStream = kStageStreamWaves;      // 12
 constexpr int kIo = kStageIoWaves;              // 4
 constexpr int kIoThreads = kIo * 64;
-constexpr int kSPW = kStageStepsPerWave;        // 4
 constexpr uint32_t kSpinLimit = 1u << 20;       // polls (with sleeps): well under a second
 constexpr int kCoherent = 16;                   // sc1: device-coherent access
+constexpr int kBatch = 8;                       // 16-byte staging loads in flight per io lane
 
-__device__ __forceinline__ uint32_t* ctr_word(const Program& pg, size_t byte_off) {
-  return reinterpret_cast<uint32_t*>(pg.ws + byte_off);
+// The program is read in place from the kernel-argument segment (constant
+// address space): stage indices are run-time values, and indexing a by-value
+// parameter would copy the whole program to scratch memory first.
+typedef const __attribute__((address_space(4))) Program* ProgPtr;
+typedef const __attribute__((address_space(4))) StageDesc* StagePtr;
+__device__ __forceinline__ ProgPtr program_arg() {
+  return (ProgPtr)__builtin_amdgcn_kernarg_segment_ptr();
 }
-__device__ __forceinline__ uint32_t* arrive_word(const Program& pg, int s, int x) {
+
+__device__ __forceinline__ uint32_t* ctr_word(ProgPtr pg, size_t byte_off) {
+  return reinterpret_cast<uint32_t*>(pg->ws + byte_off);
+}
+__device__ __forceinline__ uint32_t* arrive_word(ProgPtr pg, int s, int x) {
   return ctr_word(pg, kArriveBase + ((size_t)s * kGroups + x) * 128);
 }
 
 // Device-coherent (sc1) buffer accesses for data that crosses workgroups
 // within a launch: written through and read past the per-XCD caches, so a
-// plain store + s_waitcnt before the arrival counter replaces a full L2
-// write-back fence.
+// store + s_waitcnt before the arrival counter replaces a full L2 write-back
+// fence.
 __device__ __forceinline__ v4i ld16_c(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCoherent));
 }
@@ -80,12 +93,9 @@ __device__ __forceinline__ void st16_c(__amdgpu_buffer_rsrc_t r, uint32_t off, v
 __device__ __forceinline__ void st8_c(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v2u{v.x, v.y}, r, (int)off, 0, kCoherent);
 }
-__device__ __forceinline__ void st1_c(__amdgpu_buffer_rsrc_t r, uint32_t off, uint8_t v) {
-  __builtin_amdgcn_raw_buffer_store_b8(v, r, (int)off, 0, kCoherent);
-}
 
 // Workgroup barrier that orders LDS only: outstanding global loads (the
-// weight stream) stay in flight across it.
+// weight ring) stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
@@ -93,7 +103,8 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Barrier among the 4 io waves only (an LDS counter that only grows during
-// the launch; the k-th use waits for 4k arrivals, one per wave).
+// the launch; the k-th use waits for 4k arrivals, one per wave).  Only lane
+// 0 adds: a per-lane add would be folded into one add of the lane count.
 __device__ __forceinline__ void io_sync(uint32_t* bar, uint32_t& k, int lane) {
   ++k;
   if (lane == 0) __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -103,11 +114,11 @@ __device__ __forceinline__ void io_sync(uint32_t* bar, uint32_t& k, int lane) {
 
 // Wait until every group's arrival count for stage d reached its target
 // (io wave 0 polls, lanes 0..7 one group each; the others wait in io_sync).
-__device__ void wait_stage(const Program& pg, int d, int iw, int lane, uint32_t* bar,
+__device__ __noinline__ void wait_stage(ProgPtr pg, int d, int iw, int lane, uint32_t* bar,
                            uint32_t& k) {
   if (iw == 0) {
-    const StageDesc& sd = pg.st[d];
-    uint32_t target = lane < kGroups ? sd.arrive_target[lane] : 0;
+    StagePtr sd = &pg->st[d];
+    const uint32_t target = lane < kGroups ? sd->arrive_target[lane] : 0;
     const uint32_t* w = arrive_word(pg, d, lane < kGroups ? lane : 0);
     uint32_t it = 0;
     while (true) {
@@ -127,7 +138,7 @@ __device__ void wait_stage(const Program& pg, int d, int iw, int lane, uint32_t*
 
 // This workgroup finished its units of stage s: once all io waves' stores
 // have landed, count one arrival for the workgroup's group.
-__device__ void arrive_stage(const Program& pg, int s, int b, int iw, int lane, uint32_t* bar,
+__device__ __noinline__ void arrive_stage(ProgPtr pg, int s, int b, int iw, int lane, uint32_t* bar,
                              uint32_t& k) {
   __builtin_amdgcn_s_waitcnt(0);                        // this wave's stores done
   io_sync(bar, k, lane);
@@ -136,263 +147,512 @@ __device__ void arrive_stage(const Program& pg, int s, int b, int iw, int lane, 
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ int first_unit(const StageDesc& sd, int b, int G) {
-  const int f = (b - sd.rot) % G;
-  return f < 0 ? f + G : f;
+// Marks a wave-uniform value as such (the compiler cannot always prove it,
+// and a value it thinks divergent turns buffer resources into per-lane loops).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Workgroup b's units of a stage: [lo, hi).
+__device__ __forceinline__ void unit_range(StagePtr sd, int b, int G, int& lo, int& hi) {
+  int f = (b - sd->rot) % G;
+  if (f < 0) f += G;
+  lo = uni((int)(((int64_t)f * sd->units) / G));
+  hi = uni((int)(((int64_t)(f + 1) * sd->units) / G));
 }
 
-// Unit cursor over the workgroup's units, stage by stage.
-struct Cursor {
-  int s, u;
-};
-
-// Move c to the next unit at or after c (GEMM units only if gemm_only).
-__device__ bool seek(const Program& pg, int b, int G, Cursor& c, bool gemm_only) {
-  while (c.s < pg.nstages) {
-    const StageDesc& sd = pg.st[c.s];
-    if ((!gemm_only || sd.kind == kStageGemm) && c.u < sd.units) return true;
-    ++c.s;
-    if (c.s < pg.nstages) c.u = first_unit(pg.st[c.s], b, G);
-  }
-  return false;
+// Segment (K part, activation group) of unit v, as one comparable number.
+__device__ __forceinline__ int segment_of(StagePtr sd, int v) {
+  const int p = v / sd->tiles, t = v - p * sd->tiles;
+  return uni(p * (sd->tiles / sd->group_tiles) + t / sd->group_tiles);
 }
 
-__device__ __forceinline__ Cursor start(const Program& pg, int b, int G) {
-  return Cursor{0, first_unit(pg.st[0], b, G)};
-}
-
-// K range of a GEMM unit, in 128-wide steps.
-struct UnitRange {
-  int t, p, k0, k1;
-};
-__device__ __forceinline__ UnitRange unit_range(const StageDesc& sd, int u) {
-  UnitRange r;
-  r.t = u / sd.P;
-  r.p = u - r.t * sd.P;
-  const int S = sd.K >> 7;
-  r.k0 = r.p * sd.Sp;
-  r.k1 = min(r.k0 + sd.Sp, S);
-  return r;
-}
-
-struct WeightBuf {
-  v4i lo[kSPW], hi[kSPW];
-  uint32_t sc[kSPW];
-};
-
-// Issue the weight loads of one unit for stream wave w (all slots issued;
-// slots beyond the unit's steps are out of range and touch no memory).
-__device__ __forceinline__ void load_weights(const StageDesc& sd, int u, bool valid, int w,
-                                             int lane, WeightBuf& wb) {
-  const int S = sd.K >> 7;
-  UnitRange r = unit_range(sd, valid ? u : 0);
-  const auto rw = make_rsrc(sd.wq + (int64_t)r.t * S * 2048, (uint32_t)(S * 2048));
-  const auto rs = make_rsrc(sd.ws + (int64_t)r.t * S * 64, (uint32_t)(S * 64));
-#pragma unroll
-  for (int j = 0; j < kSPW; ++j) {
-    const int step = r.k0 + w + kStream * j;
-    const bool ok = valid && step < r.k1;
-    wb.lo[j] = buf_ld16_nt(rw, ok ? (uint32_t)(step * 2048 + lane * 16) : kOutOfRange);
-    wb.hi[j] = buf_ld16_nt(rw, ok ? (uint32_t)(step * 2048 + 1024 + lane * 16) : kOutOfRange);
-    wb.sc[j] = buf_ld8(rs, ok ? (uint32_t)(step * 64 + lane) : kOutOfRange);
-  }
+// Steps of unit v that stream wave w takes: w, w + 12, ... below the part's length.
+__device__ __forceinline__ int wave_steps(StagePtr sd, int v, int w) {
+  const int p = v / sd->tiles;
+  const int len = min(sd->Sp, sd->S - p * sd->Sp);
+  return uni(w < len ? (len - w + kStream - 1) / kStream : 0);
 }
 
 struct Lds {
-  uint8_t* act;   // [M][Sp*128 + 16] codes of the unit's K range
+  uint8_t* act;   // [M][Sp*128 + 16] codes of the current segment
   uint8_t* scl;   // [M][Sp*4 + 4] scale bytes
-  v4f* red;       // [kStream][MB][64] partial tiles
+  v4f* red;       // 2 x [kStream][MB][64] partial tiles
+  float* cs;      // [M][rope] angle rows (rotary stages)
   uint32_t* bar;  // io-wave barrier counter
 };
 
-// One GEMM unit on a stream wave: MFMAs over its steps, partial tile to LDS.
-template <int MB>
-__device__ __forceinline__ void stream_compute(const StageDesc& sd, int u, int w, int lane,
-                                               const WeightBuf& wb, Lds& L) {
-  const int g = lane >> 4, r = lane & 15;
-  const UnitRange ur = unit_range(sd, u);
-  const int ldA = sd.Sp * 128 + 16, ldS = sd.Sp * 4 + 4;
-  lds_barrier();                                        // B1: activations staged
-  v4f acc[MB];
+// ------------------------------------------------------------ stream waves
+
+// A wave's walk over the workgroup's units: stage s, unit v of the range
+// [v, hi), its part p and tile t, and this wave's steps j < n of the unit
+// (steps step0, step0 + 12, ...).  Advanced incrementally (no division per
+// step); the stage's scalars are cached at stage entry.
+struct Walk {
+  int s, v, hi, p, t, j, n, step0;
+  int tiles, S, Sp, M, group_tiles, gt, g;
+  const uint8_t* wq;
+  const uint8_t* ws;
+};
+
+__device__ __forceinline__ void walk_part(Walk& c, int w) {
+  const int len = min(c.Sp, c.S - c.p * c.Sp);
+  c.n = w < len ? (len - w + kStream - 1) / kStream : 0;
+  c.step0 = c.p * c.Sp + w;
+}
+
+// Enter stage c.s at the workgroup's first unit there (false: no units).
+__device__ __forceinline__ bool walk_enter(ProgPtr pg, int b, int G, int w, Walk& c) {
+  StagePtr sd = &pg->st[c.s];
+  int lo, hi;
+  unit_range(sd, b, G, lo, hi);
+  c.v = lo;
+  c.hi = hi;
+  c.j = 0;
+  if (lo >= hi) return false;
+  c.tiles = sd->tiles;
+  c.S = sd->S;
+  c.Sp = sd->Sp;
+  c.M = sd->M;
+  c.group_tiles = sd->group_tiles;
+  c.wq = sd->wq;
+  c.ws = sd->ws;
+  c.p = uni(lo / c.tiles);
+  c.t = lo - c.p * c.tiles;
+  c.g = uni(c.t / c.group_tiles);
+  c.gt = c.t - c.g * c.group_tiles;
+  walk_part(c, w);
+  return true;
+}
+
+__device__ __forceinline__ void walk_next_unit(Walk& c, int w) {
+  ++c.v;
+  ++c.t;
+  ++c.gt;
+  c.j = 0;
+  if (c.gt == c.group_tiles) {
+    c.gt = 0;
+    ++c.g;
+  }
+  if (c.t == c.tiles) {
+    c.t = 0;
+    c.g = 0;
+    c.gt = 0;
+    ++c.p;
+    walk_part(c, w);
+  }
+}
+
+// Next unit of the workgroup, across stages (false past the program).
+__device__ __forceinline__ bool walk_unit(ProgPtr pg, int b, int G, int w, Walk& c) {
+  if (c.s >= 0 && c.v + 1 < c.hi) {
+    walk_next_unit(c, w);
+    return true;
+  }
+  while (++c.s < pg->nstages)
+    if (walk_enter(pg, b, G, w, c)) return true;
+  return false;
+}
+
+// Next step of this wave (false past the program).
+__device__ __forceinline__ bool walk_step(ProgPtr pg, int b, int G, int w, Walk& c) {
+  ++c.j;
+  while (c.j >= c.n)
+    if (!walk_unit(pg, b, G, w, c)) return false;
+  return true;
+}
+
+struct Slot {
+  v4i lo, hi;
+  uint32_t sc;
+};
+
+// Issue the loads of the load walk's current step into ring slot q (a
+// uniform index: a short chain of scalar branches picks the registers),
+// then advance the walk.  The loads are ordinary buffer loads: the compiler
+// waits for a slot before its registers are read (conservatively, as the
+// slot index is a run-time value), which keeps every register read after
+// its data has landed.
+template <int R>
+__device__ __forceinline__ void issue(ProgPtr pg, int b, int G, int w, int lane, Walk& c,
+                                      bool& live, Slot (&ring)[R], int q) {
+  if (!live) return;
+  const int step = c.step0 + kStream * c.j;
+  const uint32_t chunk = (uint32_t)(c.t * c.S + step);   // 2 KiB step index in the stage
+  const uint32_t range = (uint32_t)(c.tiles * c.S);
+  const auto rw = make_rsrc(c.wq, range * 2048);
+  const auto rs = make_rsrc(c.ws, range * 64);
+  const uint32_t off = chunk * 2048 + lane * 16, soff = chunk * 64 + lane;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < kSPW; ++j) {
-    const int sl = w + kStream * j;                     // step within the unit
-    if (ur.k0 + sl < ur.k1) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int m = 16 * mb + r;
-        v4i blo = {0, 0, 0, 0}, bhi = {0, 0, 0, 0};
-        int bsc = 0;
-        if (m < sd.M) {
-          const uint8_t* a = L.act + m * ldA + sl * 128 + 16 * g;
-          blo = *reinterpret_cast<const v4i*>(a);
-          bhi = *reinterpret_cast<const v4i*>(a + 64);
-          bsc = L.scl[m * ldS + 4 * sl + g];
-        }
-        acc[mb] = mfma_mx16(cat8(wb.lo[j], wb.hi[j]), cat8(blo, bhi), acc[mb], (int)wb.sc[j], bsc);
-      }
+  for (int k = 0; k < R; ++k) {
+    if (q == k) {
+      ring[k].lo = buf_ld16_nt(rw, off);
+      ring[k].hi = buf_ld16_nt(rw, off + 1024);
+      ring[k].sc = buf_ld8(rs, soff);
     }
   }
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) L.red[(w * MB + mb) * 64 + lane] = acc[mb];
-  lds_barrier();                                        // B2: partials in LDS
+  live = walk_step(pg, b, G, w, c);
 }
 
 template <int MB>
-__device__ void stream_loop(const Program& pg, int b, int G, int w, int lane, Lds& L) {
-  Cursor cur = start(pg, b, G);
-  bool have = seek(pg, b, G, cur, true);
-  WeightBuf A, B;
-  load_weights(pg.st[have ? cur.s : 0], cur.u, have, w, lane, A);
-  while (have) {
-    Cursor nx = cur;
-    nx.u += G;
-    bool hn = seek(pg, b, G, nx, true);
-    load_weights(pg.st[hn ? nx.s : 0], nx.u, hn, w, lane, B);
-    stream_compute<MB>(pg.st[cur.s], cur.u, w, lane, A, L);
-    if (!hn) break;
-    cur = nx;
-    nx.u += G;
-    hn = seek(pg, b, G, nx, true);
-    load_weights(pg.st[hn ? nx.s : 0], nx.u, hn, w, lane, A);
-    stream_compute<MB>(pg.st[cur.s], cur.u, w, lane, B, L);
-    if (!hn) break;
-    cur = nx;
+__device__ __forceinline__ void end_unit(int& ord, v4f (&acc)[MB], int w, int lane, const Lds& L) {
+  v4f* red = L.red + (size_t)(ord & 1) * kStream * MB * 64;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    red[(w * MB + mb) * 64 + lane] = acc[mb];
+    acc[mb] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  ++ord;
+  lds_barrier();                                        // X: the unit's partials are in LDS
+}
+
+// Entering a unit of a new segment waits for its activations.
+__device__ __forceinline__ void begin_unit(const Walk& u, int& seg_s, int& seg_p, int& seg_g) {
+  if (u.s != seg_s || u.p != seg_p || u.g != seg_g) {
+    lds_barrier();                                      // Y: segment staged
+    seg_s = u.s;
+    seg_p = u.p;
+    seg_g = u.g;
+  }
+}
+
+// Whether the workgroup's first unit reads activations that need no wait:
+// then its staging loads are issued ahead of the weight ring (barrier Z).
+__device__ __forceinline__ bool first_is_free(ProgPtr pg, int b, int G, int& s0) {
+  for (int s = 0; s < pg->nstages; ++s) {
+    int lo, hi;
+    unit_range(&pg->st[s], b, G, lo, hi);
+    if (lo < hi) {
+      s0 = s;
+      return pg->st[s].dep < 0;
+    }
+  }
+  s0 = -1;
+  return false;
+}
+
+template <int MB, int R>
+__device__ __forceinline__ void stream_loop(ProgPtr pg, int b, int G, int w, int lane,
+                                            const Lds& L) {
+  const int g = lane >> 4, r = lane & 15;
+  int s0;
+  const bool z = first_is_free(pg, b, G, s0);
+  if (s0 < 0) return;                                   // no units
+  if (z) lds_barrier();                                 // Z: the first staging loads are out
+
+  // Prime the ring with this wave's first R steps.
+  Walk lc;
+  lc.s = -1;
+  bool live = walk_unit(pg, b, G, w, lc);
+  while (live && lc.j >= lc.n) live = walk_unit(pg, b, G, w, lc);
+  Slot ring[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) issue<R>(pg, b, G, w, lane, lc, live, ring, i);
+
+  Walk u;
+  u.s = -1;
+  walk_unit(pg, b, G, w, u);
+  int seg_s = -1, seg_p = -1, seg_g = -1, ord = 0;
+  v4f acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = v4f{0.f, 0.f, 0.f, 0.f};
+  begin_unit(u, seg_s, seg_p, seg_g);
+  int q = 0;                                            // ring slot of the next step
+  while (true) {
+    // Units with no step left for this wave still take part in their barriers.
+    bool done = false;
+    while (u.j >= u.n) {
+      end_unit<MB>(ord, acc, w, lane, L);
+      if (!walk_unit(pg, b, G, w, u)) {
+        done = true;
+        break;
+      }
+      begin_unit(u, seg_s, seg_p, seg_g);
+    }
+    if (done) break;
+    const int ldA = u.Sp * 128 + 16, ldS = u.Sp * 4 + 4;
+    const int sl = w + kStream * u.j;                   // step within the segment
+    v4i blo[MB], bhi[MB];
+    int bsc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      // Rows past M read row M-1 (no branch): their output columns are
+      // computed but never stored.
+      const int m = min(16 * mb + r, u.M - 1);
+      const uint8_t* a = L.act + m * ldA + sl * 128 + 16 * g;
+      blo[mb] = *reinterpret_cast<const v4i*>(a);
+      bhi[mb] = *reinterpret_cast<const v4i*>(a + 64);
+      bsc[mb] = L.scl[m * ldS + 4 * sl + g];
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      if (q == k) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[mb] = mfma_mx16(cat8(ring[k].lo, ring[k].hi), cat8(blo[mb], bhi[mb]), acc[mb],
+                              (int)ring[k].sc, bsc[mb]);
+      }
+    }
+    ++u.j;
+    issue<R>(pg, b, G, w, lane, lc, live, ring, q);
+    q = q == R - 1 ? 0 : q + 1;
   }
 }
 
 // ----------------------------------------------------------------- io waves
 
-// Quantize one 64-block chunk of a BF16 matrix (4 lanes per 32-block); the
-// codes go out device-coherent, for the stage that reads them.
-__device__ void io_quant_unit(const StageDesc& sd, int u, int lt) {
-  const int nbr = sd.qK >> 5;                           // blocks per row
-  const int total = sd.M * nbr;
-  const int blk = u * 64 + (lt >> 2), sub = lt & 3;
-  const bool ok = blk < total;
-  const int row = ok ? blk / nbr : 0, cb = ok ? blk - row * nbr : 0;
-  const auto rx = make_rsrc(sd.x, (uint32_t)(((sd.M - 1) * sd.ld_x + sd.qK) * 2));
-  const uint32_t xo = (uint32_t)((row * sd.ld_x + cb * 32 + sub * 8) * 2);
-  const v4i v = sd.dep >= 0 ? ld16_c(rx, ok ? xo : kOutOfRange) : buf_ld16(rx, ok ? xo : kOutOfRange);
-  uint32_t a = halves_max(bf16x2_absmax2(bf16x2_absmax2((uint32_t)v[0], (uint32_t)v[1]),
-                                         bf16x2_absmax2((uint32_t)v[2], (uint32_t)v[3])));
-  a = quad_max(a);
-  const int e = block_exponent(a);
-  const BlockScale bs = block_scale(e);
-  if (ok) {
-    uint2 c;
-    c.x = enc4_e4m3((uint32_t)v[0], (uint32_t)v[1], bs);
-    c.y = enc4_e4m3((uint32_t)v[2], (uint32_t)v[3], bs);
-    const auto rq = make_rsrc(sd.q, (uint32_t)(sd.M * sd.qK));
-    const auto rs = make_rsrc(sd.s, (uint32_t)(sd.M * nbr));
-    st8_c(rq, (uint32_t)(row * sd.qK + cb * 32 + sub * 8), c);
-    if (sub == 0) st1_c(rs, (uint32_t)(row * nbr + cb), (uint8_t)(e + 127));
+// Segment geometry of unit v.
+struct Segment {
+  int p, g, k0, ns;   // part, group, first step, steps
+};
+__device__ __forceinline__ Segment segment_geom(StagePtr sd, int v) {
+  Segment sg;
+  sg.p = v / sd->tiles;
+  sg.g = (v - sg.p * sd->tiles) / sd->group_tiles;
+  sg.k0 = sg.p * sd->Sp;
+  sg.ns = min(sd->Sp, sd->S - sg.k0);
+  return sg;
+}
+
+// MXFP8 activations of a segment into LDS: each round every io lane has
+// kBatch 16-byte code chunks and one scale dword in flight before it stores
+// any (a round covers kBatch * 256 chunks, and the scale dwords of a row are
+// an eighth of its chunks).  z: this is the workgroup's first segment and
+// the stream waves wait at barrier Z until the first round's loads are out,
+// so that they are not queued behind the weight ring.
+__device__ __noinline__ void stage_mx(StagePtr sd, Segment sg, int lt, bool z,
+                                         Lds L) {
+  const int ldA = sd->Sp * 128 + 16, ldS = sd->Sp * 4 + 4;
+  const int64_t gq = (int64_t)sg.g * sd->a_group;
+  const int lda = (int)sd->lda, ldas = lda >> 5;
+  const auto ra = make_rsrc(sd->aq + gq, (uint32_t)((sd->M - 1) * lda + sd->K));
+  const auto rs = make_rsrc(sd->as + (gq >> 5), (uint32_t)((sd->M - 1) * ldas + (sd->K >> 5)));
+  const int cpr = sg.ns * 8;                            // 16-byte chunks per row
+  const int nck = sd->M * cpr;
+  const int nsc = sd->M * sg.ns;                        // scale dwords (4 blocks each)
+  const int col0 = sg.k0 * 128;
+  for (int c0 = 0, rnd = 0; c0 < nck; c0 += kBatch * kIoThreads, ++rnd) {
+    v4i v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = c0 + i * kIoThreads + lt;
+      const int row = c / cpr, col = (c - row * cpr) * 16;
+      const uint32_t off = c < nck ? (uint32_t)(row * lda + col0 + col) : kOutOfRange;
+      v[i] = buf_ld16(ra, off);
+    }
+    const int cs = rnd * kIoThreads + lt;               // this round's scale dword
+    const int srow = cs / sg.ns, cd = cs - srow * sg.ns;
+    const uint32_t soff = cs < nsc ? (uint32_t)(srow * ldas + (sg.k0 + cd) * 4) : kOutOfRange;
+    const uint32_t sv = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)soff, 0, 0);
+    if (z && rnd == 0) lds_barrier();                   // Z
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = c0 + i * kIoThreads + lt;
+      if (c < nck) {
+        const int row = c / cpr, col = (c - row * cpr) * 16;
+        *reinterpret_cast<v4i*>(L.act + row * ldA + col) = v[i];
+      }
+    }
+    if (cs < nsc) *reinterpret_cast<uint32_t*>(L.scl + srow * ldS + cd * 4) = sv;
   }
 }
 
-// Stage a GEMM unit's activations (its K range, all M rows) into LDS;
-// activations made earlier in this launch are read device-coherent.
-__device__ void io_stage_act(const StageDesc& sd, const UnitRange& ur, int lt, Lds& L) {
-  const int ldA = sd.Sp * 128 + 16, ldS = sd.Sp * 4 + 4;
-  const int gi = ur.t / sd.group_tiles;
-  const int KB = sd.K >> 5;
-  const auto ra = make_rsrc(sd.aq + (int64_t)gi * sd.a_gs_q, (uint32_t)(sd.M * sd.K));
-  const auto rs = make_rsrc(sd.as + (int64_t)gi * sd.a_gs_s, (uint32_t)(sd.M * KB));
-  const bool coh = sd.dep >= 0;
-  const int ns = ur.k1 - ur.k0;
-  const int cpr = ns * 8;                               // 16-byte chunks per row
-  const int nck = sd.M * cpr;
-  for (int c = lt; c < nck; c += kIoThreads) {
-    const int row = c / cpr, col = (c - row * cpr) * 16;
-    const uint32_t off = (uint32_t)(row * sd.K + ur.k0 * 128 + col);
-    *reinterpret_cast<v4i*>(L.act + row * ldA + col) = coh ? ld16_c(ra, off) : buf_ld16(ra, off);
-  }
-  const int nsc = sd.M * ns;                            // scale dwords (4 blocks each)
-  for (int c = lt; c < nsc; c += kIoThreads) {
-    const int row = c / ns, cd = c - row * ns;
-    const uint32_t off = (uint32_t)(row * KB + (ur.k0 + cd) * 4);
-    *reinterpret_cast<uint32_t*>(L.scl + row * ldS + cd * 4) =
-        coh ? ld4_c(rs, off) : __builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, 0);
+// BF16 activations of a segment, quantized to MXFP8 into LDS (and written
+// out by the segment's writer).  ROPE: the source is attention heads and the
+// rotary dims turn by the row's angles (staged in L.cs) before rounding to
+// BF16.  8-element chunks; the 4 lanes of a quad hold one 32-block (the
+// chunk count per row is a multiple of 16, so quads never straddle rows).
+// z: as for stage_mx.
+template <bool ROPE>
+__device__ __noinline__ void stage_bf16(StagePtr sd, Segment sg, bool writer, int lt,
+                                           bool z, Lds L) {
+  const int ldA = sd->Sp * 128 + 16, ldS = sd->Sp * 4 + 4;
+  const int cpr = sg.ns * 16;                           // 8-element chunks per row
+  const int nck = sd->M * cpr;
+  const int col0 = sg.k0 * 128;
+  const int rope = sd->D - sd->nope, hpg = ROPE ? sd->K / sd->D : 1;
+  const uint16_t* xb = ROPE ? sd->x : sd->x + (int64_t)sg.g * sd->a_group;
+  const int64_t span = ROPE ? (int64_t)(sd->M - 1) * sd->ld_x + (int64_t)(sg.g + 1) * hpg * sd->ld_head
+                            : (int64_t)(sd->M - 1) * sd->ld_x + sd->K;
+  const auto rx = make_rsrc(xb, (uint32_t)(span * 2));
+  for (int c0 = 0, rnd = 0; c0 < nck; c0 += kBatch * kIoThreads, ++rnd) {
+    v4i v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = c0 + i * kIoThreads + lt;
+      const int row = c / cpr, col = col0 + (c - row * cpr) * 8;
+      uint32_t off = kOutOfRange;
+      if (c < nck) {
+        if constexpr (ROPE) {
+          const int hh = col / sd->D, d = col - hh * sd->D;
+          off = (uint32_t)((row * sd->ld_x + (sg.g * hpg + hh) * sd->ld_head + d) * 2);
+        } else {
+          off = (uint32_t)((row * sd->ld_x + col) * 2);
+        }
+      }
+      // BF16 sources are outputs of an earlier stage of this launch (read
+      // device-coherent), or attention heads from outside it.
+      v[i] = ROPE ? buf_ld16(rx, off) : ld16_c(rx, off);
+    }
+    if (z && rnd == 0) lds_barrier();                   // Z
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = c0 + i * kIoThreads + lt;
+      const bool ok = c < nck;
+      const int row = ok ? c / cpr : 0, cc = ok ? (c - row * cpr) * 8 : 0;
+      v4i x = v[i];
+      if constexpr (ROPE) {
+        const int col = col0 + cc, d = col - (col / sd->D) * sd->D;
+        if (ok && d >= sd->nope) {
+          const int i0 = (d - sd->nope) >> 1;
+          const float* cs = L.cs + row * rope;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float cth = cs[i0 + k], sth = cs[(rope >> 1) + i0 + k];
+            const float x1 = bf16_lo((uint32_t)x[k]), x2 = bf16_hi((uint32_t)x[k]);
+            const float y1 = x1 * cth - x2 * sth;
+            const float y2 = x2 * cth + x1 * sth;
+            x[k] = (int)(f32_to_bf16(y1) | (f32_to_bf16(y2) << 16));
+          }
+        }
+      }
+      uint32_t a = halves_max(bf16x2_absmax2(bf16x2_absmax2((uint32_t)x[0], (uint32_t)x[1]),
+                                             bf16x2_absmax2((uint32_t)x[2], (uint32_t)x[3])));
+      a = quad_max(a);
+      const int e = block_exponent(a);
+      const BlockScale bs = block_scale(e);
+      uint2 code;
+      code.x = enc4_e4m3((uint32_t)x[0], (uint32_t)x[1], bs);
+      code.y = enc4_e4m3((uint32_t)x[2], (uint32_t)x[3], bs);
+      if (ok) {
+        *reinterpret_cast<uint2*>(L.act + row * ldA + cc) = code;
+        if ((cc & 31) == 0) L.scl[row * ldS + (cc >> 5)] = (uint8_t)(e + 127);
+        if (writer) {
+          const int64_t o = (int64_t)row * sd->ldq + (int64_t)sg.g * sd->K + col0 + cc;
+          *reinterpret_cast<uint2*>(sd->q + o) = code;
+          if ((cc & 31) == 0) sd->s[o >> 5] = (uint8_t)(e + 127);
+        }
+      }
+    }
   }
 }
 
-__device__ __forceinline__ void store_out(const StageDesc& sd, int m, int n, v4f v) {
+// Angle rows of every row's position into LDS (rotary stages).  A position
+// outside the table reads row 0 and sets bit 1 of the error word.
+__device__ __noinline__ void stage_angles(ProgPtr pg, StagePtr sd, int iw, int lane,
+                             Lds L, uint32_t* bar, uint32_t& k) {
+  const int rope = sd->D - sd->nope;
+  const int lt = iw * 64 + lane;
+  const int per = rope / 4;                             // 16-byte chunks per row
+  for (int c = lt; c < sd->M * per; c += kIoThreads) {
+    const int row = c / per, q = c - row * per;
+    int64_t pos = sd->positions[row];
+    if (pos < 0 || pos >= sd->max_pos) {
+      if (q == 0)
+        __hip_atomic_fetch_or(ctr_word(pg, kCtrError * 4), 2u, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+      pos = 0;
+    }
+    *reinterpret_cast<v4f*>(L.cs + row * rope + 4 * q) =
+        *reinterpret_cast<const v4f*>(sd->cos_sin + pos * rope + 4 * q);
+  }
+  io_sync(bar, k, lane);
+}
+
+__device__ __forceinline__ void store_out(StagePtr sd, int m, int n, v4f v) {
   uint2 o;
   o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
   o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
-  if (sd.consumed) {
-    const auto ro = make_rsrc(sd.out, (uint32_t)(sd.M * sd.ld_out * 2));
-    st8_c(ro, (uint32_t)((m * sd.ld_out + n) * 2), o);
+  if (sd->consumed) {
+    const auto ro = make_rsrc(sd->out, (uint32_t)(sd->M * sd->ld_out * 2));
+    st8_c(ro, (uint32_t)((m * sd->ld_out + n) * 2), o);
   } else {
-    *reinterpret_cast<uint2*>(sd.out + (int64_t)m * sd.ld_out + n) = o;
+    *reinterpret_cast<uint2*>(sd->out + (int64_t)m * sd->ld_out + n) = o;
   }
 }
 
+// After the unit's barrier: sum its 12 partial tiles (io wave iw < MB owns
+// activation tile iw), then the BF16 output or the K-split protocol.
 template <int MB>
-__device__ void io_gemm_unit(const StageDesc& sd, int u, int iw, int lane, Lds& L) {
-  const int lt = iw * 64 + lane;
-  const UnitRange ur = unit_range(sd, u);
-  io_stage_act(sd, ur, lt, L);
-  lds_barrier();                                        // B1
-  lds_barrier();                                        // B2
-  if (iw >= MB) return;                                 // wave iw owns activation tile iw
-  // Sum the stream waves' partial tiles in wave order.
+__device__ __noinline__ void finish_unit(StagePtr sd, int v, int ord, int iw, int lane, Lds L) {
+  if (iw >= MB) return;
+  const v4f* red = L.red + (size_t)(ord & 1) * kStream * MB * 64;
   const int mb = iw;
   v4f sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int w = 0; w < kStream; ++w) sum += L.red[(w * MB + mb) * 64 + lane];
+  for (int w = 0; w < kStream; ++w) sum += red[(w * MB + mb) * 64 + lane];
+  const int p = v / sd->tiles, t = v - p * sd->tiles;
   const int m = 16 * mb + (lane & 15);
-  const int n = 16 * ur.t + 4 * (lane >> 4);
-  if (sd.P == 1) {
-    if (m < sd.M) store_out(sd, m, n, sum);
+  const int n = 16 * t + 4 * (lane >> 4);
+  if (sd->P == 1) {
+    if (m < sd->M) store_out(sd, m, n, sum);
     return;
   }
   // K split: park the FP32 partial (device-coherent); the last of the
   // tile's MB*P partial writers sums the P partials in part order.
-  const uint32_t tile_bytes = (uint32_t)(sd.P * MB * 64 * 16);
-  const auto rp = make_rsrc(reinterpret_cast<uint8_t*>(sd.part) + (int64_t)ur.t * tile_bytes,
+  const uint32_t tile_bytes = (uint32_t)(sd->P * MB * 64 * 16);
+  const auto rp = make_rsrc(reinterpret_cast<uint8_t*>(sd->part) + (int64_t)t * tile_bytes,
                             tile_bytes);
-  st16_c(rp, (uint32_t)(((ur.p * MB + mb) * 64 + lane) * 16), __builtin_bit_cast(v4i, sum));
+  st16_c(rp, (uint32_t)(((p * MB + mb) * 64 + lane) * 16), __builtin_bit_cast(v4i, sum));
   __builtin_amdgcn_s_waitcnt(0);
   uint32_t old = 0;
   if (lane == 0)
-    old = __hip_atomic_fetch_add(sd.tile_ctr + ur.t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __hip_atomic_fetch_add(sd->tile_ctr + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __builtin_amdgcn_readfirstlane(old);
-  if (old != (uint32_t)(MB * sd.P - 1)) return;
+  if (old != (uint32_t)(MB * sd->P - 1)) return;
 #pragma unroll
   for (int k = 0; k < MB; ++k) {
     v4f tot = __builtin_bit_cast(v4f, ld16_c(rp, (uint32_t)((k * 64 + lane) * 16)));
-    for (int p = 1; p < sd.P; ++p)
-      tot += __builtin_bit_cast(v4f, ld16_c(rp, (uint32_t)(((p * MB + k) * 64 + lane) * 16)));
+    for (int q = 1; q < sd->P; ++q)
+      tot += __builtin_bit_cast(v4f, ld16_c(rp, (uint32_t)(((q * MB + k) * 64 + lane) * 16)));
     const int mm = 16 * k + (lane & 15);
-    if (mm < sd.M) store_out(sd, mm, n, tot);
+    if (mm < sd->M) store_out(sd, mm, n, tot);
   }
   if (lane == 0)
-    __hip_atomic_store(sd.tile_ctr + ur.t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(sd->tile_ctr + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int MB>
-__device__ void io_loop(const Program& pg, int b, int G, int iw, int lane, Lds& L) {
+__device__ __forceinline__ void io_loop(ProgPtr pg, int b, int G, int iw, int lane, const Lds& L) {
   uint32_t k = 0;                                       // io_sync uses so far
-  Cursor cur = start(pg, b, G);
-  int waited = -1;                                      // stage whose dependency was met
-  while (seek(pg, b, G, cur, false)) {
-    const StageDesc& sd = pg.st[cur.s];
-    if (sd.dep >= 0 && waited != cur.s) {
-      wait_stage(pg, sd.dep, iw, lane, L.bar, k);
-      waited = cur.s;
+  const int lt = iw * 64 + lane;
+  int seg_s = -1, seg = -1, ord = 0;
+  int s0;
+  bool zfirst = first_is_free(pg, b, G, s0);
+  for (int s = 0; s < pg->nstages; ++s) {
+    StagePtr sd = &pg->st[s];
+    int lo, hi;
+    unit_range(sd, b, G, lo, hi);
+    if (lo >= hi) continue;
+    bool ready = false;                                 // dependency met, angles staged
+    for (int v = lo; v < hi; ++v) {
+      const int sv = segment_of(sd, v);
+      if (s != seg_s || sv != seg) {
+        if (!ready) {
+          if (sd->dep >= 0) wait_stage(pg, sd->dep, iw, lane, L.bar, k);
+          if (sd->act == kActRope) stage_angles(pg, sd, iw, lane, L, L.bar, k);
+          ready = true;
+        }
+        const Segment sg = segment_geom(sd, v);
+        const int first = sg.p * sd->tiles + sg.g * sd->group_tiles;   // segment's first unit
+        const bool writer = sd->q != nullptr && first >= lo;
+        const bool z = zfirst;                          // barrier Z inside this staging
+        zfirst = false;
+        if (sd->act == kActMx)
+          stage_mx(sd, sg, lt, z, L);
+        else if (sd->act == kActBf16)
+          stage_bf16<false>(sd, sg, writer, lt, z, L);
+        else
+          stage_bf16<true>(sd, sg, writer, lt, z, L);
+        lds_barrier();                                  // Y: segment staged
+        seg_s = s;
+        seg = sv;
+      }
+      lds_barrier();                                    // X: partials of unit v in LDS
+      finish_unit<MB>(sd, v, ord, iw, lane, L);
+      ++ord;
     }
-    if (sd.kind == kStageGemm)
-      io_gemm_unit<MB>(sd, cur.u, iw, lane, L);
-    else
-      io_quant_unit(sd, cur.u, iw * 64 + lane);
-    const int s = cur.s;
-    cur.u += G;
-    if (sd.consumed && cur.u >= sd.units) arrive_stage(pg, s, b, iw, lane, L.bar, k);
+    if (sd->consumed) arrive_stage(pg, s, b, iw, lane, L.bar, k);
   }
-  if (!pg.synced) return;
+  if (!pg->synced) return;
   // Exit counting: the last workgroup out resets the arrival counters.
   if (iw != 0) return;
   uint32_t last = 0;
@@ -417,21 +677,33 @@ __device__ void io_loop(const Program& pg, int b, int G, int iw, int lane, Lds& 
     __hip_atomic_store(ctr_word(pg, kExitTop), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Ring depth (weight steps in flight per stream wave) for MB activation tiles.
 template <int MB>
-__global__ __launch_bounds__(kStageThreads) void stage_kernel(Program pg) {
+constexpr int ring_depth() {
+  return MB == 1 ? 8 : (MB == 2 ? 6 : 4);
+}
+
+template <int MB>
+__global__ __launch_bounds__(kStageThreads) void stage_kernel(Program) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ uint32_t io_bar;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const ProgPtr pg = program_arg();
+  // The wave index is uniform across the wave: say so, so that everything
+  // derived from it (cursors, descriptors, buffer resources) stays scalar.
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
   const int G = gridDim.x, b = blockIdx.x;
+  const int M = pg->st[0].M;
   Lds L;
   L.act = smem;
-  L.scl = smem + pg.lds_act_bytes;
-  L.red = reinterpret_cast<v4f*>(smem + pg.lds_act_bytes + pg.lds_scl_bytes);
+  L.scl = smem + (size_t)M * pg->act_ld;
+  L.red = reinterpret_cast<v4f*>(L.scl + (((size_t)M * pg->scl_ld + 15) & ~(size_t)15));
+  L.cs = reinterpret_cast<float*>(L.red + (size_t)2 * kStream * MB * 64);
   L.bar = &io_bar;
   if (threadIdx.x == 0) io_bar = 0;
   __syncthreads();
   if (wave < kStream)
-    stream_loop<MB>(pg, b, G, wave, lane, L);
+    stream_loop<MB, ring_depth<MB>()>(pg, b, G, wave, lane, L);
   else
     io_loop<MB>(pg, b, G, wave - kStream, lane, L);
 }
@@ -446,12 +718,20 @@ hipError_t launch_mb(const Program& pg, hipStream_t stream) {
     if (e != hipSuccess) return e;
     configured = true;
   }
-  const size_t lds = (size_t)pg.lds_act_bytes + pg.lds_scl_bytes + (size_t)kStream * MB * 64 * 16;
-  hipLaunchKernelGGL(kern, dim3(pg.G), dim3(kStageThreads), lds, stream, pg);
+  hipLaunchKernelGGL(kern, dim3(pg.G), dim3(kStageThreads), stage_lds_bytes(pg, MB), stream, pg);
   return hipGetLastError();
 }
 
 }  // namespace
+
+size_t stage_lds_bytes(const Program& pg, int MB) {
+  const size_t M = (size_t)pg.st[0].M;
+  size_t rope = 0;
+  for (int i = 0; i < pg.nstages; ++i)
+    if (pg.st[i].act == kActRope) rope = std::max(rope, (size_t)(pg.st[i].D - pg.st[i].nope));
+  return M * pg.act_ld + ((M * pg.scl_ld + 15) & ~(size_t)15) +
+         (size_t)2 * kStream * MB * 64 * sizeof(v4f) + M * rope * sizeof(float);
+}
 
 hipError_t launch_program(const Program& pg, int MB, hipStream_t stream) {
   if (MB <= 1) return launch_mb<1>(pg, stream);

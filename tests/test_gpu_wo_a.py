@@ -7,6 +7,8 @@ Unique results are compared bit for bit: the MXFP8 codes of the rotated input
 with the oracle's grouped projection within tolerance, wo_b's output
 stage-wise (oracle GEMM on the GPU's z codes) and end to end on every row
 whose z codes match the oracle's."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -20,6 +22,14 @@ pytestmark = pytest.mark.gpu
 
 # Reduced dims (same structure: 448 + 64 head dims, 8 heads per group).
 SMALL = dict(n_heads=16, head_dim=512, nope=448, n_groups=2, rank=256, n_out=384)
+
+
+@pytest.fixture(params=["direct", "stage"], autouse=True)
+def woa_path(request, monkeypatch):
+    """Every test runs on both WO-A implementations (three direct launches,
+    or one stage-kernel launch)."""
+    monkeypatch.setenv("MXG_WOA_PATH", request.param)
+    return request.param
 
 
 def _weights(case):
@@ -55,7 +65,8 @@ def run_wo_a(case, w, M, *, with_wb=True, keep_z=True, positions=None, o_dev=Non
     pos = (case["positions"][:M] if positions is None else positions).clone()
     ref = oracle.wo_a(o_bits, pos.numpy(), case["cos_sin"], wa_q, wa_s,
                       wb_o if with_wb else None, nope=nope, n_groups=G)
-    say(f"wo_a M={M} H={H} D={D} G={G} R={R} wb={with_wb} keep_z={keep_z}")
+    say(f"wo_a M={M} H={H} D={D} G={G} R={R} wb={with_wb} keep_z={keep_z} "
+        f"path={os.environ.get('MXG_WOA_PATH')}")
     o = dev_bf16(o_bits) if o_dev is None else o_dev
     ws = torch.zeros(32 << 20, dtype=torch.uint8, device="cuda")
     z, z_q, z_s, out = mx.wo_a_fused_quantize(
