@@ -38,8 +38,9 @@
  *   - Row counts: 1 <= M <= MXG_MAX_ROWS for the GEMM entry points ([mxfp8]:
  *     the low-latency kernel covers up to 48 rows with 16-, 32- or 48-row
  *     activation tiles; more rows go to another kernel).
- *   - K must be a multiple of 128 and N a multiple of 16 for the GEMMs
- *     ([mxfp8] mxfp8_eligible requires the weight's K to be a multiple of 128).
+ *   - K must be a multiple of 128 (at most MXG_MAX_K) and N a multiple of 16
+ *     for the GEMMs ([mxfp8] mxfp8_eligible requires the weight's K to be a
+ *     multiple of 128).
  *   - Inputs holding NaN/Inf (BF16), the E4M3 NaN codes 0x7F/0xFF or the
  *     E8M0 NaN byte 0xFF are outside the contract: the results are unspecified
  *     (the hardware propagates NaN).
@@ -63,6 +64,7 @@ extern "C" {
 #define MXG_ERR_DEVICE 5    /* current device is not gfx950, or a launch failed */
 
 #define MXG_MAX_ROWS 48
+#define MXG_MAX_K 16384     /* largest contraction of the GEMM entry points */
 
 /* Human-readable text of a status code (static storage; never NULL). */
 const char *mxg_strerror(int status);
@@ -115,7 +117,7 @@ int mxfp8_pack_weights(const uint8_t *w_q, const uint8_t *w_s, int64_t N, int64_
  * with the weight's N as its M, as this one does).  FP32 accumulation, BF16
  * output, no scale, no bias.
  *
- *   M, N, K   1 <= M <= 48, N % 16 == 0, K % 128 == 0
+ *   M, N, K   1 <= M <= 48, N % 16 == 0, K % 128 == 0, K <= MXG_MAX_K
  *   x_bf16    NULL: a_q/a_s are inputs.  Non-NULL: BF16 [M, ld_x] activations
  *             that the kernel quantizes itself (as mxfp8_quantize does) and
  *             whose codes/scales it also WRITES to a_q/a_s (the pages'

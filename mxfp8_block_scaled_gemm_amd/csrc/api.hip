@@ -56,7 +56,7 @@ int validate_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* x, int64_t ld
                   const uint8_t* w_s, const uint16_t* out, size_t ws_bytes, const void* ws) {
   if (!a_q || !a_s || !w_q || !w_s || !out) return MXG_ERR_NULL;
   if (M < 1 || M > MXG_MAX_ROWS || N < 16 || N % 16 != 0 || K < 128 || K % 128 != 0 ||
-      N > (int64_t)1 << 24 || K > (int64_t)1 << 20)
+      N > (int64_t)1 << 24 || K > MXG_MAX_K)
     return MXG_ERR_SHAPE;
   if (N * K > ((int64_t)1 << 31) - 1) return MXG_ERR_SHAPE;
   if (x && (ld_x < K || ld_x * M > ((int64_t)1 << 30))) return MXG_ERR_SHAPE;
@@ -71,7 +71,7 @@ int validate_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* x, int64_t ld
 
 bool weight_ok(const mxg_weight& w) {
   return w.N >= 16 && w.N % 16 == 0 && w.K >= 128 && w.K % 128 == 0 && w.N <= ((int64_t)1 << 24) &&
-         w.K <= ((int64_t)1 << 20) && w.N * w.K <= ((int64_t)1 << 31) - 1;
+         w.K <= MXG_MAX_K && w.N * w.K <= ((int64_t)1 << 31) - 1;
 }
 
 int validate_chain(const mxg_chain* c, size_t need) {
@@ -141,6 +141,19 @@ mxg::ProgramBuilder chain_program(const mxg_chain& c, int G) {
   return pb;
 }
 
+// K-split state of a direct GEMM in workspace ws, partials from part_off on.
+void set_ksplit(GemmArgs& a, void* ws, size_t part_off) {
+  uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+  a.ctr = w ? reinterpret_cast<uint32_t*>(w + mxg::kGemmCtrOffset) : nullptr;
+  a.part = w ? reinterpret_cast<float*>(w + part_off) : nullptr;
+}
+
+// Workspace bytes a direct GEMM needs with its partials from part_off on.
+size_t direct_need(int M, int N, int K, size_t part_off, int group_tiles = 0) {
+  const size_t pb = mxg::gemm_partial_bytes(M, N, K, group_tiles);
+  return pb ? part_off + pb : 0;
+}
+
 // Chain kernel choice: by default three direct launches in stream order (B
 // quantizes A's output while staging it); MXG_CHAIN_PATH=stage runs the
 // whole chain as one stage-kernel launch.
@@ -153,12 +166,15 @@ int chain_direct(const mxg_chain& c, hipStream_t stream) {
   const int M = (int)c.M;
   GemmArgs a{nullptr, 0, const_cast<uint8_t*>(c.a_q), const_cast<uint8_t*>(c.a_s), c.wA.q, c.wA.s,
              c.out_a, M, (int)c.wA.N, (int)c.wA.K};
+  set_ksplit(a, c.workspace, mxg::kGemmPartOffset);
   hipError_t e = mxg::launch_gemm(a, stream);
   if (e != hipSuccess) return MXG_ERR_DEVICE;
   GemmArgs b{c.out_a, c.wA.N, c.b_q, c.b_s, c.wB.q, c.wB.s, c.out_b, M, (int)c.wB.N, (int)c.wB.K};
+  set_ksplit(b, c.workspace, mxg::kGemmPartOffset);
   if ((e = mxg::launch_gemm(b, stream)) != hipSuccess) return MXG_ERR_DEVICE;
   GemmArgs cc{nullptr, 0, const_cast<uint8_t*>(c.c_q), const_cast<uint8_t*>(c.c_s), c.wC.q,
               c.wC.s, c.out_c, M, (int)c.wC.N, (int)c.wC.K};
+  set_ksplit(cc, c.workspace, mxg::kGemmPartOffset);
   return launched(mxg::launch_gemm(cc, stream));
 }
 
@@ -257,7 +273,11 @@ mxg::ProgramBuilder wo_a_program(const mxg_wo_a& p, int G) {
 
 // Workspace bytes of WO-A on either path.
 size_t wo_a_need(const mxg_wo_a& p) {
-  size_t need = wo_a_layout(p).end;
+  const WoALayout l = wo_a_layout(p);
+  size_t need = l.end;
+  const int R = (int)p.wa.N / p.n_groups;
+  need = std::max(need, direct_need((int)p.M, (int)p.wa.N, (int)p.wa.K, l.end, R / 16));
+  if (p.wb.q) need = std::max(need, direct_need((int)p.M, (int)p.wb.N, (int)p.wb.K, l.end));
   const int G = mxg::stage_grid();
   if (G > 0) {
     mxg_wo_a probe = p;
@@ -298,10 +318,12 @@ int wo_a_run(const mxg_wo_a& p, hipStream_t stream) {
   ga.lda = HD;
   ga.group_tiles = R / 16;
   ga.a_group = Kg;
+  set_ksplit(ga, p.workspace, l.end);
   if ((e = mxg::launch_gemm(ga, stream)) != hipSuccess) return MXG_ERR_DEVICE;
   // 4-5. MXFP8 of z, written by wo_b's GEMM when there is one.
   if (p.wb.q) {
     GemmArgs gb{z, GR, p.z_q, p.z_s, p.wb.q, p.wb.s, p.out, M, (int)p.wb.N, (int)p.wb.K};
+    set_ksplit(gb, p.workspace, l.end);
     return launched(mxg::launch_gemm(gb, stream));
   }
   return launched(mxg::launch_quantize(z, M, GR, GR, p.z_q, p.z_s, stream));
@@ -342,22 +364,35 @@ const char* mxg_strerror(int status) {
 int mxg_version(void) { return 100; }
 
 size_t mxg_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M < 1 || M > MXG_MAX_ROWS || N < 16 || K < 128) return mxg::kCtrBytes;
+  if (M < 1 || M > MXG_MAX_ROWS || N < 16 || N % 16 || K < 128 || K % 128 || K > MXG_MAX_K)
+    return mxg::kCtrBytes;
+  size_t need = std::max(mxg::kCtrBytes,
+                         direct_need((int)M, (int)N, (int)K, mxg::kGemmPartOffset));
   const int G = mxg::stage_grid();
-  if (G <= 0) return mxg::kCtrBytes;
-  mxg::ProgramBuilder pb = gemm_program((int)M, (int)N, (int)K, nullptr, 0, nullptr, nullptr,
-                                        nullptr, nullptr, nullptr, nullptr, G);
-  return pb.workspace_bytes();
+  if (G > 0) {
+    mxg::ProgramBuilder pb = gemm_program((int)M, (int)N, (int)K, nullptr, 0, nullptr, nullptr,
+                                          nullptr, nullptr, nullptr, nullptr, G);
+    need = std::max(need, pb.workspace_bytes());
+  }
+  return need;
 }
 
 size_t mxg_chain_workspace_bytes(const mxg_chain* c) {
-  if (!c || c->M < 1 || c->M > MXG_MAX_ROWS) return mxg::kCtrBytes;
+  if (!c || c->M < 1 || c->M > MXG_MAX_ROWS || !weight_ok(c->wA) || !weight_ok(c->wB) ||
+      !weight_ok(c->wC))
+    return mxg::kCtrBytes;
+  const int M = (int)c->M;
+  size_t need = mxg::kCtrBytes;
+  for (const mxg_weight* w : {&c->wA, &c->wB, &c->wC})
+    need = std::max(need, direct_need(M, (int)w->N, (int)w->K, mxg::kGemmPartOffset));
   const int G = mxg::stage_grid();
-  if (G <= 0) return mxg::kCtrBytes;
-  mxg_chain probe = *c;
-  probe.workspace = nullptr;
-  mxg::ProgramBuilder pb = chain_program(probe, G);
-  return pb.workspace_bytes();
+  if (G > 0) {
+    mxg_chain probe = *c;
+    probe.workspace = nullptr;
+    mxg::ProgramBuilder pb = chain_program(probe, G);
+    need = std::max(need, pb.workspace_bytes());
+  }
+  return need;
 }
 
 int mxfp8_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* q, uint8_t* s,
@@ -391,6 +426,7 @@ int mxfp8_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* x_bf16, int64_t 
     return run_program(pb, (hipStream_t)stream);
   }
   GemmArgs a{x_bf16, ld_x, a_q, a_s, w_q, w_s, out, (int)M, (int)N, (int)K};
+  set_ksplit(a, workspace, mxg::kGemmPartOffset);
   return launched(mxg::launch_gemm(a, (hipStream_t)stream));
 }
 

@@ -10,27 +10,25 @@
 //   * weights arrive pre-packed in tile order (pack.hip), so each wave reads
 //     its A operand as fully contiguous 1 KiB loads and its scales as one
 //     64-byte load per step;
-//   * a workgroup owns one 16-row weight tile and the whole K; its 8 waves
-//     split K (wave w takes 128-wide steps w, w+8, ...) and each wave issues
+//   * a workgroup owns one 16-row weight tile and the whole K; its 16 waves
+//     split K (wave w takes 128-wide steps w, w+16, ...) and each wave issues
 //     every weight load it will need up front, predicated by buffer range
 //     checks rather than branches, so nothing waits on anything until the
 //     stream is in flight;
 //   * the activations (at most M*K bytes, read by every workgroup) are
-//     staged once per workgroup: loaded with coalesced 16-byte accesses
-//     before the weight loads are issued, quantized in registers when they
-//     come as BF16, and parked in LDS, from where each wave reads its B
-//     operands;
-//   * the 8 partial tiles are summed through LDS in wave order
+//     staged per workgroup: loaded with coalesced 16-byte accesses before
+//     the weight loads are issued, quantized in registers when they come as
+//     BF16, and parked in LDS, from where each wave reads its B operands;
+//     when M*K does not fit (rows above 16, or very long K) they go through
+//     LDS one 16-step K-chunk at a time;
+//   * the 16 partial tiles are summed through LDS in wave order
 //     (deterministic), rounded to BF16 and stored.
-// Rows above 16 (the 32- and 48-row buckets) take a second kernel that reads
-// its activations straight from global memory.
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
 
 namespace mxg {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
+constexpr int kM16Waves = 16;   // waves per workgroup of the GEMM kernels
 
 __host__ __device__ constexpr int act_ld(int K) { return K + 16; }          // LDS bytes per code row
 __host__ __device__ constexpr int scale_ld(int K) { return (K >> 5) + 4; }  // LDS bytes per scale row
@@ -220,161 +218,197 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
   }
 }
 
-// ----------------------------------------------------------- M = 17..48 rows
-//
-// MB activation tiles of 16 rows share each weight tile.  Activations are
-// read straight from global memory per step (too many rows to stage the whole
-// K in LDS); SPW weight steps per chunk.
-template <int MB, int SPW, bool FQ>
-__global__ __launch_bounds__(kThreads) void gemm_wide_kernel(GemmArgs p) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, r = lane & 15;
-  const int K = p.K, KB = K >> 5, S = K >> 7;
-  const int t = xcd_tile(blockIdx.x, p.N >> 4);
-  const int my = S > wave ? (S - wave + kWaves - 1) / kWaves : 0;
-  const auto rw = make_rsrc(p.w_q + (int64_t)t * S * 2048, (uint32_t)(S * 2048));
-  const auto rws = make_rsrc(p.w_s + (int64_t)t * S * 64, (uint32_t)(S * 64));
-  const int64_t grp = p.group_tiles ? (int64_t)(t / p.group_tiles) * p.a_group : 0;
+typedef unsigned v4u32 __attribute__((ext_vector_type(4)));
 
+// ------------------------------------------------- 2D tiling (any M <= 48)
+//
+// When one full-K weight tile per workgroup does not suit the shape (rows
+// above 16: every workgroup would pull all M*K activation bytes through its
+// CU; or a tile count that leaves part of the chip with a second round), a
+// workgroup takes T weight tiles over one of P K parts.  The activation
+// traffic per workgroup falls by P, the weight bytes per workgroup stay
+// near one tile's, and the grid stays near one workgroup per CU.
+//
+// Workgroup (tile group tg, part q): tiles [T tg, T tg + T), steps
+// [q Sp, q Sp + ns).  Wave w serves tile w mod T, taking the steps
+// w / T + (16 / T) j of it, so slot j lies in K-chunk j / T (16 steps,
+// staged through LDS; chunk c is read by slots [c T, c T + T)).  As in the
+// M <= 16 kernel, every weight load is issued up front, after the first
+// (or every) activation chunk's loads.  The 16 / T partial tiles of each
+// tile are summed through LDS in wave order; with P > 1 the FP32 tile sums
+// go to the workspace and the last of the P workgroups of a tile group to
+// arrive adds them in part order (deterministic) and stores BF16.
+template <int MB, int T, int SPW, int NB, int CHM>
+__global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p) {
+  constexpr int W = kM16Waves, kT = W * 64, WPT = W / T;  // waves per tile
+  constexpr int kLdA = 16 * 128 + 16;                   // LDS bytes per code row of a chunk
+  constexpr int kLdS = 16 * 4 + 4;                      // LDS bytes per scale row of a chunk
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ uint32_t s_last;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, r = lane & 15;
+  const int M = p.M, K = p.K, S = K >> 7, Sp = p.Sp, P = p.P;
+  const int ngroups = (p.N >> 4) / T;
+  const int q = blockIdx.x / ngroups;
+  const int tg = xcd_tile(blockIdx.x - q * ngroups, ngroups);
+  const int k0 = q * Sp, ns = min(Sp, S - k0);          // this part's steps
+  const int nch = (ns + 15) >> 4;
+  const int tt = wave % T, wi = wave / T;               // my tile, my index among its waves
+  const int tile = tg * T + tt;
+  uint8_t* s_act = smem;                                // [M][kLdA]
+  uint8_t* s_scl = smem + M * kLdA;                     // [M][kLdS]
+  v4f* s_red = reinterpret_cast<v4f*>(smem);            // [W][MB][64], after the last chunk
+
+  // A tile group lies in one activation group (the plan keeps T | group_tiles).
+  const int64_t grp = p.group_tiles ? (int64_t)(tg * T / p.group_tiles) * p.a_group : 0;
+  const int lda = (int)p.lda, ldas = lda >> 5;
+  const auto ra = make_rsrc(p.a_q + grp, (uint32_t)((M - 1) * lda + K));
+  const auto rs = make_rsrc(p.a_s + (grp >> 5), (uint32_t)((M - 1) * ldas + (K >> 5)));
+  // Chunk c: steps [k0 + 16c, k0 + 16c + 16) within the part.
+  auto stage_load = [&](int c, v4i (&st)[CHM], uint32_t& sc) {
+    const int nsc_steps = min(16, ns - 16 * c);
+    const int cpr = nsc_steps * 8, nck = M * cpr;
+    const int col0 = (k0 + 16 * c) * 128;
+#pragma unroll
+    for (int i = 0; i < CHM; ++i) {
+      const int cc = tid + i * kT;
+      const int row = cc / cpr, col = (cc - row * cpr) * 16;
+      st[i] = buf_ld16(ra, cc < nck ? (uint32_t)(row * lda + col0 + col) : kOutOfRange);
+    }
+    const int nsc = M * nsc_steps;
+    const int row = tid / nsc_steps, cd = tid - row * nsc_steps;
+    sc = __builtin_amdgcn_raw_buffer_load_b32(
+        rs, tid < nsc ? row * ldas + (k0 + 16 * c + cd) * 4 : (int)kOutOfRange, 0, 0);
+  };
+  auto stage_park = [&](int c, const v4i (&st)[CHM], uint32_t sc) {
+    const int nsc_steps = min(16, ns - 16 * c);
+    const int cpr = nsc_steps * 8, nck = M * cpr;
+#pragma unroll
+    for (int i = 0; i < CHM; ++i) {
+      const int cc = tid + i * kT;
+      if (cc < nck) {
+        const int row = cc / cpr, col = (cc - row * cpr) * 16;
+        *reinterpret_cast<v4i*>(s_act + row * kLdA + col) = st[i];
+      }
+    }
+    const int nsc = M * nsc_steps;
+    if (tid < nsc) {
+      const int row = tid / nsc_steps, cd = tid - row * nsc_steps;
+      *reinterpret_cast<uint32_t*>(s_scl + row * kLdS + cd * 4) = sc;
+    }
+  };
+
+  // 1. Activations (chunk 0, or all chunks) ahead of the weight stream.
+  v4i st[NB][CHM];
+  uint32_t sc[NB];
+#pragma unroll
+  for (int c = 0; c < NB; ++c)
+    if (c < nch) stage_load(c, st[c], sc[c]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. The weight stream: slot j = step wi + WPT j of my tile.
+  const auto rw = make_rsrc(p.w_q, (uint32_t)((p.N >> 4) * S * 2048));
+  const auto rws = make_rsrc(p.w_s, (uint32_t)((p.N >> 4) * S * 64));
+  v4i wlo[SPW], whi[SPW];
+  uint32_t wsc[SPW];
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) {
+    const int stp = wi + WPT * j;
+    const bool ok = stp < ns;
+    const uint32_t chunk = (uint32_t)(tile * S + k0 + stp);
+    wlo[j] = buf_ld16_nt(rw, ok ? chunk * 2048 + lane * 16 : kOutOfRange);
+    whi[j] = buf_ld16_nt(rw, ok ? chunk * 2048 + 1024 + lane * 16 : kOutOfRange);
+    wsc[j] = buf_ld8(rws, ok ? chunk * 64 + lane : kOutOfRange);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. Chunk by chunk: park it, (prefetch the next), the MFMAs of its slots.
   v4f acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  for (int c0 = 0; c0 < my; c0 += SPW) {
-    v4i wlo[SPW], whi[SPW];
-    uint32_t wsc[SPW];
+  constexpr int NCH = (SPW + T - 1) / T;
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int s = wave + kWaves * (c0 + j);
-      const bool ok = c0 + j < my;
-      wlo[j] = buf_ld16_nt(rw, ok ? (uint32_t)(s * 2048 + lane * 16) : kOutOfRange);
-      whi[j] = buf_ld16_nt(rw, ok ? (uint32_t)(s * 2048 + 1024 + lane * 16) : kOutOfRange);
-      wsc[j] = buf_ld8(rws, ok ? (uint32_t)(s * 64 + lane) : kOutOfRange);
-    }
-    if constexpr (!FQ) {
-      v4i alo[SPW][MB], ahi[SPW][MB];
-      int asc[SPW][MB];
+  for (int c = 0; c < NCH; ++c) {
+    if (c < nch) {                                      // uniform
+      stage_park(c, st[NB > 1 ? c : 0], sc[NB > 1 ? c : 0]);
+      __syncthreads();
+      if (NB == 1 && c + 1 < nch) stage_load(c + 1, st[0], sc[0]);
 #pragma unroll
-      for (int j = 0; j < SPW; ++j) {
-        const int s = wave + kWaves * min(c0 + j, my - 1);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int m = 16 * mb + r;
-          if (m < p.M && c0 + j < my) {
-            const uint8_t* ap = p.a_q + grp + (int64_t)m * p.lda + s * 128 + 16 * g;
-            alo[j][mb] = ld16(ap);
-            ahi[j][mb] = ld16(ap + 64);
-            asc[j][mb] = p.a_s[(grp >> 5) + (int64_t)m * (p.lda >> 5) + 4 * s + g];
-          } else {
-            alo[j][mb] = ahi[j][mb] = v4i{0, 0, 0, 0};
-            asc[j][mb] = 0;
-          }
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < SPW; ++j) {
-        if (c0 + j < my) {
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            acc[mb] = mfma_mx16(cat8(wlo[j], whi[j]), cat8(alo[j][mb], ahi[j][mb]), acc[mb],
-                                (int)wsc[j], asc[j][mb]);
-        }
-      }
-    } else {
-      // BF16 activations quantized in registers: lane (g, r) holds K
-      // [16g, 16g+16) and [64+16g, ..+16) of row m, i.e. half of MFMA block
-      // g/2 and half of block 2 + g/2; lane g ^ 1 holds the other halves.
-      v4i x0[SPW][MB], x1[SPW][MB], x2[SPW][MB], x3[SPW][MB];
-#pragma unroll
-      for (int j = 0; j < SPW; ++j) {
-        const int s = wave + kWaves * min(c0 + j, my - 1);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int m = 16 * mb + r;
-          if (m < p.M && c0 + j < my) {
-            const uint16_t* xp = p.x + (int64_t)m * p.ld_x + s * 128 + 16 * g;
-            x0[j][mb] = ld16(xp);
-            x1[j][mb] = ld16(xp + 8);
-            x2[j][mb] = ld16(xp + 64);
-            x3[j][mb] = ld16(xp + 72);
-          } else {
-            x0[j][mb] = x1[j][mb] = x2[j][mb] = x3[j][mb] = v4i{0, 0, 0, 0};
-          }
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < SPW; ++j) {
-        if (c0 + j < my) {
-          const int s = wave + kWaves * (c0 + j);
+      for (int j = c * T; j < c * T + T && j < SPW; ++j) {
+        const int stp = wi + WPT * j;
+        if (stp < ns) {
+          const int sl = stp - 16 * c;                  // step within the chunk
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
-            uint32_t alo = 0, ahi = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              alo = bf16x2_absmax2(alo, bf16x2_absmax2((uint32_t)x0[j][mb][i], (uint32_t)x1[j][mb][i]));
-              ahi = bf16x2_absmax2(ahi, bf16x2_absmax2((uint32_t)x2[j][mb][i], (uint32_t)x3[j][mb][i]));
-            }
-            alo = halves_max(alo);
-            ahi = halves_max(ahi);
-            alo = max(alo, (uint32_t)__shfl_xor((int)alo, 16));
-            ahi = max(ahi, (uint32_t)__shfl_xor((int)ahi, 16));
-            const int elo = block_exponent(alo), ehi = block_exponent(ahi);
-            // The MFMA takes block b's scale from lanes g == b: g = 0 and 3
-            // own it; g = 1 needs block 1 (first halves of g = 2, 3) and g = 2
-            // needs block 2 (second halves of g = 0, 1).
-            const int give = (g == 1) ? ehi : elo;
-            const int src = (g == 1) ? lane + 16 : ((g == 2) ? lane - 16 : lane);
-            const int got = __shfl(give, src);
-            const int e = (g == 0) ? elo : ((g == 3) ? ehi : got);
-            const BlockScale blo = block_scale(elo), bhi = block_scale(ehi);
-            v4i clo, chi;
-            clo[0] = (int)enc4_e4m3((uint32_t)x0[j][mb][0], (uint32_t)x0[j][mb][1], blo);
-            clo[1] = (int)enc4_e4m3((uint32_t)x0[j][mb][2], (uint32_t)x0[j][mb][3], blo);
-            clo[2] = (int)enc4_e4m3((uint32_t)x1[j][mb][0], (uint32_t)x1[j][mb][1], blo);
-            clo[3] = (int)enc4_e4m3((uint32_t)x1[j][mb][2], (uint32_t)x1[j][mb][3], blo);
-            chi[0] = (int)enc4_e4m3((uint32_t)x2[j][mb][0], (uint32_t)x2[j][mb][1], bhi);
-            chi[1] = (int)enc4_e4m3((uint32_t)x2[j][mb][2], (uint32_t)x2[j][mb][3], bhi);
-            chi[2] = (int)enc4_e4m3((uint32_t)x3[j][mb][0], (uint32_t)x3[j][mb][1], bhi);
-            chi[3] = (int)enc4_e4m3((uint32_t)x3[j][mb][2], (uint32_t)x3[j][mb][3], bhi);
-            const int m = 16 * mb + r;
-            if (blockIdx.x == 0 && m < p.M) {
-              uint8_t* qp = p.a_q + (int64_t)m * K + s * 128 + 16 * g;
-              st16(qp, clo);
-              st16(qp + 64, chi);
-              p.a_s[(int64_t)m * KB + 4 * s + g] = (uint8_t)(e + 127);
-            }
-            acc[mb] = mfma_mx16(cat8(wlo[j], whi[j]), cat8(clo, chi), acc[mb], (int)wsc[j],
-                                e + 127);
+            const int m = min(16 * mb + r, M - 1);      // rows past M: never stored
+            const uint8_t* a = s_act + m * kLdA + sl * 128 + 16 * g;
+            const v4i blo = *reinterpret_cast<const v4i*>(a);
+            const v4i bhi = *reinterpret_cast<const v4i*>(a + 64);
+            const int bsc = s_scl[m * kLdS + 4 * sl + g];
+            acc[mb] = mfma_mx16(cat8(wlo[j], whi[j]), cat8(blo, bhi), acc[mb], (int)wsc[j], bsc);
           }
         }
       }
+      __syncthreads();
     }
   }
 
-  __shared__ v4f red[kWaves][MB][64];
+  // 4. Per tile: sum its WPT partial tiles in wave order (wave tt*MB + mb
+  //    sums tile tt's row block mb).
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) red[wave][mb][lane] = acc[mb];
+  for (int mb = 0; mb < MB; ++mb) s_red[(wave * MB + mb) * 64 + lane] = acc[mb];
   __syncthreads();
-  const int tid = threadIdx.x;
-  if (tid < MB * 64) {
-    const int mb = tid >> 6, ln = tid & 63;
-    v4f sum = red[0][mb][ln];
+  const bool red = wave < T * MB;
+  const int rt = wave / MB, rmb = wave - rt * MB;        // tile and row block I sum
+  v4f sum = {0.f, 0.f, 0.f, 0.f};
+  if (red) {
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) sum += red[w][mb][ln];
-    const int m = 16 * mb + (ln & 15);
-    const int n = 16 * t + 4 * (ln >> 4);
-    if (m < p.M) {
+    for (int i = 0; i < WPT; ++i) sum += s_red[((rt + T * i) * MB + rmb) * 64 + lane];
+  }
+  const int otile = tg * T + rt;
+  const int m = 16 * rmb + (lane & 15), n = 16 * otile + 4 * (lane >> 4);
+  if (P == 1) {
+    if (red && m < M) {
       uint2 o;
       o.x = f32_to_bf16(sum[0]) | (f32_to_bf16(sum[1]) << 16);
       o.y = f32_to_bf16(sum[2]) | (f32_to_bf16(sum[3]) << 16);
       *reinterpret_cast<uint2*>(p.out + (int64_t)m * p.N + n) = o;
     }
+    return;
   }
+  // K split: FP32 tile sums to the workspace (device-coherent), then one
+  // arrival per workgroup on the tile group's counter.
+  const uint32_t pstride = (uint32_t)(P * MB * 64 * 16);        // bytes per tile
+  const auto rp = make_rsrc(reinterpret_cast<uint8_t*>(p.part), (uint32_t)((p.N >> 4) * pstride));
+  if (red)
+    __builtin_amdgcn_raw_buffer_store_b128(
+        __builtin_bit_cast(v4u32, sum), rp,
+        (int)(otile * pstride + ((q * MB + rmb) * 64 + lane) * 16), 0, 16);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(p.ctr + tg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)(P - 1);
+  __syncthreads();
+  if (!s_last) return;
+  if (red) {
+    v4f tot = {0.f, 0.f, 0.f, 0.f};
+    for (int qq = 0; qq < P; ++qq)
+      tot += __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rp, (int)(otile * pstride + ((qq * MB + rmb) * 64 + lane) * 16),
+                                         0, 16));
+    if (m < M) {
+      uint2 o;
+      o.x = f32_to_bf16(tot[0]) | (f32_to_bf16(tot[1]) << 16);
+      o.y = f32_to_bf16(tot[2]) | (f32_to_bf16(tot[3]) << 16);
+      *reinterpret_cast<uint2*>(p.out + (int64_t)m * p.N + n) = o;
+    }
+  }
+  if (tid == 0) __hip_atomic_store(p.ctr + tg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ launch
-
-constexpr int kM16Waves = 16;
 
 size_t gemm_m16_lds_bytes(int M, int K) {
   return (size_t)((M * act_ld(K) + M * scale_ld(K) + 15) & ~15) + kM16Waves * 64 * sizeof(v4f);
@@ -416,11 +450,122 @@ static hipError_t launch_m16_spw(const GemmArgs& a, int spw, int ch, hipStream_t
   return launch_m16_ch<4, FQ>(a, ch, stream);
 }
 
-template <int MB, int SPW, bool FQ>
-static hipError_t launch_wide(const GemmArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_wide_kernel<MB, SPW, FQ>), dim3(a.N / 16), dim3(kThreads), 0, stream,
+size_t gemm_2d_lds_bytes(int M, int MB) {
+  const size_t act = (size_t)M * (16 * 128 + 16) + (size_t)M * (16 * 4 + 4);
+  const size_t red = (size_t)kM16Waves * MB * 64 * sizeof(v4f);
+  return ((act > red ? act : red) + 15) & ~(size_t)15;
+}
+
+namespace {
+
+// A 2D plan: T tiles per workgroup, P K parts of Sp steps, SPW weight slots
+// per wave.
+struct Plan {
+  int T, P, Sp, SPW;
+  double cost;
+};
+
+constexpr int kSlotSizes[] = {1, 2, 3, 4, 6, 8};
+
+int round_slots(int spw) {
+  for (int v : kSlotSizes)
+    if (spw <= v) return v;
+  return 0;
+}
+
+// The plan whose busiest workgroup moves the fewest bytes: weights at its
+// share of HBM bandwidth, activations at the rate one CU pulls them from L2,
+// plus the cross-workgroup sum of a K split.  Rates from measurements on
+// MI355X (about 6.5 TB/s of weights streamed chip-wide; about 46 GB/s of
+// activations into one CU while every CU reads the same lines).
+Plan choose_plan(int M, int N, int K, int group_tiles, int cus) {
+  const int tiles = N / 16, S = K / 128, MB = (M + 15) / 16;
+  Plan best{0, 0, 0, 0, 1e30};
+  for (int T : {1, 2, 4}) {
+    if (tiles % T || (group_tiles && group_tiles % T) || T * MB > 16) continue;
+    for (int P : {1, 2, 3, 4, 6, 8}) {
+      if (P > S) break;
+      const int Sp = (S + P - 1) / P;
+      if ((P - 1) * Sp >= S) continue;                  // no empty part
+      const int spw = round_slots((T * Sp + 15) / 16);
+      if (spw == 0) continue;
+      const int groups = tiles / T, wgs = groups * P;
+      if (P > 1 && (8192 + (size_t)groups * 4 > 65536)) continue;
+      const int rounds = (wgs + cus - 1) / cus;
+      const int active = wgs < cus ? wgs : cus;
+      const double wb = (double)T * Sp * 2112.0, ab = (double)M * Sp * 132.0;
+      const double cost = rounds * (wb / (6.5e12 / active) + ab / 46e9) + (P > 1 ? 1.5e-6 : 0.0);
+      if (cost < best.cost) best = Plan{T, P, Sp, spw, cost};
+    }
+  }
+  return best;
+}
+
+int device_cus() {
+  static int cached = 0;
+  if (cached == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus > 0)
+      cached = cus;
+    else
+      return 256;
+  }
+  return cached;
+}
+
+template <int MB, int T, int SPW>
+hipError_t launch_2d(const GemmArgs& a, hipStream_t stream) {
+  constexpr int CHM = (MB * 16 * 16 * 8 + kM16Waves * 64 - 1) / (kM16Waves * 64);
+  constexpr int NCH = (SPW + T - 1) / T;
+  // Every chunk's activations in registers while they fit beside the slots.
+  constexpr int NB = NCH * CHM * 4 + SPW * 9 + MB * 4 <= 120 ? NCH : 1;
+  auto kern = gemm_2d_kernel<MB, T, SPW, NB, CHM>;
+  static bool configured = false;
+  if (!configured) {
+    // 160 KiB of LDS per workgroup, less the kernel's static word
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       160 * 1024 - 64);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  const int grid = (a.N / 16 / T) * a.P;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kM16Waves * 64), gemm_2d_lds_bytes(a.M, MB), stream,
                      a);
   return hipGetLastError();
+}
+
+template <int MB, int T>
+hipError_t launch_2d_spw(const GemmArgs& a, int spw, hipStream_t stream) {
+  switch (spw) {
+    case 1: return launch_2d<MB, T, 1>(a, stream);
+    case 2: return launch_2d<MB, T, 2>(a, stream);
+    case 3: return launch_2d<MB, T, 3>(a, stream);
+    case 4: return launch_2d<MB, T, 4>(a, stream);
+    case 6: return launch_2d<MB, T, 6>(a, stream);
+    default: return launch_2d<MB, T, 8>(a, stream);
+  }
+}
+
+template <int MB>
+hipError_t launch_2d_t(const GemmArgs& a, int T, int spw, hipStream_t stream) {
+  if (T == 1) return launch_2d_spw<MB, 1>(a, spw, stream);
+  if (T == 2) return launch_2d_spw<MB, 2>(a, spw, stream);
+  return launch_2d_spw<MB, 4>(a, spw, stream);
+}
+
+}  // namespace
+
+size_t gemm_partial_bytes(int M, int N, int K, int group_tiles) {
+  const Plan pl = choose_plan(M, N, K, group_tiles, device_cus());
+  return pl.P > 1 ? (size_t)(N / 16) * pl.P * ((M + 15) / 16) * 64 * 16 : 0;
+}
+
+int gemm_counter_words(int M, int N, int K, int group_tiles) {
+  const Plan pl = choose_plan(M, N, K, group_tiles, device_cus());
+  return pl.P > 1 ? N / 16 / pl.T : 0;
 }
 
 // Whether the M <= 16 kernel can stage this activation in LDS.
@@ -435,7 +580,12 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
   const int steps = (S + kM16Waves - 1) / kM16Waves;       // weight steps per wave
   const int per = fq ? a.M * a.K / 8 : a.M * a.K / 16;     // 16-byte staging chunks
   const int ch = (per + kM16Waves * 64 - 1) / (kM16Waves * 64);
-  if (gemm_m16_fits(a.M, a.K) && steps <= 4) {
+  const Plan pl = choose_plan(a.M, a.N, a.K, a.group_tiles, device_cus());
+  // One full-K tile per workgroup with the whole activation in LDS when the
+  // grid takes one round of the chip: the tiles fit one workgroup per CU, or
+  // two workgroups share a CU's LDS.  Otherwise the 2D kernel.
+  const bool one_round = a.N / 16 <= device_cus() || gemm_m16_lds_bytes(a.M, a.K) <= 80 * 1024;
+  if (gemm_m16_fits(a.M, a.K) && steps <= 4 && (one_round || (pl.T == 1 && pl.P == 1))) {
     if (!fq && ch <= 16) return launch_m16_spw<false>(a, steps, ch, stream);
     // In-kernel quantize while the weight stream is in flight when the
     // activation is small (every workgroup quantizes all of it, which costs
@@ -450,15 +600,21 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
       return launch_gemm(b, stream);
     }
   }
-  const int mb = (a.M + 15) / 16;
-  if (!fq) {
-    if (mb == 1) return launch_wide<1, 8, false>(a, stream);
-    if (mb == 2) return launch_wide<2, 6, false>(a, stream);
-    return launch_wide<3, 4, false>(a, stream);
+  // Otherwise the 2D kernel; BF16 input is quantized by its own launch first.
+  if (fq) {
+    hipError_t e = launch_quantize(a.x, a.M, a.K, a.ld_x, a.a_q, a.a_s, stream);
+    if (e != hipSuccess) return e;
   }
-  if (mb == 1) return launch_wide<1, 6, true>(a, stream);
-  if (mb == 2) return launch_wide<2, 4, true>(a, stream);
-  return launch_wide<3, 3, true>(a, stream);
+  GemmArgs b = a;
+  b.x = nullptr;
+  if (pl.T == 0) return hipErrorInvalidValue;
+  b.P = pl.P;
+  b.Sp = pl.Sp;
+  if (pl.P > 1 && (b.ctr == nullptr || b.part == nullptr)) return hipErrorInvalidValue;
+  const int mb = (a.M + 15) / 16;
+  if (mb == 1) return launch_2d_t<1>(b, pl.T, pl.SPW, stream);
+  if (mb == 2) return launch_2d_t<2>(b, pl.T, pl.SPW, stream);
+  return launch_2d_t<3>(b, pl.T, pl.SPW, stream);
 }
 
 }  // namespace mxg

@@ -23,7 +23,23 @@ struct GemmArgs {
   int64_t lda = 0;       // 0: K
   int group_tiles = 0;
   int64_t a_group = 0;
+  // Workspace of a K-split plan: tile-group counters at ctr (zero on entry,
+  // zero again on exit) and FP32 partial tiles at part.  May be null when
+  // gemm_workspace_bytes() is 0 for the shape.
+  uint32_t* ctr = nullptr;
+  float* part = nullptr;
+  int P = 1, Sp = 0;     // K split of the 2D kernel (set by the launcher)
 };
+
+// Bytes of FP32 partials the GEMM of this shape needs (0: no K split); the
+// counters need gemm_counter_words() words.
+size_t gemm_partial_bytes(int M, int N, int K, int group_tiles = 0);
+int gemm_counter_words(int M, int N, int K, int group_tiles = 0);
+
+// Workspace offsets of the direct kernels' K-split state (the first 64 KiB
+// of every workspace are counters, zero between calls).
+constexpr size_t kGemmCtrOffset = 8192;
+constexpr size_t kGemmPartOffset = 64 * 1024;
 
 hipError_t launch_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
                            uint8_t* q, uint8_t* s, hipStream_t stream);
