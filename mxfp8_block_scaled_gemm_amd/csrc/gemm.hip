@@ -23,6 +23,9 @@
 //     LDS one 16-step K-chunk at a time;
 //   * the 16 partial tiles are summed through LDS in wave order
 //     (deterministic), rounded to BF16 and stored.
+#include <cstdlib>
+#include <cstring>
+
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
 
@@ -324,10 +327,54 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p) {
   __builtin_amdgcn_sched_barrier(0);
 
   // 3. Chunk by chunk: park it, (prefetch the next), the MFMAs of its slots.
+  //    When every chunk is in registers and the part fits LDS, all chunks
+  //    are parked side by side behind one barrier and each wave then runs
+  //    its MFMAs as its own weights land.
   v4f acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = v4f{0.f, 0.f, 0.f, 0.f};
   constexpr int NCH = (SPW + T - 1) / T;
+  if constexpr (NB == NCH && NB > 1) {
+    const int ldA = Sp * 128 + 16, ldS = Sp * 4 + 4;
+    uint8_t* w_scl = smem + M * ldA;
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      if (c < nch) {
+        const int nsc_steps = min(16, ns - 16 * c);
+        const int cpr = nsc_steps * 8, nck = M * cpr;
+#pragma unroll
+        for (int i = 0; i < CHM; ++i) {
+          const int cc = tid + i * kT;
+          if (cc < nck) {
+            const int row = cc / cpr, col = (cc - row * cpr) * 16;
+            *reinterpret_cast<v4i*>(s_act + row * ldA + 2048 * c + col) = st[c][i];
+          }
+        }
+        const int nsc = M * nsc_steps;
+        if (tid < nsc) {
+          const int row = tid / nsc_steps, cd = tid - row * nsc_steps;
+          *reinterpret_cast<uint32_t*>(w_scl + row * ldS + 64 * c + cd * 4) = sc[c];
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int stp = wi + WPT * j;
+      if (stp < ns) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int m = min(16 * mb + r, M - 1);        // rows past M: never stored
+          const uint8_t* a = s_act + m * ldA + stp * 128 + 16 * g;
+          const v4i blo = *reinterpret_cast<const v4i*>(a);
+          const v4i bhi = *reinterpret_cast<const v4i*>(a + 64);
+          const int bsc = w_scl[m * ldS + 4 * stp + g];
+          acc[mb] = mfma_mx16(cat8(wlo[j], whi[j]), cat8(blo, bhi), acc[mb], (int)wsc[j], bsc);
+        }
+      }
+    }
+    __syncthreads();                                    // LDS reused for the sums
+  } else {
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     if (c < nch) {                                      // uniform
@@ -352,6 +399,7 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p) {
       }
       __syncthreads();
     }
+  }
   }
 
   // 4. Per tile: sum its WPT partial tiles in wave order (wave tt*MB + mb
@@ -473,11 +521,23 @@ int round_slots(int spw) {
   return 0;
 }
 
-// The plan whose busiest workgroup moves the fewest bytes: weights at its
-// share of HBM bandwidth, activations at the rate one CU pulls them from L2,
-// plus the cross-workgroup sum of a K split.  Rates from measurements on
+// The time model of a plan: the busiest workgroup's bytes, weights at its
+// share of HBM bandwidth and activations at the rate one CU pulls them from
+// L2, plus the cross-workgroup sum of a K split.  Rates from measurements on
 // MI355X (about 6.5 TB/s of weights streamed chip-wide; about 46 GB/s of
-// activations into one CU while every CU reads the same lines).
+// activations into one CU while every CU reads the same lines).  T = P = 1
+// also models the M <= 16 kernel (one full-K tile per workgroup).
+double plan_cost(int M, int N, int K, int T, int P, int cus) {
+  const int tiles = N / 16, S = K / 128;
+  const int Sp = (S + P - 1) / P;
+  const int groups = tiles / T, wgs = groups * P;
+  const int rounds = (wgs + cus - 1) / cus;
+  const int active = wgs < cus ? wgs : cus;
+  const double wb = (double)T * Sp * 2112.0, ab = (double)M * Sp * 132.0;
+  return rounds * (wb / (6.5e12 / active) + ab / 46e9) + (P > 1 ? 1.5e-6 : 0.0);
+}
+
+// The 2D plan of least modelled time.
 Plan choose_plan(int M, int N, int K, int group_tiles, int cus) {
   const int tiles = N / 16, S = K / 128, MB = (M + 15) / 16;
   Plan best{0, 0, 0, 0, 1e30};
@@ -489,12 +549,8 @@ Plan choose_plan(int M, int N, int K, int group_tiles, int cus) {
       if ((P - 1) * Sp >= S) continue;                  // no empty part
       const int spw = round_slots((T * Sp + 15) / 16);
       if (spw == 0) continue;
-      const int groups = tiles / T, wgs = groups * P;
-      if (P > 1 && (8192 + (size_t)groups * 4 > 65536)) continue;
-      const int rounds = (wgs + cus - 1) / cus;
-      const int active = wgs < cus ? wgs : cus;
-      const double wb = (double)T * Sp * 2112.0, ab = (double)M * Sp * 132.0;
-      const double cost = rounds * (wb / (6.5e12 / active) + ab / 46e9) + (P > 1 ? 1.5e-6 : 0.0);
+      if (P > 1 && (8192 + (size_t)(tiles / T) * 4 > 65536)) continue;
+      const double cost = plan_cost(M, N, K, T, P, cus);
       if (cost < best.cost) best = Plan{T, P, Sp, spw, cost};
     }
   }
@@ -519,21 +575,39 @@ template <int MB, int T, int SPW>
 hipError_t launch_2d(const GemmArgs& a, hipStream_t stream) {
   constexpr int CHM = (MB * 16 * 16 * 8 + kM16Waves * 64 - 1) / (kM16Waves * 64);
   constexpr int NCH = (SPW + T - 1) / T;
-  // Every chunk's activations in registers while they fit beside the slots.
-  constexpr int NB = NCH * CHM * 4 + SPW * 9 + MB * 4 <= 120 ? NCH : 1;
-  auto kern = gemm_2d_kernel<MB, T, SPW, NB, CHM>;
-  static bool configured = false;
-  if (!configured) {
-    // 160 KiB of LDS per workgroup, less the kernel's static word
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       160 * 1024 - 64);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  // The whole part's activations in registers (then in LDS at once) while
+  // they fit beside the weight slots; otherwise chunk by chunk.
+  constexpr bool kRegs = NCH * CHM * 4 + SPW * 9 + MB * 4 <= 120;
+  const size_t whole_lds = (size_t)a.M * (a.Sp * 128 + 16) + (size_t)a.M * (a.Sp * 4 + 4);
+  const bool whole = kRegs && NCH > 1 && whole_lds <= 160 * 1024 - 64;
   const int grid = (a.N / 16 / T) * a.P;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kM16Waves * 64), gemm_2d_lds_bytes(a.M, MB), stream,
-                     a);
+  if (whole) {
+    auto kern = gemm_2d_kernel<MB, T, SPW, (kRegs ? NCH : 1), CHM>;
+    static bool configured = false;
+    if (!configured) {
+      // 160 KiB of LDS per workgroup, less the kernel's static word
+      hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         160 * 1024 - 64);
+      if (e != hipSuccess) return e;
+      configured = true;
+    }
+    size_t lds = gemm_2d_lds_bytes(a.M, MB);
+    if (whole_lds > lds) lds = (whole_lds + 15) & ~(size_t)15;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kM16Waves * 64), lds, stream, a);
+  } else {
+    auto kern = gemm_2d_kernel<MB, T, SPW, 1, CHM>;
+    static bool configured = false;
+    if (!configured) {
+      hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         160 * 1024 - 64);
+      if (e != hipSuccess) return e;
+      configured = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kM16Waves * 64), gemm_2d_lds_bytes(a.M, MB), stream,
+                       a);
+  }
   return hipGetLastError();
 }
 
@@ -568,6 +642,16 @@ int gemm_counter_words(int M, int N, int K, int group_tiles) {
   return pl.P > 1 ? N / 16 / pl.T : 0;
 }
 
+// MXG_DIRECT_KERNEL ("m16" / "2d") forces the kernel where both apply
+// (tests use it to cover both on the same shapes); 0 = choose.
+int forced_kernel() {
+  const char* e = std::getenv("MXG_DIRECT_KERNEL");
+  if (!e) return 0;
+  if (std::strcmp(e, "m16") == 0) return 1;
+  if (std::strcmp(e, "2d") == 0) return 2;
+  return 0;
+}
+
 // Whether the M <= 16 kernel can stage this activation in LDS.
 bool gemm_m16_fits(int M, int K) { return M <= 16 && gemm_m16_lds_bytes(M, K) <= 160 * 1024; }
 
@@ -581,11 +665,14 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
   const int per = fq ? a.M * a.K / 8 : a.M * a.K / 16;     // 16-byte staging chunks
   const int ch = (per + kM16Waves * 64 - 1) / (kM16Waves * 64);
   const Plan pl = choose_plan(a.M, a.N, a.K, a.group_tiles, device_cus());
-  // One full-K tile per workgroup with the whole activation in LDS when the
-  // grid takes one round of the chip: the tiles fit one workgroup per CU, or
-  // two workgroups share a CU's LDS.  Otherwise the 2D kernel.
-  const bool one_round = a.N / 16 <= device_cus() || gemm_m16_lds_bytes(a.M, a.K) <= 80 * 1024;
-  if (gemm_m16_fits(a.M, a.K) && steps <= 4 && (one_round || (pl.T == 1 && pl.P == 1))) {
+  // One full-K tile per workgroup with the whole activation in LDS unless
+  // the model gives a 2D plan at most 3/4 of its time: the M <= 16 kernel
+  // keeps more loads in flight per CU (two workgroups share a CU when their
+  // LDS fits) and has less fixed cost, which the model leaves out.
+  const bool m16_fast = pl.cost >= 0.75 * plan_cost(a.M, a.N, a.K, 1, 1, device_cus());
+  const int force = forced_kernel();                       // tests: 1 = M <= 16 kernel, 2 = 2D
+  const bool m16_ok = gemm_m16_fits(a.M, a.K) && steps <= 4;
+  if (m16_ok && (force == 1 || (force == 0 && m16_fast))) {
     if (!fq && ch <= 16) return launch_m16_spw<false>(a, steps, ch, stream);
     // In-kernel quantize while the weight stream is in flight when the
     // activation is small (every workgroup quantizes all of it, which costs

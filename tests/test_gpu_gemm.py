@@ -17,10 +17,17 @@ from helpers import check_gemm, dev_bf16, dev_u8, host_bits, host_u8, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=["stage", "direct"])
+@pytest.fixture(params=["stage", "direct", "direct-m16", "direct-2d"])
 def path(request, monkeypatch):
-    """Run a test through the persistent stage kernel and the direct kernels."""
-    monkeypatch.setenv("MXG_GEMM_PATH", request.param)
+    """Run a test through the persistent stage kernel and the direct kernels:
+    as routed, and with the M <= 16 kernel or the 2D-tiled kernel forced
+    wherever it applies."""
+    kind, _, kernel = request.param.partition("-")
+    monkeypatch.setenv("MXG_GEMM_PATH", kind)
+    if kernel:
+        monkeypatch.setenv("MXG_DIRECT_KERNEL", kernel)
+    else:
+        monkeypatch.delenv("MXG_DIRECT_KERNEL", raising=False)
     return request.param
 
 _wcache = {}
