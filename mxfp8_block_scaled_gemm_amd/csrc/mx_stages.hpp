@@ -47,6 +47,7 @@ struct StageDesc {
   int consumed;                // a later stage depends on this one
   int M, N, K, S;              // S = K / 128
   int tiles, P, Sp, units, rot;
+  int uq, ur;                  // units / G, units % G (workgroup f from rot takes uq, +1 if f < ur)
   int group_tiles;             // weight tiles per activation group
   uint16_t arrive_target[kGroups];  // workgroups of each group with units here
   const uint8_t* wq;           // packed weight codes (mxfp8_pack_weights order)

@@ -123,13 +123,15 @@ bool ProgramBuilder::finish() {
     // more in one stage are not the same ones in the next.
     d.rot = rot;
     rot = (rot + d.units) % pg_.G;
-    // Workgroups b with units in this stage: f = (b - rot) mod G has a
-    // non-empty range [f*U/G, (f+1)*U/G).
+    // Workgroup b, f = (b - rot) mod G places from the rotation, takes the
+    // units [f*uq + min(f, ur), ...) of count uq + (f < ur): the workgroups
+    // with units are those with uq > 0 or f < ur.
+    d.uq = d.units / pg_.G;
+    d.ur = d.units % pg_.G;
     for (int x = 0; x < kGroups; ++x) d.arrive_target[x] = 0;
     for (int b = 0; b < pg_.G; ++b) {
       const int f = ((b - d.rot) % pg_.G + pg_.G) % pg_.G;
-      const long lo = (long)f * d.units / pg_.G, hi = (long)(f + 1) * d.units / pg_.G;
-      if (hi > lo) ++d.arrive_target[b % kGroups];
+      if (d.uq > 0 || f < d.ur) ++d.arrive_target[b % kGroups];
     }
     if (d.dep >= 0) {
       pg_.st[d.dep].consumed = 1;

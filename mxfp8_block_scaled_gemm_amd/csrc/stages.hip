@@ -82,9 +82,6 @@ __device__ __forceinline__ uint32_t* arrive_word(ProgPtr pg, int s, int x) {
 __device__ __forceinline__ v4i ld16_c(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCoherent));
 }
-__device__ __forceinline__ uint32_t ld4_c(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kCoherent);
-}
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void st16_c(__amdgpu_buffer_rsrc_t r, uint32_t off, v4i v) {
@@ -92,6 +89,20 @@ __device__ __forceinline__ void st16_c(__amdgpu_buffer_rsrc_t r, uint32_t off, v
 }
 __device__ __forceinline__ void st8_c(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v2u{v.x, v.y}, r, (int)off, 0, kCoherent);
+}
+
+// Marks a wave-uniform value as such (the compiler cannot always prove it,
+// and a value it thinks divergent turns buffer resources into per-lane loops).
+// Arguments of a non-inlined function arrive in vector registers, so each
+// such function marks its uniform arguments again on entry: descriptor
+// fields are then scalar loads rather than vector loads.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+template <class P>
+__device__ __forceinline__ P uni_ptr(P p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (P)(((uint64_t)hi << 32) | lo);
 }
 
 // Workgroup barrier that orders LDS only: outstanding global loads (the
@@ -116,6 +127,9 @@ __device__ __forceinline__ void io_sync(uint32_t* bar, uint32_t& k, int lane) {
 // (io wave 0 polls, lanes 0..7 one group each; the others wait in io_sync).
 __device__ __noinline__ void wait_stage(ProgPtr pg, int d, int iw, int lane, uint32_t* bar,
                            uint32_t& k) {
+  pg = uni_ptr(pg);
+  d = uni(d);
+  iw = uni(iw);
   if (iw == 0) {
     StagePtr sd = &pg->st[d];
     const uint32_t target = lane < kGroups ? sd->arrive_target[lane] : 0;
@@ -140,6 +154,10 @@ __device__ __noinline__ void wait_stage(ProgPtr pg, int d, int iw, int lane, uin
 // have landed, count one arrival for the workgroup's group.
 __device__ __noinline__ void arrive_stage(ProgPtr pg, int s, int b, int iw, int lane, uint32_t* bar,
                              uint32_t& k) {
+  pg = uni_ptr(pg);
+  s = uni(s);
+  b = uni(b);
+  iw = uni(iw);
   __builtin_amdgcn_s_waitcnt(0);                        // this wave's stores done
   io_sync(bar, k, lane);
   if (iw == 0 && lane == 0)
@@ -147,29 +165,15 @@ __device__ __noinline__ void arrive_stage(ProgPtr pg, int s, int b, int iw, int 
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Marks a wave-uniform value as such (the compiler cannot always prove it,
-// and a value it thinks divergent turns buffer resources into per-lane loops).
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
 // Workgroup b's units of a stage: [lo, hi).
+// The f-th workgroup from the stage's rotation takes uq units, one more
+// while f < ur (uq, ur = units / G, units % G from the host: no division).
 __device__ __forceinline__ void unit_range(StagePtr sd, int b, int G, int& lo, int& hi) {
-  int f = (b - sd->rot) % G;
+  int f = b - sd->rot;
   if (f < 0) f += G;
-  lo = uni((int)(((int64_t)f * sd->units) / G));
-  hi = uni((int)(((int64_t)(f + 1) * sd->units) / G));
-}
-
-// Segment (K part, activation group) of unit v, as one comparable number.
-__device__ __forceinline__ int segment_of(StagePtr sd, int v) {
-  const int p = v / sd->tiles, t = v - p * sd->tiles;
-  return uni(p * (sd->tiles / sd->group_tiles) + t / sd->group_tiles);
-}
-
-// Steps of unit v that stream wave w takes: w, w + 12, ... below the part's length.
-__device__ __forceinline__ int wave_steps(StagePtr sd, int v, int w) {
-  const int p = v / sd->tiles;
-  const int len = min(sd->Sp, sd->S - p * sd->Sp);
-  return uni(w < len ? (len - w + kStream - 1) / kStream : 0);
+  const int uq = sd->uq, ur = sd->ur;
+  lo = uni(f * uq + min(f, ur));
+  hi = uni(lo + uq + (f < ur ? 1 : 0));
 }
 
 struct Lds {
@@ -265,31 +269,24 @@ struct Slot {
   uint32_t sc;
 };
 
-// Issue the loads of the load walk's current step into ring slot q (a
-// uniform index: a short chain of scalar branches picks the registers),
-// then advance the walk.  The loads are ordinary buffer loads: the compiler
-// waits for a slot before its registers are read (conservatively, as the
-// slot index is a run-time value), which keeps every register read after
-// its data has landed.
-template <int R>
+// Issue the loads of the load walk's current step into a ring slot, then
+// advance the walk.  Past the end of the walk the same three loads go to an
+// empty buffer (they read nothing and return zeros): every issue is then
+// exactly three loads, so the wait before a slot is read is a constant count
+// of loads issued after it, which the compiler derives by itself because the
+// ring slots are compile-time indices.
 __device__ __forceinline__ void issue(ProgPtr pg, int b, int G, int w, int lane, Walk& c,
-                                      bool& live, Slot (&ring)[R], int q) {
-  if (!live) return;
+                                      bool& live, Slot& slot) {
   const int step = c.step0 + kStream * c.j;
   const uint32_t chunk = (uint32_t)(c.t * c.S + step);   // 2 KiB step index in the stage
-  const uint32_t range = (uint32_t)(c.tiles * c.S);
-  const auto rw = make_rsrc(c.wq, range * 2048);
-  const auto rs = make_rsrc(c.ws, range * 64);
-  const uint32_t off = chunk * 2048 + lane * 16, soff = chunk * 64 + lane;
-#pragma unroll
-  for (int k = 0; k < R; ++k) {
-    if (q == k) {
-      ring[k].lo = buf_ld16_nt(rw, off);
-      ring[k].hi = buf_ld16_nt(rw, off + 1024);
-      ring[k].sc = buf_ld8(rs, soff);
-    }
-  }
-  live = walk_step(pg, b, G, w, c);
+  const uint32_t range = live ? (uint32_t)(c.tiles * c.S) : 0u;
+  const auto rw = make_rsrc(live ? c.wq : nullptr, range * 2048);
+  const auto rs = make_rsrc(live ? c.ws : nullptr, range * 64);
+  const uint32_t off = live ? chunk * 2048 + lane * 16 : kOutOfRange;
+  slot.lo = buf_ld16_nt(rw, off);
+  slot.hi = buf_ld16_nt(rw, live ? off + 1024 : kOutOfRange);
+  slot.sc = buf_ld8(rs, live ? chunk * 64 + lane : kOutOfRange);
+  if (live) live = walk_step(pg, b, G, w, c);
 }
 
 template <int MB>
@@ -314,18 +311,13 @@ __device__ __forceinline__ void begin_unit(const Walk& u, int& seg_s, int& seg_p
   }
 }
 
-// Whether the workgroup's first unit reads activations that need no wait:
-// then its staging loads are issued ahead of the weight ring (barrier Z).
-__device__ __forceinline__ bool first_is_free(ProgPtr pg, int b, int G, int& s0) {
+// Whether the workgroup has any unit in the program.
+__device__ __forceinline__ bool has_units(ProgPtr pg, int b, int G) {
   for (int s = 0; s < pg->nstages; ++s) {
     int lo, hi;
     unit_range(&pg->st[s], b, G, lo, hi);
-    if (lo < hi) {
-      s0 = s;
-      return pg->st[s].dep < 0;
-    }
+    if (lo < hi) return true;
   }
-  s0 = -1;
   return false;
 }
 
@@ -333,10 +325,10 @@ template <int MB, int R>
 __device__ __forceinline__ void stream_loop(ProgPtr pg, int b, int G, int w, int lane,
                                             const Lds& L) {
   const int g = lane >> 4, r = lane & 15;
-  int s0;
-  const bool z = first_is_free(pg, b, G, s0);
-  if (s0 < 0) return;                                   // no units
-  if (z) lds_barrier();                                 // Z: the first staging loads are out
+  if (!has_units(pg, b, G)) return;
+  // The weight stream starts at once.  (Holding it until the first
+  // activation loads are out measured slower: the io waves take longer to
+  // reach them than the stream they would be ahead of.)
 
   // Prime the ring with this wave's first R steps.
   Walk lc;
@@ -345,7 +337,7 @@ __device__ __forceinline__ void stream_loop(ProgPtr pg, int b, int G, int w, int
   while (live && lc.j >= lc.n) live = walk_unit(pg, b, G, w, lc);
   Slot ring[R];
 #pragma unroll
-  for (int i = 0; i < R; ++i) issue<R>(pg, b, G, w, lane, lc, live, ring, i);
+  for (int i = 0; i < R; ++i) issue(pg, b, G, w, lane, lc, live, ring[i]);
 
   Walk u;
   u.s = -1;
@@ -355,45 +347,39 @@ __device__ __forceinline__ void stream_loop(ProgPtr pg, int b, int G, int w, int
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = v4f{0.f, 0.f, 0.f, 0.f};
   begin_unit(u, seg_s, seg_p, seg_g);
-  int q = 0;                                            // ring slot of the next step
-  while (true) {
-    // Units with no step left for this wave still take part in their barriers.
-    bool done = false;
-    while (u.j >= u.n) {
-      end_unit<MB>(ord, acc, w, lane, L);
-      if (!walk_unit(pg, b, G, w, u)) {
-        done = true;
-        break;
-      }
-      begin_unit(u, seg_s, seg_p, seg_g);
-    }
-    if (done) break;
-    const int ldA = u.Sp * 128 + 16, ldS = u.Sp * 4 + 4;
-    const int sl = w + kStream * u.j;                   // step within the segment
-    v4i blo[MB], bhi[MB];
-    int bsc[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      // Rows past M read row M-1 (no branch): their output columns are
-      // computed but never stored.
-      const int m = min(16 * mb + r, u.M - 1);
-      const uint8_t* a = L.act + m * ldA + sl * 128 + 16 * g;
-      blo[mb] = *reinterpret_cast<const v4i*>(a);
-      bhi[mb] = *reinterpret_cast<const v4i*>(a + 64);
-      bsc[mb] = L.scl[m * ldS + 4 * sl + g];
-    }
+  // The k-th step overall reads ring slot k mod R: the loop runs R steps per
+  // pass with the slot fixed at compile time in each.
+  bool done = false;
+  while (!done) {
 #pragma unroll
     for (int k = 0; k < R; ++k) {
-      if (q == k) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          acc[mb] = mfma_mx16(cat8(ring[k].lo, ring[k].hi), cat8(blo[mb], bhi[mb]), acc[mb],
-                              (int)ring[k].sc, bsc[mb]);
+      // Units with no step left for this wave still take part in their barriers.
+      while (u.j >= u.n) {
+        end_unit<MB>(ord, acc, w, lane, L);
+        if (!walk_unit(pg, b, G, w, u)) {
+          done = true;
+          break;
+        }
+        begin_unit(u, seg_s, seg_p, seg_g);
       }
+      if (done) break;
+      const int ldA = u.Sp * 128 + 16, ldS = u.Sp * 4 + 4;
+      const int sl = w + kStream * u.j;                 // step within the segment
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        // Rows past M read row M-1 (no branch): their output columns are
+        // computed but never stored.
+        const int m = min(16 * mb + r, u.M - 1);
+        const uint8_t* a = L.act + m * ldA + sl * 128 + 16 * g;
+        const v4i blo = *reinterpret_cast<const v4i*>(a);
+        const v4i bhi = *reinterpret_cast<const v4i*>(a + 64);
+        const int bsc = L.scl[m * ldS + 4 * sl + g];
+        acc[mb] = mfma_mx16(cat8(ring[k].lo, ring[k].hi), cat8(blo, bhi), acc[mb],
+                            (int)ring[k].sc, bsc);
+      }
+      ++u.j;
+      issue(pg, b, G, w, lane, lc, live, ring[k]);
     }
-    ++u.j;
-    issue<R>(pg, b, G, w, lane, lc, live, ring, q);
-    q = q == R - 1 ? 0 : q + 1;
   }
 }
 
@@ -403,11 +389,18 @@ __device__ __forceinline__ void stream_loop(ProgPtr pg, int b, int G, int w, int
 struct Segment {
   int p, g, k0, ns;   // part, group, first step, steps
 };
-__device__ __forceinline__ Segment segment_geom(StagePtr sd, int v) {
+__device__ __forceinline__ Segment uni_seg(Segment sg) {
+  sg.p = uni(sg.p);
+  sg.g = uni(sg.g);
+  sg.k0 = uni(sg.k0);
+  sg.ns = uni(sg.ns);
+  return sg;
+}
+__device__ __forceinline__ Segment segment_geom(StagePtr sd, int p, int g) {
   Segment sg;
-  sg.p = v / sd->tiles;
-  sg.g = (v - sg.p * sd->tiles) / sd->group_tiles;
-  sg.k0 = sg.p * sd->Sp;
+  sg.p = p;
+  sg.g = g;
+  sg.k0 = p * sd->Sp;
   sg.ns = min(sd->Sp, sd->S - sg.k0);
   return sg;
 }
@@ -415,11 +408,10 @@ __device__ __forceinline__ Segment segment_geom(StagePtr sd, int v) {
 // MXFP8 activations of a segment into LDS: each round every io lane has
 // kBatch 16-byte code chunks and one scale dword in flight before it stores
 // any (a round covers kBatch * 256 chunks, and the scale dwords of a row are
-// an eighth of its chunks).  z: this is the workgroup's first segment and
-// the stream waves wait at barrier Z until the first round's loads are out,
-// so that they are not queued behind the weight ring.
-__device__ __noinline__ void stage_mx(StagePtr sd, Segment sg, int lt, bool z,
-                                         Lds L) {
+// an eighth of its chunks).
+__device__ __noinline__ void stage_mx(StagePtr sd, Segment sg, int lt, Lds L) {
+  sd = uni_ptr(sd);
+  sg = uni_seg(sg);
   const int ldA = sd->Sp * 128 + 16, ldS = sd->Sp * 4 + 4;
   const int64_t gq = (int64_t)sg.g * sd->a_group;
   const int lda = (int)sd->lda, ldas = lda >> 5;
@@ -442,7 +434,6 @@ __device__ __noinline__ void stage_mx(StagePtr sd, Segment sg, int lt, bool z,
     const int srow = cs / sg.ns, cd = cs - srow * sg.ns;
     const uint32_t soff = cs < nsc ? (uint32_t)(srow * ldas + (sg.k0 + cd) * 4) : kOutOfRange;
     const uint32_t sv = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)soff, 0, 0);
-    if (z && rnd == 0) lds_barrier();                   // Z
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int c = c0 + i * kIoThreads + lt;
@@ -460,10 +451,11 @@ __device__ __noinline__ void stage_mx(StagePtr sd, Segment sg, int lt, bool z,
 // rotary dims turn by the row's angles (staged in L.cs) before rounding to
 // BF16.  8-element chunks; the 4 lanes of a quad hold one 32-block (the
 // chunk count per row is a multiple of 16, so quads never straddle rows).
-// z: as for stage_mx.
 template <bool ROPE>
-__device__ __noinline__ void stage_bf16(StagePtr sd, Segment sg, bool writer, int lt,
-                                           bool z, Lds L) {
+__device__ __noinline__ void stage_bf16(StagePtr sd, Segment sg, bool writer, int lt, Lds L) {
+  sd = uni_ptr(sd);
+  sg = uni_seg(sg);
+  writer = uni(writer);
   const int ldA = sd->Sp * 128 + 16, ldS = sd->Sp * 4 + 4;
   const int cpr = sg.ns * 16;                           // 8-element chunks per row
   const int nck = sd->M * cpr;
@@ -473,7 +465,7 @@ __device__ __noinline__ void stage_bf16(StagePtr sd, Segment sg, bool writer, in
   const int64_t span = ROPE ? (int64_t)(sd->M - 1) * sd->ld_x + (int64_t)(sg.g + 1) * hpg * sd->ld_head
                             : (int64_t)(sd->M - 1) * sd->ld_x + sd->K;
   const auto rx = make_rsrc(xb, (uint32_t)(span * 2));
-  for (int c0 = 0, rnd = 0; c0 < nck; c0 += kBatch * kIoThreads, ++rnd) {
+  for (int c0 = 0; c0 < nck; c0 += kBatch * kIoThreads) {
     v4i v[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
@@ -492,7 +484,6 @@ __device__ __noinline__ void stage_bf16(StagePtr sd, Segment sg, bool writer, in
       // device-coherent), or attention heads from outside it.
       v[i] = ROPE ? buf_ld16(rx, off) : ld16_c(rx, off);
     }
-    if (z && rnd == 0) lds_barrier();                   // Z
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int c = c0 + i * kIoThreads + lt;
@@ -539,6 +530,9 @@ __device__ __noinline__ void stage_bf16(StagePtr sd, Segment sg, bool writer, in
 // outside the table reads row 0 and sets bit 1 of the error word.
 __device__ __noinline__ void stage_angles(ProgPtr pg, StagePtr sd, int iw, int lane,
                              Lds L, uint32_t* bar, uint32_t& k) {
+  pg = uni_ptr(pg);
+  sd = uni_ptr(sd);
+  iw = uni(iw);
   const int rope = sd->D - sd->nope;
   const int lt = iw * 64 + lane;
   const int per = rope / 4;                             // 16-byte chunks per row
@@ -572,14 +566,19 @@ __device__ __forceinline__ void store_out(StagePtr sd, int m, int n, v4f v) {
 // After the unit's barrier: sum its 12 partial tiles (io wave iw < MB owns
 // activation tile iw), then the BF16 output or the K-split protocol.
 template <int MB>
-__device__ __noinline__ void finish_unit(StagePtr sd, int v, int ord, int iw, int lane, Lds L) {
+__device__ __noinline__ void finish_unit(StagePtr sd, int p, int t, int ord, int iw, int lane,
+                                         Lds L) {
+  sd = uni_ptr(sd);
+  p = uni(p);
+  t = uni(t);
+  ord = uni(ord);
+  iw = uni(iw);
   if (iw >= MB) return;
   const v4f* red = L.red + (size_t)(ord & 1) * kStream * MB * 64;
   const int mb = iw;
   v4f sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int w = 0; w < kStream; ++w) sum += red[(w * MB + mb) * 64 + lane];
-  const int p = v / sd->tiles, t = v - p * sd->tiles;
   const int m = 16 * mb + (lane & 15);
   const int n = 16 * t + 4 * (lane >> 4);
   if (sd->P == 1) {
@@ -614,41 +613,53 @@ template <int MB>
 __device__ __forceinline__ void io_loop(ProgPtr pg, int b, int G, int iw, int lane, const Lds& L) {
   uint32_t k = 0;                                       // io_sync uses so far
   const int lt = iw * 64 + lane;
-  int seg_s = -1, seg = -1, ord = 0;
-  int s0;
-  bool zfirst = first_is_free(pg, b, G, s0);
+  int seg_s = -1, seg_p = -1, seg_g = -1, ord = 0;
   for (int s = 0; s < pg->nstages; ++s) {
     StagePtr sd = &pg->st[s];
     int lo, hi;
     unit_range(sd, b, G, lo, hi);
     if (lo >= hi) continue;
     bool ready = false;                                 // dependency met, angles staged
+    // Unit v = p * tiles + t; its activation group g = t / group_tiles
+    // (gt: t's index within the group), advanced without dividing per unit.
+    const int tiles = sd->tiles, group_tiles = sd->group_tiles;
+    int p = uni(lo / tiles), t = lo - p * tiles;
+    int g = uni(t / group_tiles), gt = t - g * group_tiles;
     for (int v = lo; v < hi; ++v) {
-      const int sv = segment_of(sd, v);
-      if (s != seg_s || sv != seg) {
+      if (s != seg_s || p != seg_p || g != seg_g) {
         if (!ready) {
           if (sd->dep >= 0) wait_stage(pg, sd->dep, iw, lane, L.bar, k);
           if (sd->act == kActRope) stage_angles(pg, sd, iw, lane, L, L.bar, k);
           ready = true;
         }
-        const Segment sg = segment_geom(sd, v);
-        const int first = sg.p * sd->tiles + sg.g * sd->group_tiles;   // segment's first unit
+        const Segment sg = segment_geom(sd, p, g);
+        const int first = p * tiles + g * group_tiles;  // segment's first unit
         const bool writer = sd->q != nullptr && first >= lo;
-        const bool z = zfirst;                          // barrier Z inside this staging
-        zfirst = false;
         if (sd->act == kActMx)
-          stage_mx(sd, sg, lt, z, L);
+          stage_mx(sd, sg, lt, L);
         else if (sd->act == kActBf16)
-          stage_bf16<false>(sd, sg, writer, lt, z, L);
+          stage_bf16<false>(sd, sg, writer, lt, L);
         else
-          stage_bf16<true>(sd, sg, writer, lt, z, L);
+          stage_bf16<true>(sd, sg, writer, lt, L);
         lds_barrier();                                  // Y: segment staged
         seg_s = s;
-        seg = sv;
+        seg_p = p;
+        seg_g = g;
       }
       lds_barrier();                                    // X: partials of unit v in LDS
-      finish_unit<MB>(sd, v, ord, iw, lane, L);
+      finish_unit<MB>(sd, p, t, ord, iw, lane, L);
       ++ord;
+      ++t;
+      if (++gt == group_tiles) {
+        gt = 0;
+        ++g;
+      }
+      if (t == tiles) {
+        t = 0;
+        g = 0;
+        gt = 0;
+        ++p;
+      }
     }
     if (sd->consumed) arrive_stage(pg, s, b, iw, lane, L.bar, k);
   }
@@ -677,10 +688,12 @@ __device__ __forceinline__ void io_loop(ProgPtr pg, int b, int G, int iw, int la
     __hip_atomic_store(ctr_word(pg, kExitTop), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Ring depth (weight steps in flight per stream wave) for MB activation tiles.
+// Ring depth (weight steps in flight per stream wave): 4 steps, 96 KiB per
+// CU over the 12 stream waves.  Deeper rings measured slower: activation
+// loads issued by the io waves queue behind every weight byte in flight.
 template <int MB>
 constexpr int ring_depth() {
-  return MB == 1 ? 8 : (MB == 2 ? 6 : 4);
+  return 4;
 }
 
 template <int MB>
@@ -700,6 +713,17 @@ __global__ __launch_bounds__(kStageThreads) void stage_kernel(Program) {
   L.red = reinterpret_cast<v4f*>(L.scl + (((size_t)M * pg->scl_ld + 15) & ~(size_t)15));
   L.cs = reinterpret_cast<float*>(L.red + (size_t)2 * kStream * MB * 64);
   L.bar = &io_bar;
+  // Touch every 64-byte line of the program at once: the walks below read
+  // it through chains of dependent scalar loads, which then hit the scalar
+  // cache instead of each waiting for memory.
+  {
+    typedef const __attribute__((address_space(4))) uint32_t* KWord;
+    const KWord raw = (KWord)pg;
+    uint32_t sink = 0;
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(Program) / 4); i += 16) sink ^= raw[i];
+    asm volatile("" ::"s"(sink));
+  }
   if (threadIdx.x == 0) io_bar = 0;
   __syncthreads();
   if (wave < kStream)
