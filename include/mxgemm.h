@@ -169,10 +169,15 @@ typedef struct {
  *   B:  out_b = b . wB^T
  *   C:  out_c = c . wC^T                       (c: MXFP8 [M, wC.K])
  * Each stage reads its activations only once the previous stage has finished
- * (C included), but every stage's weight stream starts as early as the
- * hardware allows: weights never depend on the previous stage ([mxfp8] page:
- * the low-latency kernel loads its weights before its grid dependency wait
- * so the weight read overlaps the previous kernel).
+ * (C included).  Weights never depend on the previous stage, and the pages
+ * overlap the next weight read with the previous kernel ([mxfp8] page: the
+ * low-latency kernel loads its weights before its grid dependency wait).
+ * The default runs the three stages as three launches in stream order (each
+ * stage's weight read starts when the previous launch ends); a persistent
+ * one-launch form, whose stages stream their weights ahead of the
+ * dependency wait, is selected with MXG_CHAIN_PATH=stage in the
+ * environment.  Both give the same results to the tolerance of
+ * mxfp8_gemm; the three launches are the faster on MI355X.
  *
  * Shapes: 1 <= M <= 48; each weight N % 16 == 0, K % 128 == 0; wB.K <= wA.N,
  * wB.K % 128 == 0.  out_a/out_b/out_c are BF16 [M, N] row-major, b_q/b_s

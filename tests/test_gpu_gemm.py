@@ -85,6 +85,13 @@ def test_shapes(N, K, fused, path):
         run_case(M, N, K, seed=N + K, fused=fused)
 
 
+@pytest.mark.parametrize("M", [1, 16, 17, 48])
+@pytest.mark.parametrize("fused", [False, True])
+def test_largest_contraction(M, fused, path):
+    # K = MXG_MAX_K: the longest activation rows (LDS chunking, K split)
+    run_case(M, 512, 16384, seed=M, fused=fused)
+
+
 def test_single_gemm_config(path):
     # M=4, N=1024, K=2048, x ~ N(0,1), W ~ N(0,0.02), seed 0
     run_case(4, 1024, 2048, seed=0)
@@ -205,12 +212,15 @@ def test_pack_is_the_documented_permutation(N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(8, 4096, 5120), (4, 5120, 8192), (33, 2048, 5120)])
-def test_workspace_left_clean(M, N, K, monkeypatch):
-    """Repeated stage-kernel calls (distributed quantize, K-split tiles) on one
-    workspace keep working: every counter is reset by the call that used it
-    (a stale tile counter would make the next call's wait expire and set the
-    error word), and the results stay bitwise identical."""
-    monkeypatch.setenv("MXG_GEMM_PATH", "stage")
+@pytest.mark.parametrize("kind", ["stage", "direct"])
+def test_workspace_left_clean(M, N, K, kind, monkeypatch):
+    """Repeated calls (stage kernel: distributed quantize, K-split tiles;
+    direct kernels: K-split tiles) on one workspace keep
+    working: every counter is reset by the call that used it (a stale tile
+    counter would make the next call's wait expire and set the error word),
+    and the results stay bitwise identical."""
+    monkeypatch.setenv("MXG_GEMM_PATH", kind)
+    monkeypatch.delenv("MXG_DIRECT_KERNEL", raising=False)
     w, _ = _weights(N, K, 0)
     ws = torch.zeros(int(mx.lib().mxg_gemm_workspace_bytes(M, N, K)) + 4096, dtype=torch.uint8,
                      device="cuda")
@@ -227,3 +237,4 @@ def test_workspace_left_clean(M, N, K, monkeypatch):
     torch.cuda.synchronize()
     assert mx.workspace_error(ws) == 0
     assert not ws[:65536].any(), "counters must be back to zero"
+
