@@ -122,7 +122,8 @@ int mxfp8_pack_weights(const uint8_t *w_q, const uint8_t *w_s, int64_t N, int64_
  *             that the kernel quantizes itself (as mxfp8_quantize does) and
  *             whose codes/scales it also WRITES to a_q/a_s (the pages'
  *             wide_mm quantizes a BF16 x before its GEMM; here both run in
- *             one launch).
+ *             one launch when M*K <= 65536, else a quantize launch runs
+ *             first on the same stream).
  *   ld_x      row stride of x_bf16 in elements (ignored when x_bf16 is NULL)
  *   a_q, a_s  MXFP8 activations [M, K] / [M, K/32]
  *   w_q, w_s  MXFP8 weight [N, K] / [N, K/32], packed by mxfp8_pack_weights

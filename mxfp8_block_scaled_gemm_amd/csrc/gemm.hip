@@ -47,26 +47,33 @@ __device__ __forceinline__ int xcd_tile(int b, int tiles) {
   return 4 * (xcd + 8 * (k >> 2)) + (k & 3);
 }
 
-// Quantize one 8-element BF16 chunk (16 bytes) whose block of 32 is spread
-// over the 4 lanes tid & ~3 .. (tid & ~3) + 3; returns the 8 codes and the
-// block's exponent.  All 64 lanes must call it (it shuffles).
-__device__ __forceinline__ uint2 quant_chunk8(v4i v, int& e) {
-  uint32_t a = halves_max(bf16x2_absmax2(bf16x2_absmax2((uint32_t)v[0], (uint32_t)v[1]),
-                                         bf16x2_absmax2((uint32_t)v[2], (uint32_t)v[3])));
-  a = quad_max(a);
-  e = block_exponent(a);
+// Quantize one whole 32-element BF16 block held by this lane (4 x 16 bytes)
+// to its 32 E4M3 codes (2 x 16 bytes) and its exponent.  One lane per block
+// keeps the per-block work (amax, exponent, scale) to one copy, where lanes
+// sharing a block would each repeat it.
+__device__ __forceinline__ void quant_block32(const v4i* v, v4i& c0, v4i& c1, int& e) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    m = bf16x2_absmax2(m, bf16x2_absmax2(bf16x2_absmax2((uint32_t)v[k][0], (uint32_t)v[k][1]),
+                                         bf16x2_absmax2((uint32_t)v[k][2], (uint32_t)v[k][3])));
+  e = block_exponent(halves_max(m));
   const BlockScale bs = block_scale(e);
-  uint2 c;
-  c.x = enc4_e4m3((uint32_t)v[0], (uint32_t)v[1], bs);
-  c.y = enc4_e4m3((uint32_t)v[2], (uint32_t)v[3], bs);
-  return c;
+  uint32_t c[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    c[2 * k] = enc4_e4m3((uint32_t)v[k][0], (uint32_t)v[k][1], bs);
+    c[2 * k + 1] = enc4_e4m3((uint32_t)v[k][2], (uint32_t)v[k][3], bs);
+  }
+  c0 = v4i{(int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+  c1 = v4i{(int)c[4], (int)c[5], (int)c[6], (int)c[7]};
 }
 
 // ----------------------------------------------------------- M <= 16 rows
 //
 // W waves split K; SPW: weight steps a wave holds in registers (>= its step
-// count); CH: 16-byte activation chunks each thread stages (>= M*K/16/(64W)
-// for MXFP8 input, M*K/8/(64W) for BF16 input).
+// count); CH: what each thread stages: 16-byte code chunks (>= M*K/16/(64W))
+// for MXFP8 input, whole 32-element blocks (>= M*K/32/(64W)) for BF16 input.
 template <int W, int SPW, int CH, bool FQ>
 __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
   constexpr int kThreads = W * 64;
@@ -82,9 +89,9 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
 
   // 1. Activation staging loads (L2-resident, small): issued first so that
   //    waiting for them does not wait for the weight stream.
-  v4i st[CH];
+  v4i st[FQ ? 4 * CH : CH];
   uint32_t sc[FQ ? 1 : 2];
-  const int nck = FQ ? (M * K) >> 3 : (M * K) >> 4;        // 16-byte chunks
+  const int nck = FQ ? (M * K) >> 5 : (M * K) >> 4;        // 32-blocks, or 16-byte chunks
   auto chunk = [&](int i) {                                // chunk id, or -1
     const int c = tid + i * kThreads;
     return c < nck ? c : -1;
@@ -113,12 +120,14 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
     }
   } else {
     const auto rx = make_rsrc(p.x, (uint32_t)(((M - 1) * p.ld_x + K) * 2));
-    const int cpr = K >> 3;                                // 8-element chunks per row
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int c = chunk(i);
-      const int row = c / cpr, col = (c - row * cpr) * 8;
-      st[i] = buf_ld16(rx, c >= 0 ? (uint32_t)(row * p.ld_x + col) * 2u : kOutOfRange);
+      const int c = chunk(i);                              // block: row c / KB, 32 columns
+      const int row = c / KB, col = (c - row * KB) * 32;
+      const uint32_t off = (uint32_t)(row * p.ld_x + col) * 2u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        st[4 * i + k] = buf_ld16(rx, c >= 0 ? off + 16 * k : kOutOfRange);
     }
   }
 
@@ -165,20 +174,22 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
       }
     }
   } else {
-    const int cpr = K >> 3;
     const bool writer = blockIdx.x == 0;   // one workgroup writes the codes out
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = chunk(i);
-      int e;
-      const uint2 codes = quant_chunk8(st[i], e);
       if (c >= 0) {
-        const int row = c / cpr, col = (c - row * cpr) * 8;
-        *reinterpret_cast<uint2*>(s_act + row * ldA + col) = codes;
-        if ((c & 3) == 0) s_scl[row * ldS + (col >> 5)] = (uint8_t)(e + 127);
+        v4i c0, c1;
+        int e;
+        quant_block32(&st[4 * i], c0, c1, e);
+        const int row = c / KB, cb = c - row * KB, col = cb * 32;
+        *reinterpret_cast<v4i*>(s_act + row * ldA + col) = c0;
+        *reinterpret_cast<v4i*>(s_act + row * ldA + col + 16) = c1;
+        s_scl[row * ldS + cb] = (uint8_t)(e + 127);
         if (writer) {
-          *reinterpret_cast<uint2*>(p.a_q + (int64_t)row * K + col) = codes;
-          if ((c & 3) == 0) p.a_s[(int64_t)row * KB + (col >> 5)] = (uint8_t)(e + 127);
+          *reinterpret_cast<v4i*>(p.a_q + (int64_t)row * K + col) = c0;
+          *reinterpret_cast<v4i*>(p.a_q + (int64_t)row * K + col + 16) = c1;
+          p.a_s[(int64_t)row * KB + cb] = (uint8_t)(e + 127);
         }
       }
     }
@@ -480,8 +491,8 @@ static hipError_t launch_m16(const GemmArgs& a, hipStream_t stream) {
 template <int SPW, bool FQ>
 static hipError_t launch_m16_ch(const GemmArgs& a, int ch, hipStream_t stream) {
   if constexpr (FQ) {
-    if (ch <= 2) return launch_m16<SPW, 2, FQ>(a, stream);
-    return launch_m16<SPW, 4, FQ>(a, stream);
+    if (ch <= 1) return launch_m16<SPW, 1, FQ>(a, stream);
+    return launch_m16<SPW, 2, FQ>(a, stream);
   } else {
     if (ch <= 2) return launch_m16<SPW, 2, FQ>(a, stream);
     if (ch <= 4) return launch_m16<SPW, 4, FQ>(a, stream);
@@ -662,23 +673,28 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
   if (fq && (a.group_tiles != 0 || a.lda != a.K)) return hipErrorInvalidValue;
   const int S = a.K / 128;
   const int steps = (S + kM16Waves - 1) / kM16Waves;       // weight steps per wave
-  const int per = fq ? a.M * a.K / 8 : a.M * a.K / 16;     // 16-byte staging chunks
+  const int per = fq ? a.M * a.K / 32 : a.M * a.K / 16;    // 32-blocks, or 16-byte chunks
   const int ch = (per + kM16Waves * 64 - 1) / (kM16Waves * 64);
   const Plan pl = choose_plan(a.M, a.N, a.K, a.group_tiles, device_cus());
   // One full-K tile per workgroup with the whole activation in LDS unless
   // the model gives a 2D plan at most 3/4 of its time: the M <= 16 kernel
   // keeps more loads in flight per CU (two workgroups share a CU when their
-  // LDS fits) and has less fixed cost, which the model leaves out.
+  // LDS fits) and has less fixed cost, which the model leaves out.  (With
+  // BF16 input either choice pays about as much for the quantize: in-kernel
+  // in the M <= 16 kernel, a launch before the 2D kernel.)
   const bool m16_fast = pl.cost >= 0.75 * plan_cost(a.M, a.N, a.K, 1, 1, device_cus());
+  // In-kernel quantize up to two 32-blocks per thread (M*K <= 65536):
+  // measured faster than a quantize launch up to there, slower beyond.
+  const bool fq_inline = fq && ch <= 2;
   const int force = forced_kernel();                       // tests: 1 = M <= 16 kernel, 2 = 2D
   const bool m16_ok = gemm_m16_fits(a.M, a.K) && steps <= 4;
   if (m16_ok && (force == 1 || (force == 0 && m16_fast))) {
     if (!fq && ch <= 16) return launch_m16_spw<false>(a, steps, ch, stream);
     // In-kernel quantize while the weight stream is in flight when the
-    // activation is small (every workgroup quantizes all of it, which costs
-    // more than a separate launch from about 8 rows of 5120); larger
-    // activations are quantized by their own launch first.
-    if (fq && ch <= 4) return launch_m16_spw<true>(a, steps, ch, stream);
+    // activation is small enough (every workgroup quantizes all of it, one
+    // 32-block per lane at a time); larger activations are quantized by
+    // their own launch first.
+    if (fq_inline) return launch_m16_spw<true>(a, steps, ch, stream);
     if (fq) {
       hipError_t e = launch_quantize(a.x, a.M, a.K, a.ld_x, a.a_q, a.a_s, stream);
       if (e != hipSuccess) return e;
