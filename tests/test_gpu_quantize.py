@@ -89,3 +89,38 @@ def test_rejected_call_writes_nothing():
     torch.cuda.synchronize()
     assert st == 3
     assert (q == 0xAB).all() and (s == 0xCD).all()
+
+
+@pytest.mark.parametrize("shift", [0, 3, 9])
+def test_exhaustive_bf16_values_fused_in_gemm(shift, monkeypatch):
+    """The quantize fused into the M <= 16 GEMM kernel (one 32-block per
+    lane) on the same blocks as above: every finite BF16 value, the codes
+    and scales it writes out must equal the oracle's."""
+    monkeypatch.setenv("MXG_GEMM_PATH", "direct")
+    monkeypatch.setenv("MXG_DIRECT_KERNEL", "m16")
+    say(f"fused quantize exhaustive shift={shift}")
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = oracle.bf16_value(b)
+    comp = np.abs(v) * 2.0 ** shift
+    keep = np.isfinite(v) & np.isfinite(comp) & (comp < 3.0e38)
+    x = np.zeros((keep.sum(), 32), dtype=np.uint16)
+    x[:, 3] = b[keep]
+    x[:, 20] = oracle.bf16_round(comp[keep])
+    M, K = 8, 8192                                  # 2048 blocks per call: quantized in-kernel
+    per = M * K // 32
+    x = np.concatenate([x, np.zeros((-len(x) % per, 32), np.uint16)])
+    oq, os_ = oracle.quantize(x)
+    w = mx.PackedWeight.from_rows(torch.zeros(16, K, dtype=torch.uint8, device="cuda"),
+                                  torch.full((16, K // 32), 127, dtype=torch.uint8, device="cuda"))
+    gq = np.empty_like(oq)
+    gs = np.empty_like(os_)
+    for i in range(0, len(x), per):
+        xb = dev_bf16(x[i:i + per].reshape(M, K))
+        a_q = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+        a_s = torch.empty(M, K // 32, dtype=torch.uint8, device="cuda")
+        mx.mxfp8_gemm(a_q, a_s, w, x=xb)
+        torch.cuda.synchronize()
+        gq[i:i + per] = host_u8(a_q).reshape(per, 32)
+        gs[i:i + per] = host_u8(a_s).reshape(per, 1)
+    assert np.array_equal(gs, os_)
+    assert np.array_equal(gq, oq)
