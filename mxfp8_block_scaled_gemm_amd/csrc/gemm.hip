@@ -10,19 +10,22 @@
 //   * weights arrive pre-packed in tile order (pack.hip), so each wave reads
 //     its A operand as fully contiguous 1 KiB loads and its scales as one
 //     64-byte load per step;
-//   * a workgroup owns one 16-row weight tile and the whole K; its 16 waves
-//     split K (wave w takes 128-wide steps w, w+16, ...) and each wave issues
-//     every weight load it will need up front, predicated by buffer range
-//     checks rather than branches, so nothing waits on anything until the
-//     stream is in flight;
+//   * M <= 16 kernel: a workgroup owns one 16-row weight tile and the whole
+//     K; its 16 waves split K (wave w takes 128-wide steps w, w+16, ...) and
+//     each wave issues every weight load it will need up front, predicated
+//     by buffer range checks rather than branches, so nothing waits on
+//     anything until the stream is in flight;
 //   * the activations (at most M*K bytes, read by every workgroup) are
 //     staged per workgroup: loaded with coalesced 16-byte accesses before
 //     the weight loads are issued, quantized in registers when they come as
-//     BF16, and parked in LDS, from where each wave reads its B operands;
-//     when M*K does not fit (rows above 16, or very long K) they go through
-//     LDS one 16-step K-chunk at a time;
+//     BF16 (one 32-element block per lane), and parked in LDS, from where
+//     each wave reads its B operands;
 //   * the 16 partial tiles are summed through LDS in wave order
-//     (deterministic), rounded to BF16 and stored.
+//     (deterministic), rounded to BF16 and stored;
+//   * 2D kernel (rows above 16, and shapes whose tile count fits the chip
+//     badly): a workgroup takes 1, 2 or 4 weight tiles over one K part, the
+//     activations go through LDS in 2048-wide K chunks, and K parts are
+//     summed across workgroups in part order by the last to arrive.
 #include <cstdlib>
 #include <cstring>
 
