@@ -311,7 +311,7 @@ def main():
                     help="only the dominant kernel's timing (for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); the "
+        print(f"bench.py: this library runs on one GPU only (asked for {args.gpus}); the "
               "multi-GPU sharding of the path is a design note, not a measured mode.",
               file=sys.stderr)
         sys.exit(2)
