@@ -238,3 +238,9 @@ def test_workspace_left_clean(M, N, K, kind, monkeypatch):
     assert mx.workspace_error(ws) == 0
     assert not ws[:65536].any(), "counters must be back to zero"
 
+
+
+@pytest.mark.parametrize("M", [1, 5, 17])
+def test_widest_output(M, path):
+    # 2048 weight tiles: several rounds of workgroups over the CUs
+    run_case(M, 32768, 1024, seed=M)
