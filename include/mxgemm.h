@@ -73,6 +73,22 @@ const char *mxg_strerror(int status);
 int mxg_version(void);
 
 /*
+ * mxg_hbm_read_probe -- a measurement aid, not a step of the method: reads
+ * `tiles` consecutive blocks of `tile_bytes` bytes from src (device memory),
+ * one workgroup per block, with the access pattern of the GEMMs' weight
+ * stream (16 waves, each issuing all of its 2 KiB steps at once), and
+ * computes nothing.  Timing it against mxfp8_gemm on the same bytes gives
+ * the single-launch streaming ceiling the GEMM is measured against.
+ *   src         16-byte aligned, at least tiles * tile_bytes bytes (read only)
+ *   tile_bytes  multiple of 16, at most 131072; 1 <= tiles <= 2^20
+ *   sink        a device word the kernel writes only for one improbable
+ *               folded value of the data (so no load can be optimized away)
+ * Status as above; nothing is launched on an error.
+ */
+int mxg_hbm_read_probe(const void *src, int64_t tiles, int64_t tile_bytes, uint32_t *sink,
+                       void *stream);
+
+/*
  * mxfp8_quantize -- BF16 -> MXFP8 ([mxfp8] pinned_mm and wide_mm quantize a
  * BF16 input with mxfp8_e4m3_quantize; [cute] AllReduceMHC's mxfp8_out
  * receives the layer input as MXFP8).
