@@ -97,7 +97,8 @@ def time_graph(fn, reps: int, stream) -> float:
 
 
 def decode_bucket(dev, steps: int, warmup: int, stream):
-    """The headline workload; returns the timing record."""
+    """The decode-bucket workload (M = 1, 2, 4, 8; N = 4096; K = 5120); returns
+    the timing record."""
     N, K, Ms = 4096, 5120, (1, 2, 4, 8)
     copies = weight_copies(N, K, dev)
     x8 = synth.gemm_case(8, N, K, seed=0)["x"].to(dev)

@@ -92,7 +92,7 @@ def test_largest_contraction(M, fused, path):
     run_case(M, 512, 16384, seed=M, fused=fused)
 
 
-def test_single_gemm_config(path):
+def test_m4_n1024_k2048(path):
     # M=4, N=1024, K=2048, x ~ N(0,1), W ~ N(0,0.02), seed 0
     run_case(4, 1024, 2048, seed=0)
     run_case(4, 1024, 2048, seed=0, fused=True)
