@@ -176,24 +176,22 @@ def roofline_kernel(dev, stream, reps: int = 200):
 
 
 def stream_ceiling(dev, stream, reps: int = 600):
-    """The single-launch streaming floor for the roofline kernel's weight
-    bytes: the library's read-only probe over the same 256 tiles x 84480
-    bytes (N=4096, K=5120 codes + scales), rotated over >= 512 MB of
-    buffers, one HIP graph of `reps` launches timed with HIP events."""
-    tiles, tile_bytes = 4096 // 16, (5120 // 128) * 2112
-    nbytes = tiles * tile_bytes
-    bufs = [torch.zeros(nbytes, dtype=torch.uint8, device=dev)
-            for _ in range(max(2, math.ceil(ROTATE_BYTES / nbytes)))]
+    """The single-launch streaming floor for the roofline kernel's weight:
+    the library's read-only probe reading the same rotated weight copies
+    (N=4096, K=5120) with the same load pattern, one HIP graph of `reps`
+    launches timed with HIP events on its launch stream."""
+    N, K = 4096, 5120
+    copies = weight_copies(N, K, dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def call(i):
-        mx.hbm_read_probe(bufs[i % len(bufs)], tiles, tile_bytes, sink)
+        mx.hbm_read_probe(copies[i % len(copies)], sink)
     with torch.cuda.stream(stream):
         for i in range(20):
             call(i)
     us = time_graph(call, reps, stream) * 1e3 / reps
-    del bufs
-    return {"us": us, "bytes": nbytes, "GBs": nbytes / (us * 1e-6) / 1e9}
+    b = mx_bytes(N, K)
+    return {"us": us, "bytes": b, "GBs": b / (us * 1e-6) / 1e9}
 
 
 def chain_case(dev, stream, M: int, reps: int = 200):
@@ -389,8 +387,8 @@ def main():
                      "avg_launch_us": round(roof["us"], 3),
                      "bytes_per_launch": int(roof["bytes"]),
                      "traffic": profiled_traffic()},
-        "stream_ceiling": {"kernel": "hbm_read_kernel: the same weight bytes, the same load "
-                                     "pattern, nothing else",
+        "stream_ceiling": {"kernel": "hbm_read_kernel: the same weight copies read with the "
+                                     "same load pattern, nothing else",
                            "us": round(ceil["us"], 3), "GBs": round(ceil["GBs"], 1),
                            "frac": round(ceil["GBs"] / HBM_PEAK_GBS, 4),
                            "roofline_vs_ceiling": round(roof["GBs"] / ceil["GBs"], 4)},

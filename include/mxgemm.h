@@ -73,20 +73,20 @@ const char *mxg_strerror(int status);
 int mxg_version(void);
 
 /*
- * mxg_hbm_read_probe -- a measurement aid, not a step of the method: reads
- * `tiles` consecutive blocks of `tile_bytes` bytes from src (device memory),
- * one workgroup per block, with the access pattern of the GEMMs' weight
- * stream (16 waves, each issuing all of its 2 KiB steps at once), and
- * computes nothing.  Timing it against mxfp8_gemm on the same bytes gives
- * the single-launch streaming ceiling the GEMM is measured against.
- *   src         16-byte aligned, at least tiles * tile_bytes bytes (read only)
- *   tile_bytes  multiple of 16, at most 131072; 1 <= tiles <= 2^20
+ * mxg_hbm_read_probe -- a measurement aid, not a step of the method: reads a
+ * weight packed by mxfp8_pack_weights (N rows, K columns) exactly as the
+ * GEMMs' weight stream reads it (one workgroup of 16 waves per 16-row tile,
+ * each wave issuing all of its 128-wide K steps at once) and computes
+ * nothing.  Timing it against mxfp8_gemm on the same weight gives the
+ * single-launch streaming ceiling the GEMM is measured against.
+ *   w_q, w_s    packed weight codes (N*K bytes) and scales (N*K/32 bytes)
+ *   N, K        N % 16 == 0, K % 128 == 0, K <= 8192
  *   sink        a device word the kernel writes only for one improbable
  *               folded value of the data (so no load can be optimized away)
  * Status as above; nothing is launched on an error.
  */
-int mxg_hbm_read_probe(const void *src, int64_t tiles, int64_t tile_bytes, uint32_t *sink,
-                       void *stream);
+int mxg_hbm_read_probe(const uint8_t *w_q, const uint8_t *w_s, int64_t N, int64_t K,
+                       uint32_t *sink, void *stream);
 
 /*
  * mxfp8_quantize -- BF16 -> MXFP8 ([mxfp8] pinned_mm and wide_mm quantize a

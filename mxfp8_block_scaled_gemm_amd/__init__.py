@@ -74,7 +74,7 @@ def lib() -> ctypes.CDLL:
         L.mxg_strerror.restype = ctypes.c_char_p
         L.mxg_version.argtypes = []
         L.mxg_version.restype = ctypes.c_int
-        L.mxg_hbm_read_probe.argtypes = [vp, i64, i64, vp, vp]
+        L.mxg_hbm_read_probe.argtypes = [vp, vp, i64, i64, vp, vp]
         L.mxg_hbm_read_probe.restype = ctypes.c_int
         L.mxfp8_quantize.argtypes = [vp, i64, i64, i64, vp, vp, vp]
         L.mxfp8_quantize.restype = ctypes.c_int
@@ -148,15 +148,12 @@ def workspace_error(ws: torch.Tensor) -> int:
     return int(ws[20:24].view(torch.int32).item())
 
 
-def hbm_read_probe(src: torch.Tensor, tiles: int, tile_bytes: int, sink: torch.Tensor,
-                   stream=None) -> None:
-    """Measurement aid: read tiles * tile_bytes bytes of src with the GEMMs'
-    weight-stream access pattern, computing nothing (mxg_hbm_read_probe)."""
-    if not src.is_cuda or src.numel() * src.element_size() < tiles * tile_bytes:
-        raise ValueError("src must be a device tensor of at least tiles * tile_bytes bytes")
+def hbm_read_probe(w: "PackedWeight", sink: torch.Tensor, stream=None) -> None:
+    """Measurement aid: read the packed weight w as the GEMMs' weight stream
+    does, computing nothing (mxg_hbm_read_probe)."""
     if not sink.is_cuda or sink.dtype != torch.int32 or sink.numel() < 1:
         raise ValueError("sink must be a device int32 tensor")
-    _check(lib().mxg_hbm_read_probe(src.data_ptr(), tiles, tile_bytes, sink.data_ptr(),
+    _check(lib().mxg_hbm_read_probe(w.q.data_ptr(), w.s.data_ptr(), w.N, w.K, sink.data_ptr(),
                                      _stream(stream)))
 
 

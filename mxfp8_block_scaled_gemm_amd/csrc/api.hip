@@ -403,17 +403,17 @@ int mxfp8_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_
   return launched(mxg::launch_quantize(x, M, K, ld_x, q, s, (hipStream_t)stream));
 }
 
-int mxg_hbm_read_probe(const void* src, int64_t tiles, int64_t tile_bytes, uint32_t* sink,
-                       void* stream) {
-  if (!src || !sink) return MXG_ERR_NULL;
-  if (tiles < 1 || tiles > (1 << 20) || tile_bytes < 16 || tile_bytes > 131072 ||
-      tile_bytes % 16 != 0)
+int mxg_hbm_read_probe(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K,
+                       uint32_t* sink, void* stream) {
+  if (!w_q || !w_s || !sink) return MXG_ERR_NULL;
+  if (N < 16 || N % 16 != 0 || N > ((int64_t)1 << 24) || K < 128 || K % 128 != 0 || K > 8192)
     return MXG_ERR_SHAPE;
-  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return MXG_ERR_ALIGN;
+  if (!aligned16(w_q) || !aligned16(w_s) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
+    return MXG_ERR_ALIGN;
   int st = check_device();
   if (st != MXG_OK) return st;
-  return launched(mxg::launch_hbm_read(reinterpret_cast<const uint8_t*>(src), (int)tiles,
-                                       (uint32_t)tile_bytes, sink, (hipStream_t)stream));
+  return launched(
+      mxg::launch_hbm_read(w_q, w_s, (int)(N / 16), (int)(K / 128), sink, (hipStream_t)stream));
 }
 
 int mxfp8_pack_weights(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K,

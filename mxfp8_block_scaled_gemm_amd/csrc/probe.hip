@@ -1,45 +1,54 @@
-// HBM read ceiling of a single launch: reads the same bytes the small-row
-// GEMM's weight stream reads, with the same access pattern (one workgroup of
-// 16 waves per 16-row weight tile, every wave issuing all of its 2 KiB steps
-// up front as non-temporal 16-byte buffer loads), and does nothing else.
-// Its per-launch time is the floor any kernel streaming those bytes in one
-// launch meets on this machine: launch and drain included, no arithmetic,
-// no activations, no output.  The loaded words are folded into one value
-// that is stored only when it equals a pattern the caller never writes, so
-// no load can be dropped and nothing is written.
+// HBM read ceiling of a single launch: reads a packed MXFP8 weight exactly as
+// the small-row GEMM's weight stream does (one workgroup of 16 waves per
+// 16-row tile; every wave issues all of its 128-wide K steps up front, each
+// step two non-temporal 16-byte code loads and one scale-byte load per lane)
+// and does nothing else.  Its per-launch time is the floor any kernel
+// streaming that weight in one launch meets on this machine: launch and
+// drain included, no arithmetic, no activations, no output.  The loaded
+// words are folded into one value that is stored only when it equals a
+// pattern no weight produces by accident, so no load can be dropped and
+// nothing is written.
 #include "mx_device.hpp"
 #include "mx_launch.hpp"
 
 namespace mxg {
 
 constexpr int kProbeWaves = 16;
-constexpr int kProbeSlots = 4;    // steps per wave: tiles up to 128 KiB
+constexpr int kProbeSlots = 4;    // steps per wave: K up to 8192
 
-__global__ __launch_bounds__(kProbeWaves * 64) void hbm_read_kernel(const uint8_t* src,
-                                                                     uint32_t tile_bytes,
-                                                                     uint32_t* sink) {
+__global__ __launch_bounds__(kProbeWaves * 64) void hbm_read_kernel(const uint8_t* w_q,
+                                                                     const uint8_t* w_s,
+                                                                     int steps, uint32_t* sink) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const auto r = make_rsrc(src + (size_t)blockIdx.x * tile_bytes, tile_bytes);
-  v4i v[2 * kProbeSlots];
+  const int t = blockIdx.x;
+  const auto rq = make_rsrc(w_q + (size_t)t * steps * 2048, (uint32_t)(steps * 2048));
+  const auto rs = make_rsrc(w_s + (size_t)t * steps * 64, (uint32_t)(steps * 64));
+  v4i lo[kProbeSlots], hi[kProbeSlots];
+  uint32_t sc[kProbeSlots];
 #pragma unroll
   for (int j = 0; j < kProbeSlots; ++j) {
-    const uint32_t step = (uint32_t)(wave + kProbeWaves * j) * 2048u;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      v[2 * j + h] = buf_ld16_nt(r, step + 1024u * h + 16u * lane);
+    const int s = wave + kProbeWaves * j;
+    const bool ok = s < steps;
+    lo[j] = buf_ld16_nt(rq, ok ? (uint32_t)(s * 2048 + 16 * lane) : kOutOfRange);
+    hi[j] = buf_ld16_nt(rq, ok ? (uint32_t)(s * 2048 + 1024 + 16 * lane) : kOutOfRange);
+    sc[j] = buf_ld8(rs, ok ? (uint32_t)(s * 64 + lane) : kOutOfRange);
   }
-  v4i acc = v[0];
+  v4i acc = lo[0] ^ hi[0];
+  uint32_t a = sc[0];
 #pragma unroll
-  for (int i = 1; i < 2 * kProbeSlots; ++i) acc ^= v[i];
-  const uint32_t x = (uint32_t)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+  for (int j = 1; j < kProbeSlots; ++j) {
+    acc ^= lo[j] ^ hi[j];
+    a ^= sc[j];
+  }
+  const uint32_t x = (uint32_t)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) ^ (a << 24);
   if (x == 0x9E3779B9u && acc[0] == 0x7F4A7C15) sink[0] = x;
 }
 
-hipError_t launch_hbm_read(const uint8_t* src, int tiles, uint32_t tile_bytes, uint32_t* sink,
-                           hipStream_t stream) {
-  hipLaunchKernelGGL(hbm_read_kernel, dim3(tiles), dim3(kProbeWaves * 64), 0, stream, src,
-                     tile_bytes, sink);
+hipError_t launch_hbm_read(const uint8_t* w_q, const uint8_t* w_s, int tiles, int steps,
+                           uint32_t* sink, hipStream_t stream) {
+  hipLaunchKernelGGL(hbm_read_kernel, dim3(tiles), dim3(kProbeWaves * 64), 0, stream, w_q, w_s,
+                     steps, sink);
   return hipGetLastError();
 }
 

@@ -87,14 +87,13 @@ def test_quantize_rejects(lib, args, status):
 
 
 @pytest.mark.parametrize("args,status", [
-    ((None, 256, 84480, P(1)), 1),
-    ((P(0), 256, 84480, None), 1),
-    ((P(0), 0, 84480, P(1)), 3),
-    ((P(0), 256, 8, P(1)), 3),
-    ((P(0), 256, 131072 + 16, P(1)), 3),
-    ((P(0), 256, 84488, P(1)), 3),
-    ((ctypes.c_void_p(A + 8), 256, 84480, P(1)), 2),
-    ((P(0), 256, 84480, ctypes.c_void_p(A + 2)), 2),
+    ((None, P(1), 4096, 5120, P(2)), 1),
+    ((P(0), P(1), 4096, 5120, None), 1),
+    ((P(0), P(1), 4100, 5120, P(2)), 3),
+    ((P(0), P(1), 4096, 5000, P(2)), 3),
+    ((P(0), P(1), 4096, 8192 + 128, P(2)), 3),
+    ((ctypes.c_void_p(A + 8), P(1), 4096, 5120, P(2)), 2),
+    ((P(0), P(1), 4096, 5120, ctypes.c_void_p(A + 2)), 2),
 ])
 def test_hbm_read_probe_rejects(lib, args, status):
     assert lib.mxg_hbm_read_probe(*args, None) == status
@@ -107,7 +106,7 @@ def test_forced_foreign_arch_is_rejected_before_launch(lib, monkeypatch):
     assert gemm(lib) == 5
     assert lib.mxfp8_quantize(P(0), 4, 64, 64, P(1), P(2), None) == 5
     assert lib.wo_a_fused_quantize(ctypes.byref(_wo_a()), None) == 5
-    assert lib.mxg_hbm_read_probe(P(0), 256, 84480, P(1), None) == 5
+    assert lib.mxg_hbm_read_probe(P(0), P(1), 4096, 5120, P(2), None) == 5
 
 
 def test_workspace_size_is_positive(lib):
