@@ -255,8 +255,12 @@ typedef unsigned v4u32 __attribute__((ext_vector_type(4)));
 // tile are summed through LDS in wave order; with P > 1 the FP32 tile sums
 // go to the workspace and the last of the P workgroups of a tile group to
 // arrive adds them in part order (deterministic) and stores BF16.
-template <int MB, int T, int SPW, int NB, int CHM>
+template <int MB, int T, int SPW, int NB, int CHM, bool FQ>
 __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p) {
+  // Registers per thread per K chunk: CHM 16-byte code chunks, or with BF16
+  // input (M <= 16) one whole 32-element block per thread (64 per row).
+  constexpr int CHL = FQ ? 4 : CHM;
+  static_assert(!FQ || MB == 1, "BF16 staging serves up to 16 rows");
   constexpr int W = kM16Waves, kT = W * 64, WPT = W / T;  // waves per tile
   constexpr int kLdA = 16 * 128 + 16;                   // LDS bytes per code row of a chunk
   constexpr int kLdS = 16 * 4 + 4;                      // LDS bytes per scale row of a chunk
@@ -283,7 +287,7 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p) {
   const auto ra = make_rsrc(p.a_q + grp, (uint32_t)((M - 1) * lda + K));
   const auto rs = make_rsrc(p.a_s + (grp >> 5), (uint32_t)((M - 1) * ldas + (K >> 5)));
   // Chunk c: steps [k0 + 16c, k0 + 16c + 16) within the part.
-  auto stage_load = [&](int c, v4i (&st)[CHM], uint32_t& sc) {
+  auto stage_load = [&](int c, v4i (&st)[CHL], uint32_t& sc) {
     const int nsc_steps = min(16, ns - 16 * c);
     const int cpr = nsc_steps * 8, nck = M * cpr;
     const int col0 = (k0 + 16 * c) * 128;
@@ -298,7 +302,7 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p) {
     sc = __builtin_amdgcn_raw_buffer_load_b32(
         rs, tid < nsc ? row * ldas + (k0 + 16 * c + cd) * 4 : (int)kOutOfRange, 0, 0);
   };
-  auto stage_park = [&](int c, const v4i (&st)[CHM], uint32_t sc) {
+  auto stage_park = [&](int c, const v4i (&st)[CHL], uint32_t sc) {
     const int nsc_steps = min(16, ns - 16 * c);
     const int cpr = nsc_steps * 8, nck = M * cpr;
 #pragma unroll
@@ -316,12 +320,53 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p) {
     }
   };
 
+  // BF16 input: the chunk's 32-element blocks (64 per row), one whole block
+  // per thread, quantized while parked; the first tile group's workgroups
+  // also write the codes out.
+  auto load_bf16 = [&](int c, v4i (&st)[CHL]) {
+    const int nsc_steps = min(16, ns - 16 * c);
+    const int col0 = (k0 + 16 * c) * 128;
+    const auto rx = make_rsrc(p.x, (uint32_t)(((M - 1) * p.ld_x + K) * 2));
+    const int bpr = nsc_steps * 4, nblk = M * bpr;
+    const int row = tid / bpr, cb = tid - row * bpr;
+    const uint32_t off = (uint32_t)(row * p.ld_x + col0 + cb * 32) * 2u;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) st[h] = buf_ld16(rx, tid < nblk ? off + 16 * h : kOutOfRange);
+  };
+  auto park_bf16 = [&](int c, const v4i (&st)[CHL], uint8_t* act, int ldA_, uint8_t* scl,
+                       int ldS_) {
+    const int nsc_steps = min(16, ns - 16 * c);
+    const int bpr = nsc_steps * 4, nblk = M * bpr;
+    const int col0 = (k0 + 16 * c) * 128;
+    if (tid < nblk) {
+      const int row = tid / bpr, cb = tid - row * bpr;
+      v4i c0, c1;
+      int e;
+      quant_block32(&st[0], c0, c1, e);
+      *reinterpret_cast<v4i*>(act + row * ldA_ + cb * 32) = c0;
+      *reinterpret_cast<v4i*>(act + row * ldA_ + cb * 32 + 16) = c1;
+      scl[row * ldS_ + cb] = (uint8_t)(e + 127);
+      if (tg == 0) {
+        uint8_t* qo = p.a_q + (int64_t)row * K + col0 + cb * 32;
+        *reinterpret_cast<v4i*>(qo) = c0;
+        *reinterpret_cast<v4i*>(qo + 16) = c1;
+        p.a_s[((int64_t)row * K + col0 + cb * 32) >> 5] = (uint8_t)(e + 127);
+      }
+    }
+  };
+
   // 1. Activations (chunk 0, or all chunks) ahead of the weight stream.
-  v4i st[NB][CHM];
+  v4i st[NB][CHL];
   uint32_t sc[NB];
 #pragma unroll
-  for (int c = 0; c < NB; ++c)
-    if (c < nch) stage_load(c, st[c], sc[c]);
+  for (int c = 0; c < NB; ++c) {
+    if (c < nch) {
+      if constexpr (FQ)
+        load_bf16(c, st[c]);
+      else
+        stage_load(c, st[c], sc[c]);
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // 2. The weight stream: slot j = step wi + WPT j of my tile.
@@ -353,7 +398,8 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p) {
     uint8_t* w_scl = smem + M * ldA;
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
-      if (c < nch) {
+      if (FQ && c < nch) park_bf16(c, st[c], s_act + 2048 * c, ldA, w_scl + 64 * c, ldS);
+      if (!FQ && c < nch) {
         const int nsc_steps = min(16, ns - 16 * c);
         const int cpr = nsc_steps * 8, nck = M * cpr;
 #pragma unroll
@@ -392,9 +438,17 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p) {
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     if (c < nch) {                                      // uniform
-      stage_park(c, st[NB > 1 ? c : 0], sc[NB > 1 ? c : 0]);
+      if constexpr (FQ)
+        park_bf16(c, st[NB > 1 ? c : 0], s_act, kLdA, s_scl, kLdS);
+      else
+        stage_park(c, st[NB > 1 ? c : 0], sc[NB > 1 ? c : 0]);
       __syncthreads();
-      if (NB == 1 && c + 1 < nch) stage_load(c + 1, st[0], sc[0]);
+      if (NB == 1 && c + 1 < nch) {
+        if constexpr (FQ)
+          load_bf16(c + 1, st[0]);
+        else
+          stage_load(c + 1, st[0], sc[0]);
+      }
 #pragma unroll
       for (int j = c * T; j < c * T + T && j < SPW; ++j) {
         const int stp = wi + WPT * j;
@@ -585,18 +639,19 @@ int device_cus() {
   return cached;
 }
 
-template <int MB, int T, int SPW>
+template <int MB, int T, int SPW, bool FQ>
 hipError_t launch_2d(const GemmArgs& a, hipStream_t stream) {
   constexpr int CHM = (MB * 16 * 16 * 8 + kM16Waves * 64 - 1) / (kM16Waves * 64);
+  constexpr int CHL = FQ ? 4 : CHM;                      // staging registers per chunk (v4i)
   constexpr int NCH = (SPW + T - 1) / T;
   // The whole part's activations in registers (then in LDS at once) while
   // they fit beside the weight slots; otherwise chunk by chunk.
-  constexpr bool kRegs = NCH * CHM * 4 + SPW * 9 + MB * 4 <= 120;
+  constexpr bool kRegs = NCH * CHL * 4 + SPW * 9 + MB * 4 <= 120;
   const size_t whole_lds = (size_t)a.M * (a.Sp * 128 + 16) + (size_t)a.M * (a.Sp * 4 + 4);
   const bool whole = kRegs && NCH > 1 && whole_lds <= 160 * 1024 - 64;
   const int grid = (a.N / 16 / T) * a.P;
   if (whole) {
-    auto kern = gemm_2d_kernel<MB, T, SPW, (kRegs ? NCH : 1), CHM>;
+    auto kern = gemm_2d_kernel<MB, T, SPW, (kRegs ? NCH : 1), CHM, FQ>;
     static bool configured = false;
     if (!configured) {
       // 160 KiB of LDS per workgroup, less the kernel's static word
@@ -610,7 +665,7 @@ hipError_t launch_2d(const GemmArgs& a, hipStream_t stream) {
     if (whole_lds > lds) lds = (whole_lds + 15) & ~(size_t)15;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kM16Waves * 64), lds, stream, a);
   } else {
-    auto kern = gemm_2d_kernel<MB, T, SPW, 1, CHM>;
+    auto kern = gemm_2d_kernel<MB, T, SPW, 1, CHM, FQ>;
     static bool configured = false;
     if (!configured) {
       hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -625,23 +680,37 @@ hipError_t launch_2d(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MB, int T>
+template <int MB, int T, bool FQ>
 hipError_t launch_2d_spw(const GemmArgs& a, int spw, hipStream_t stream) {
   switch (spw) {
-    case 1: return launch_2d<MB, T, 1>(a, stream);
-    case 2: return launch_2d<MB, T, 2>(a, stream);
-    case 3: return launch_2d<MB, T, 3>(a, stream);
-    case 4: return launch_2d<MB, T, 4>(a, stream);
-    case 6: return launch_2d<MB, T, 6>(a, stream);
-    default: return launch_2d<MB, T, 8>(a, stream);
+    case 1: return launch_2d<MB, T, 1, FQ>(a, stream);
+    case 2: return launch_2d<MB, T, 2, FQ>(a, stream);
+    case 3: return launch_2d<MB, T, 3, FQ>(a, stream);
+    case 4: return launch_2d<MB, T, 4, FQ>(a, stream);
+    case 6: return launch_2d<MB, T, 6, FQ>(a, stream);
+    default: return launch_2d<MB, T, 8, FQ>(a, stream);
   }
 }
 
-template <int MB>
+template <int MB, bool FQ>
 hipError_t launch_2d_t(const GemmArgs& a, int T, int spw, hipStream_t stream) {
-  if (T == 1) return launch_2d_spw<MB, 1>(a, spw, stream);
-  if (T == 2) return launch_2d_spw<MB, 2>(a, spw, stream);
-  return launch_2d_spw<MB, 4>(a, spw, stream);
+  if (T == 1) return launch_2d_spw<MB, 1, FQ>(a, spw, stream);
+  if (T == 2) return launch_2d_spw<MB, 2, FQ>(a, spw, stream);
+  return launch_2d_spw<MB, 4, FQ>(a, spw, stream);
+}
+
+// With BF16 input only for M <= 16 (larger row counts would spill the
+// staging registers); the caller quantizes the others first.
+template <bool FQ>
+hipError_t launch_2d_mb(const GemmArgs& a, int T, int spw, hipStream_t stream) {
+  const int mb = (a.M + 15) / 16;
+  if (mb == 1) return launch_2d_t<1, FQ>(a, T, spw, stream);
+  if constexpr (FQ) {
+    return hipErrorInvalidValue;
+  } else {
+    if (mb == 2) return launch_2d_t<2, FQ>(a, T, spw, stream);
+    return launch_2d_t<3, FQ>(a, T, spw, stream);
+  }
 }
 
 }  // namespace
@@ -706,21 +775,28 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
       return launch_gemm(b, stream);
     }
   }
-  // Otherwise the 2D kernel; BF16 input is quantized by its own launch first.
+  // Otherwise the 2D kernel.  BF16 input is quantized while staging when
+  // M <= 16 and a workgroup's share is small (M * Sp <= 1024: at most four
+  // 32-blocks per thread over its K part), else by its own launch first.
+  if (pl.T == 0) return hipErrorInvalidValue;
+  GemmArgs b = a;
+  b.P = pl.P;
+  b.Sp = pl.Sp;
+  if (pl.P > 1 && (b.ctr == nullptr || b.part == nullptr)) return hipErrorInvalidValue;
+  // (Only where the kernel holds the whole part's BF16 blocks in registers:
+  // chunk by chunk, the in-kernel quantize measured no faster.)
+  const int nch_fq = (pl.SPW + pl.T - 1) / pl.T;
+  const bool fq_regs = nch_fq * 16 + pl.SPW * 9 + 4 <= 120 &&
+                       (size_t)a.M * (pl.Sp * 128 + 16) + (size_t)a.M * (pl.Sp * 4 + 4) <=
+                           160 * 1024 - 64;
+  if (fq && a.M <= 16 && a.M * pl.Sp <= 1024 && fq_regs)
+    return launch_2d_mb<true>(b, pl.T, pl.SPW, stream);
   if (fq) {
     hipError_t e = launch_quantize(a.x, a.M, a.K, a.ld_x, a.a_q, a.a_s, stream);
     if (e != hipSuccess) return e;
   }
-  GemmArgs b = a;
   b.x = nullptr;
-  if (pl.T == 0) return hipErrorInvalidValue;
-  b.P = pl.P;
-  b.Sp = pl.Sp;
-  if (pl.P > 1 && (b.ctr == nullptr || b.part == nullptr)) return hipErrorInvalidValue;
-  const int mb = (a.M + 15) / 16;
-  if (mb == 1) return launch_2d_t<1>(b, pl.T, pl.SPW, stream);
-  if (mb == 2) return launch_2d_t<2>(b, pl.T, pl.SPW, stream);
-  return launch_2d_t<3>(b, pl.T, pl.SPW, stream);
+  return launch_2d_mb<false>(b, pl.T, pl.SPW, stream);
 }
 
 }  // namespace mxg
