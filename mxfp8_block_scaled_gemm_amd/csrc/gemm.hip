@@ -755,9 +755,12 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
   // BF16 input either choice pays about as much for the quantize: in-kernel
   // in the M <= 16 kernel, a launch before the 2D kernel.)
   const bool m16_fast = pl.cost >= 0.75 * plan_cost(a.M, a.N, a.K, 1, 1, device_cus());
-  // In-kernel quantize up to two 32-blocks per thread (M*K <= 65536):
-  // measured faster than a quantize launch up to there, slower beyond.
-  const bool fq_inline = fq && ch <= 2;
+  // In-kernel quantize up to two 32-blocks per thread (M*K <= 65536) per
+  // workgroup a CU runs: measured faster than a quantize launch up to there
+  // (every workgroup repeats the whole quantize, so a grid of two rounds
+  // counts double).
+  const int per_cu = (a.N / 16 + device_cus() - 1) / device_cus();
+  const bool fq_inline = fq && ch * per_cu <= 2;
   const int force = forced_kernel();                       // tests: 1 = M <= 16 kernel, 2 = 2D
   const bool m16_ok = gemm_m16_fits(a.M, a.K) && steps <= 4;
   if (m16_ok && (force == 1 || (force == 0 && m16_fast))) {
