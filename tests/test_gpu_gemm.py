@@ -244,3 +244,27 @@ def test_workspace_left_clean(M, N, K, kind, monkeypatch):
 def test_widest_output(M, path):
     # 2048 weight tiles: several rounds of workgroups over the CUs
     run_case(M, 32768, 1024, seed=M)
+
+
+@pytest.mark.parametrize("M", [3, 16, 40])
+def test_strided_bf16_input(M, path):
+    # x as the leading K columns of a wider BF16 matrix (row stride > K), as
+    # the chain's requantize reads A's output; quantized in whichever kernel
+    # serves the shape.
+    N, K, ld = 512, 1024, 1024 + 96
+    case = synth.gemm_case(M, N, K, seed=M + 1)
+    x_bits = synth.bits(case["x"])
+    ow_q, ow_s = oracle.quantize(synth.bits(case["w"]))
+    oa_q, oa_s = oracle.quantize(x_bits)
+    ref = oracle.gemm(oa_q, oa_s, ow_q, ow_s)
+    say(f"gemm strided bf16 input M={M} ld={ld}")
+    wide = torch.zeros(M, ld, dtype=torch.bfloat16)
+    wide[:, :K] = case["x"]
+    x = wide.cuda()[:, :K]
+    w = mx.PackedWeight.from_rows(dev_u8(ow_q), dev_u8(ow_s))
+    a_q = torch.full((M, K), 0x55, dtype=torch.uint8, device="cuda")
+    a_s = torch.full((M, K // 32), 0x55, dtype=torch.uint8, device="cuda")
+    out = mx.mxfp8_gemm(a_q, a_s, w, x=x)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u8(a_q), oa_q) and np.array_equal(host_u8(a_s), oa_s)
+    check_gemm(out, ref, f"strided M={M}")
