@@ -13,8 +13,8 @@ single-stage functions, in the order the pages give.
 
 Sources ("pages"): vLLM API documentation pages for
 ``vllm.models.deepseek_v41.nvidia.specialized_decode.attention.mxfp8`` ([mxfp8]),
-``...attention.step`` ([step]) and ``vllm.models.deepseek_v41.nvidia.ops.o_proj``
-([o_proj]).
+``...attention.step`` ([step]), ``vllm.models.deepseek_v41.nvidia.ops.cute_dsl``
+([cute]) and ``vllm.models.deepseek_v41.nvidia.ops.o_proj`` ([o_proj]).
 
 Array conventions: BF16 tensors are numpy ``uint16`` bit patterns, E4M3 codes and
 E8M0 scale bytes are ``uint8``; everything is row-major and C-contiguous unless a
@@ -77,6 +77,8 @@ def _load():
                                      ctypes.POINTER(ctypes.c_int64),
                                      ctypes.POINTER(ctypes.c_float), i64, u16p]
             lib.orc_rope.restype = ctypes.c_int
+            lib.orc_rmsnorm.argtypes = [u16p, i64, i64, i64, u16p, ctypes.c_double, f64p]
+            lib.orc_rmsnorm.restype = ctypes.c_int
             lib.orc_set_threads.argtypes = [ctypes.c_int]
             lib.orc_set_threads.restype = None
             lib.orc_num_threads.argtypes = []
@@ -238,6 +240,49 @@ def rope(o_bf16: np.ndarray, positions: np.ndarray, cos_sin: np.ndarray,
     if rc != 0:
         raise ValueError("orc_rope rejected the input")
     return y
+
+
+# ----------------------------------------------------------------- RMSNorm
+
+def rmsnorm(x_bf16: np.ndarray, w_bf16: np.ndarray, eps: float, K: int | None = None):
+    """Unrounded fp64 RMSNorm of the leading K columns of BF16 rows:
+    y = x * w / sqrt(mean(x^2) + eps) (the normalisation [step]
+    _split_qkv_and_norm and [cute] AllReduceMHC apply before an MXFP8
+    quantize).  ``x_bf16``: uint16 [M, >=K]; ``w_bf16``: uint16 [K]."""
+    x = np.ascontiguousarray(np.asarray(x_bf16))
+    w = np.ascontiguousarray(np.asarray(w_bf16))
+    if x.dtype != np.uint16 or x.ndim != 2 or w.dtype != np.uint16:
+        raise TypeError("x_bf16 and w_bf16 must be uint16 arrays")
+    M = x.shape[0]
+    K = x.shape[1] if K is None else K
+    if w.shape != (K,):
+        raise ValueError("w_bf16 must hold K values")
+    y = np.zeros((M, K), dtype=np.float64)
+    rc = _load().orc_rmsnorm(_ptr(x, ctypes.c_uint16), M, K, x.shape[1],
+                             _ptr(w, ctypes.c_uint16), float(eps), _ptr(y, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("orc_rmsnorm rejected the input")
+    return y
+
+
+def rmsnorm_quantize(x_bf16: np.ndarray, w_bf16: np.ndarray, eps: float, K: int | None = None):
+    """RMSNorm rounded once to BF16, then the MXFP8 quantize of that BF16
+    tensor (every inter-stage tensor is BF16 before it is requantized).
+    Returns (y fp64 unrounded, y BF16 bits, codes, scales)."""
+    y = rmsnorm(x_bf16, w_bf16, eps, K)
+    yb = bf16_round(y)
+    q, s = quantize(yb)
+    return y, yb, q, s
+
+
+def rmsnorm_tolerance(y_ref: np.ndarray, K: int) -> np.ndarray:
+    """Bound on |BF16 result - exact value| for an FP32 evaluation of the
+    RMSNorm (sum of K squares in any order, a division, a square root, a
+    reciprocal, two products) rounded once to BF16: half a BF16 ulp (BF16
+    keeps 8 significant bits, so 2^-8 relative at most) plus (K/2 + 4) units
+    of FP32 rounding (2^-24 relative), plus the smallest BF16 subnormal step
+    for results near zero."""
+    return (2.0 ** -8 + (K / 2 + 4) * 2.0 ** -24) * np.abs(y_ref) + 2.0 ** -133
 
 
 # ------------------------------------------------------------ compositions

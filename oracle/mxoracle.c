@@ -278,6 +278,37 @@ int orc_rope(const uint16_t *o, int64_t M, int64_t H, int64_t D, int64_t ld_row,
     return 0;
 }
 
+/* RMSNorm of BF16 rows, unrounded ([step] AttentionStep.run normalises the
+ * leading columns of fused_wqa_wkv's output in _split_qkv_and_norm before they
+ * are requantized for wq_b; [cute] AllReduceMHC normalises its collapse with a
+ * BF16 norm_weight and norm_eps and can write the result as MXFP8):
+ *   y[m][j] = x[m][j] * w[j] / sqrt(mean_k x[m][k]^2 + eps),
+ * the root-mean-square normalisation with a per-column gain.  Reading (the
+ * pages print no formula): the mean runs over the K normalised columns, eps
+ * is added inside the square root, and the exact real value (here fp64) is
+ * what the product path rounds once to BF16 before its MXFP8 quantize.
+ * x: BF16 [M, >= K] with row stride ldx; w: BF16 [K]; y: fp64 [M, K]. */
+int orc_rmsnorm(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const uint16_t *w,
+                double eps, double *y)
+{
+    if (K < 1 || ldx < K || !(eps >= 0.0))
+        return -1;
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *row = x + m * ldx;
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = orc_bf16_value(row[k]);
+            if (!isfinite(v))
+                return -1;
+            ss += v * v;
+        }
+        double r = 1.0 / sqrt(ss / (double)K + eps);
+        for (int64_t k = 0; k < K; ++k)
+            y[m * K + k] = orc_bf16_value(row[k]) * orc_bf16_value(w[k]) * r;
+    }
+    return 0;
+}
+
 /* Thread count for the parallel loop of orc_gemm: set it, and read back the
  * number a parallel region actually runs with. */
 void orc_set_threads(int n)
