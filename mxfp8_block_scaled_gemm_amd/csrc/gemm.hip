@@ -92,8 +92,10 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
 
   // 1. Activation staging loads (L2-resident, small): issued first so that
   //    waiting for them does not wait for the weight stream.
+  // Scale dwords are an eighth of the 16-byte code chunks.
+  constexpr int SCR = FQ ? 1 : (CH + 7) / 8;
   v4i st[FQ ? 4 * CH : CH];
-  uint32_t sc[FQ ? 1 : 2];
+  uint32_t sc[SCR];
   const int nck = FQ ? (M * K) >> 5 : (M * K) >> 4;        // 32-blocks, or 16-byte chunks
   auto chunk = [&](int i) {                                // chunk id, or -1
     const int c = tid + i * kThreads;
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
     const auto rs = make_rsrc(p.a_s + (grp >> 5), (uint32_t)((M - 1) * ldas + KB));
     const int nsc = (M * KB) >> 2, spr = KB >> 2;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < SCR; ++i) {
       const int c = tid + i * kThreads;
       const int row = c / spr, col = (c - row * spr) * 4;
       sc[i] = __builtin_amdgcn_raw_buffer_load_b32(
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
     const int spr = KB >> 2;
     const int nsc = (M * KB) >> 2;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < SCR; ++i) {
       const int c = tid + i * kThreads;
       if (c < nsc) {
         const int row = c / spr, col = (c - row * spr) * 4;
@@ -226,12 +228,10 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
 #pragma unroll
     for (int w = 1; w < W; ++w) sum += s_red[w * 64 + lane];
     const int m = lane & 15, n = 16 * t + 4 * (lane >> 4);
-    if (m < M) {
-      uint2 o;
-      o.x = f32_to_bf16(sum[0]) | (f32_to_bf16(sum[1]) << 16);
-      o.y = f32_to_bf16(sum[2]) | (f32_to_bf16(sum[3]) << 16);
-      *reinterpret_cast<uint2*>(p.out + (int64_t)m * p.N + n) = o;
-    }
+    uint2 o;
+    o.x = f32_to_bf16(sum[0]) | (f32_to_bf16(sum[1]) << 16);
+    o.y = f32_to_bf16(sum[2]) | (f32_to_bf16(sum[3]) << 16);
+    if (m < M) *reinterpret_cast<uint2*>(p.out + (int64_t)m * p.N + n) = o;
   }
 }
 
@@ -526,14 +526,14 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p) {
 
 // ------------------------------------------------------------------ launch
 
-size_t gemm_m16_lds_bytes(int M, int K) {
-  return (size_t)((M * act_ld(K) + M * scale_ld(K) + 15) & ~15) + kM16Waves * 64 * sizeof(v4f);
+size_t gemm_m16_lds_bytes(int M, int K, int W) {
+  return (size_t)((M * act_ld(K) + M * scale_ld(K) + 15) & ~15) + (size_t)W * 64 * sizeof(v4f);
 }
 
-template <int SPW, int CH, bool FQ>
+template <int W, int SPW, int CH, bool FQ>
 static hipError_t launch_m16(const GemmArgs& a, hipStream_t stream) {
-  auto kern = gemm_m16_kernel<kM16Waves, SPW, CH, FQ>;
-  const size_t lds = gemm_m16_lds_bytes(a.M, a.K);
+  auto kern = gemm_m16_kernel<W, SPW, CH, FQ>;
+  const size_t lds = gemm_m16_lds_bytes(a.M, a.K, W);
   static bool configured = false;   // raise the dynamic-LDS limit once per instance
   if (!configured) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -541,29 +541,51 @@ static hipError_t launch_m16(const GemmArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL(kern, dim3(a.N / 16), dim3(kM16Waves * 64), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3(a.N / 16), dim3(W * 64), lds, stream, a);
   return hipGetLastError();
 }
 
-template <int SPW, bool FQ>
+// Staging registers per thread: 16-byte code chunks (MXFP8 input) or whole
+// 32-element blocks (BF16 input), rounded up to an instantiated count.
+template <int W, int SPW, bool FQ>
 static hipError_t launch_m16_ch(const GemmArgs& a, int ch, hipStream_t stream) {
   if constexpr (FQ) {
-    if (ch <= 1) return launch_m16<SPW, 1, FQ>(a, stream);
-    return launch_m16<SPW, 2, FQ>(a, stream);
+    if (ch <= 1) return launch_m16<W, SPW, 1, FQ>(a, stream);
+    if (ch <= 2) return launch_m16<W, SPW, 2, FQ>(a, stream);
   } else {
-    if (ch <= 2) return launch_m16<SPW, 2, FQ>(a, stream);
-    if (ch <= 4) return launch_m16<SPW, 4, FQ>(a, stream);
-    if (ch <= 8) return launch_m16<SPW, 8, FQ>(a, stream);
-    return launch_m16<SPW, 16, FQ>(a, stream);
+    if (ch <= 2) return launch_m16<W, SPW, 2, FQ>(a, stream);
+    if (ch <= 4) return launch_m16<W, SPW, 4, FQ>(a, stream);
+    if constexpr (W == 16) {
+      if (ch <= 8) return launch_m16<W, SPW, 8, FQ>(a, stream);
+      if (ch <= 16) return launch_m16<W, SPW, 16, FQ>(a, stream);
+    }
   }
+  return hipErrorInvalidValue;
 }
 
+// Largest staging-register count instantiated for W waves (W = 4: one
+// MXFP8 row only).
+int m16_max_ch(int W, bool fq) { return fq ? (W == 4 ? 0 : 2) : (W == 4 ? 4 : 16); }
+
+// Most weight steps per wave instantiated for W waves.
+int m16_max_spw(int W) { return W == 4 ? 16 : 4; }
+
 template <bool FQ>
-static hipError_t launch_m16_spw(const GemmArgs& a, int spw, int ch, hipStream_t stream) {
-  if (spw <= 1) return launch_m16_ch<1, FQ>(a, ch, stream);
-  if (spw <= 2) return launch_m16_ch<2, FQ>(a, ch, stream);
-  if (spw <= 3) return launch_m16_ch<3, FQ>(a, ch, stream);
-  return launch_m16_ch<4, FQ>(a, ch, stream);
+static hipError_t launch_m16_w(const GemmArgs& a, int W, int spw, int ch, hipStream_t stream) {
+  if constexpr (!FQ) {
+    if (W == 4) {
+      if (spw <= 4) return launch_m16_ch<4, 4, FQ>(a, ch, stream);
+      if (spw <= 8) return launch_m16_ch<4, 8, FQ>(a, ch, stream);
+      if (spw <= 10) return launch_m16_ch<4, 10, FQ>(a, ch, stream);
+      if (spw <= 12) return launch_m16_ch<4, 12, FQ>(a, ch, stream);
+      return launch_m16_ch<4, 16, FQ>(a, ch, stream);
+    }
+  }
+  if (W != 16) return hipErrorInvalidValue;
+  if (spw <= 1) return launch_m16_ch<16, 1, FQ>(a, ch, stream);
+  if (spw <= 2) return launch_m16_ch<16, 2, FQ>(a, ch, stream);
+  if (spw <= 3) return launch_m16_ch<16, 3, FQ>(a, ch, stream);
+  return launch_m16_ch<16, 4, FQ>(a, ch, stream);
 }
 
 size_t gemm_2d_lds_bytes(int M, int MB) {
@@ -736,7 +758,32 @@ int forced_kernel() {
 }
 
 // Whether the M <= 16 kernel can stage this activation in LDS.
-bool gemm_m16_fits(int M, int K) { return M <= 16 && gemm_m16_lds_bytes(M, K) <= 160 * 1024; }
+bool gemm_m16_fits(int M, int K, int W) {
+  return M <= 16 && gemm_m16_lds_bytes(M, K, W) <= 160 * 1024;
+}
+
+// Waves per workgroup of the M <= 16 kernel.  With one MXFP8 row, 4 waves
+// holding up to 16 weight steps each (fewer waves to launch, fewer partial
+// tiles to sum, the activation a few hundred bytes) measured 6-8 % faster
+// than 16 waves at K = 1536, 4096 and 8192 on MI355X, but 3 % slower at
+// K = 5120 (10 steps per wave against 2 or 3), which keeps 16.  With more
+// rows, or BF16 input, the activation staging and quantize spread over 16
+// waves win.  MXG_M16_WAVES=16 forces 16 waves for one row as well (tests
+// cover both); 0 is returned when the kernel cannot take the shape.
+int m16_waves(int M, int K, bool fq) {
+  const int S = K / 128;
+  const char* e = std::getenv("MXG_M16_WAVES");
+  const int want = e && std::atoi(e) == 16 ? 16 : 0;
+  for (int W : {4, 16}) {
+    if (want && W != want) continue;
+    if (W == 4 && (M != 1 || fq || K == 5120)) continue;
+    const int steps = (S + W - 1) / W;
+    const int per = fq ? M * K / 32 : M * K / 16;
+    const int ch = (per + W * 64 - 1) / (W * 64);
+    if (steps <= m16_max_spw(W) && ch <= m16_max_ch(W, fq) && gemm_m16_fits(M, K, W)) return W;
+  }
+  return 0;
+}
 
 hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
   GemmArgs a = args;
@@ -744,9 +791,6 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
   const bool fq = a.x != nullptr;
   if (fq && (a.group_tiles != 0 || a.lda != a.K)) return hipErrorInvalidValue;
   const int S = a.K / 128;
-  const int steps = (S + kM16Waves - 1) / kM16Waves;       // weight steps per wave
-  const int per = fq ? a.M * a.K / 32 : a.M * a.K / 16;    // 32-blocks, or 16-byte chunks
-  const int ch = (per + kM16Waves * 64 - 1) / (kM16Waves * 64);
   const Plan pl = choose_plan(a.M, a.N, a.K, a.group_tiles, device_cus());
   // One full-K tile per workgroup with the whole activation in LDS unless
   // the model gives a 2D plan at most 3/4 of its time: the M <= 16 kernel
@@ -755,28 +799,29 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
   // BF16 input either choice pays about as much for the quantize: in-kernel
   // in the M <= 16 kernel, a launch before the 2D kernel.)
   const bool m16_fast = pl.cost >= 0.75 * plan_cost(a.M, a.N, a.K, 1, 1, device_cus());
-  // In-kernel quantize up to two 32-blocks per thread (M*K <= 65536) per
-  // workgroup a CU runs: measured faster than a quantize launch up to there
-  // (every workgroup repeats the whole quantize, so a grid of two rounds
-  // counts double).
+  // In-kernel quantize up to 2048 32-blocks (M*K <= 65536) per workgroup a
+  // CU runs: measured faster than a quantize launch up to there (every
+  // workgroup repeats the whole quantize, so a grid of two rounds counts
+  // double).
   const int per_cu = (a.N / 16 + device_cus() - 1) / device_cus();
-  const bool fq_inline = fq && ch * per_cu <= 2;
+  const bool fq_inline = fq && (a.M * a.K / 32) * per_cu <= 2048;
   const int force = forced_kernel();                       // tests: 1 = M <= 16 kernel, 2 = 2D
-  const bool m16_ok = gemm_m16_fits(a.M, a.K) && steps <= 4;
-  if (m16_ok && (force == 1 || (force == 0 && m16_fast))) {
-    if (!fq && ch <= 16) return launch_m16_spw<false>(a, steps, ch, stream);
+  const int W = m16_waves(a.M, a.K, fq && fq_inline);
+  if (W && (force == 1 || (force == 0 && m16_fast))) {
+    const int steps = (S + W - 1) / W;                     // weight steps per wave
+    const int per = fq ? a.M * a.K / 32 : a.M * a.K / 16;  // 32-blocks, or 16-byte chunks
+    const int ch = (per + W * 64 - 1) / (W * 64);
+    if (!fq) return launch_m16_w<false>(a, W, steps, ch, stream);
     // In-kernel quantize while the weight stream is in flight when the
     // activation is small enough (every workgroup quantizes all of it, one
     // 32-block per lane at a time); larger activations are quantized by
     // their own launch first.
-    if (fq_inline) return launch_m16_spw<true>(a, steps, ch, stream);
-    if (fq) {
-      hipError_t e = launch_quantize(a.x, a.M, a.K, a.ld_x, a.a_q, a.a_s, stream);
-      if (e != hipSuccess) return e;
-      GemmArgs b = a;
-      b.x = nullptr;
-      return launch_gemm(b, stream);
-    }
+    if (fq_inline) return launch_m16_w<true>(a, W, steps, ch, stream);
+    hipError_t e = launch_quantize(a.x, a.M, a.K, a.ld_x, a.a_q, a.a_s, stream);
+    if (e != hipSuccess) return e;
+    GemmArgs b = a;
+    b.x = nullptr;
+    return launch_gemm(b, stream);
   }
   // Otherwise the 2D kernel.  BF16 input is quantized while staging when
   // M <= 16 and a workgroup's share is small (M * Sp <= 1024: at most four

@@ -46,6 +46,11 @@ hipError_t launch_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 
+// RMSNorm + MXFP8 of BF16 rows (rmsnorm.hip); layout 1 = 128 x 4 scale tiles.
+hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                                   const uint16_t* w, float eps, uint16_t* y, int64_t ld_y,
+                                   uint8_t* q, uint8_t* s, int layout, hipStream_t stream);
+
 // Rotary embedding + MXFP8 of the grouped WO-A input (wo_a.hip).
 struct RopeQuantArgs {
   const uint16_t* o;          // BF16, head h of row m at o + m*ld_row + h*ld_head

@@ -268,3 +268,18 @@ def test_strided_bf16_input(M, path):
     torch.cuda.synchronize()
     assert np.array_equal(host_u8(a_q), oa_q) and np.array_equal(host_u8(a_s), oa_s)
     check_gemm(out, ref, f"strided M={M}")
+
+
+@pytest.mark.parametrize("N,K", [(2048, 5120), (8192, 1536), (1024, 4096), (5120, 8192), (256, 128)])
+@pytest.mark.parametrize("waves", ["routed", "16"])
+def test_one_row_both_wave_counts(N, K, waves, monkeypatch):
+    # One MXFP8 row: the M <= 16 kernel runs with 4 waves per workgroup
+    # (up to 16 weight steps per wave) except at K = 5120; forcing 16 waves
+    # covers the other split on the same shapes.
+    monkeypatch.setenv("MXG_GEMM_PATH", "direct")
+    monkeypatch.setenv("MXG_DIRECT_KERNEL", "m16")
+    if waves == "16":
+        monkeypatch.setenv("MXG_M16_WAVES", "16")
+    else:
+        monkeypatch.delenv("MXG_M16_WAVES", raising=False)
+    run_case(1, N, K, seed=K + 7)
