@@ -111,6 +111,52 @@ int mxg_hbm_read_probe(const uint8_t *w_q, const uint8_t *w_s, int64_t N, int64_
 int mxfp8_quantize(const uint16_t *x, int64_t M, int64_t K, int64_t ld_x,
                    uint8_t *q, uint8_t *s, void *stream);
 
+/* Layouts of MXFP8 scale bytes written by mxfp8_rmsnorm_quantize. */
+#define MXG_SCALES_ROW_MAJOR 0 /* [M, K/32], row-major                          */
+#define MXG_SCALES_128X4 1     /* 128 x 4 tiles ([mxfp8] module text: F8_128x4) */
+
+/* Bytes of a 128x4-tiled scale buffer for M rows of K columns:
+ * ceil(M/128)*128 rows times ceil(K/128)*4 scale columns. */
+size_t mxg_scale_bytes_128x4(int64_t M, int64_t K);
+
+/*
+ * mxfp8_rmsnorm_quantize -- RMSNorm of BF16 rows followed by the MXFP8
+ * quantize of the normalised rows, in one launch ([step] AttentionStep.run:
+ * _split_qkv_and_norm normalises the leading columns of fused_wqa_wkv's
+ * output before they go to wq_b as MXFP8; [cute] AllReduceMHC: norm_weight
+ * and norm_eps, with mxfp8_out receiving the normalised layer input as MXFP8
+ * with swizzled 128x4 scales).
+ *
+ * For each row m:
+ *   r = 1 / sqrt(mean_{k<K} x[m,k]^2 + eps)  (FP32, sum in any order)
+ *   y[m,k] = BF16_RNE(x[m,k] * r * w[k])      (FP32 products)
+ *   (q, s) = the quantize of mxfp8_quantize applied to the BF16 row y[m, :].
+ * The pages print no formula; the mean runs over the K normalised columns
+ * and eps sits inside the square root.
+ *
+ *   x             BF16 [M, ld_x]; columns [0, K) of each row are normalised
+ *   M             rows, 1 <= M <= 65535
+ *   K             columns, multiple of 128, <= MXG_MAX_K
+ *   ld_x          row stride of x in elements, >= K, multiple of 8
+ *   w             BF16 [K] per-column gain (norm weight)
+ *   eps           >= 0, finite
+ *   y             out (optional, NULL = not written): BF16 [M, ld_y]
+ *   ld_y          row stride of y in elements, >= K, multiple of 8
+ *   q             out: E4M3 codes [M, K]
+ *   s             out: scale bytes, laid out per scale_layout:
+ *                 MXG_SCALES_ROW_MAJOR: [M, K/32];
+ *                 MXG_SCALES_128X4: mxg_scale_bytes_128x4(M, K) bytes, the
+ *                 scale of row m, block b at
+ *                   ((m/128)*(K/128) + b/4)*512 + (m%32)*16 + ((m%128)/32)*4 + b%4;
+ *                 padding bytes are not written (zero them once, as the
+ *                 pages' MXFP8 buffers are zero-allocated)
+ * Codes and scales are a deterministic function of the BF16 row y.  Status
+ * as above; nothing is launched or written on an error.
+ */
+int mxfp8_rmsnorm_quantize(const uint16_t *x, int64_t M, int64_t K, int64_t ld_x,
+                           const uint16_t *w, float eps, uint16_t *y, int64_t ld_y,
+                           uint8_t *q, uint8_t *s, int32_t scale_layout, void *stream);
+
 /*
  * mxfp8_pack_weights -- one-time repack of an MXFP8 weight into the tile
  * order the GEMM kernels stream.  A pure permutation of bytes:

@@ -78,6 +78,11 @@ def lib() -> ctypes.CDLL:
         L.mxg_hbm_read_probe.restype = ctypes.c_int
         L.mxfp8_quantize.argtypes = [vp, i64, i64, i64, vp, vp, vp]
         L.mxfp8_quantize.restype = ctypes.c_int
+        L.mxfp8_rmsnorm_quantize.argtypes = [vp, i64, i64, i64, vp, ctypes.c_float, vp, i64,
+                                             vp, vp, ctypes.c_int32, vp]
+        L.mxfp8_rmsnorm_quantize.restype = ctypes.c_int
+        L.mxg_scale_bytes_128x4.argtypes = [i64, i64]
+        L.mxg_scale_bytes_128x4.restype = sz
         L.mxfp8_pack_weights.argtypes = [vp, vp, i64, i64, vp, vp, vp]
         L.mxfp8_pack_weights.restype = ctypes.c_int
         L.mxfp8_gemm.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -173,6 +178,46 @@ def mxfp8_quantize(x: torch.Tensor, K: int | None = None, q: torch.Tensor | None
     _expect(s, torch.uint8, "s", (M, K // 32))
     _check(lib().mxfp8_quantize(_ptr(x), M, K, x.stride(0), _ptr(q), _ptr(s), _stream(stream)))
     return q, s
+
+
+SCALES_ROW_MAJOR = 0   # [M, K/32]
+SCALES_128X4 = 1       # 128 x 4 scale tiles (mxg_scale_bytes_128x4 bytes)
+
+
+def scale_bytes_128x4(M: int, K: int) -> int:
+    return int(lib().mxg_scale_bytes_128x4(M, K))
+
+
+def mxfp8_rmsnorm_quantize(x: torch.Tensor, w: torch.Tensor, eps: float, K: int | None = None,
+                           y: torch.Tensor | None = None, q: torch.Tensor | None = None,
+                           s: torch.Tensor | None = None, scale_layout: int = SCALES_ROW_MAJOR,
+                           write_y: bool = True, stream=None):
+    """RMSNorm of the leading K columns of BF16 rows x [M, >=K] with gain w
+    [K], then MXFP8 of the BF16 result.  Returns (y BF16 [M, K] or None,
+    codes [M, K], scales): scales [M, K/32], or a flat zero-initialised
+    buffer of scale_bytes_128x4(M, K) bytes in 128 x 4 tiles."""
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or x.stride(1) != 1:
+        raise TypeError("x must be a 2-D bfloat16 tensor with unit stride along K")
+    M = x.shape[0]
+    K = x.shape[1] if K is None else int(K)
+    _expect(w, torch.bfloat16, "w", (K,))
+    if write_y and y is None:
+        y = torch.empty(M, K, dtype=torch.bfloat16, device=x.device)
+    if y is not None and (y.dim() != 2 or y.dtype != torch.bfloat16 or y.stride(1) != 1 or
+                          y.shape[0] != M or y.shape[1] < K or not y.is_cuda):
+        raise TypeError("y must be a bfloat16 [M, >=K] tensor with unit stride along K")
+    if q is None:
+        q = torch.empty(M, K, dtype=torch.uint8, device=x.device)
+    _expect(q, torch.uint8, "q", (M, K))
+    if s is None:
+        if scale_layout == SCALES_128X4:
+            s = torch.zeros(scale_bytes_128x4(M, K), dtype=torch.uint8, device=x.device)
+        else:
+            s = torch.empty(M, K // 32, dtype=torch.uint8, device=x.device)
+    _check(lib().mxfp8_rmsnorm_quantize(_ptr(x), M, K, x.stride(0), _ptr(w), float(eps), _ptr(y),
+                                        y.stride(0) if y is not None else 0, _ptr(q), _ptr(s),
+                                        int(scale_layout), _stream(stream)))
+    return y, q, s
 
 
 def mxfp8_pack_weights(w_q: torch.Tensor, w_s: torch.Tensor, wp_q: torch.Tensor | None = None,

@@ -51,6 +51,21 @@ int validate_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, con
   return MXG_OK;
 }
 
+int validate_rmsnorm(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint16_t* w,
+                     float eps, const uint16_t* y, int64_t ld_y, const uint8_t* q,
+                     const uint8_t* s, int32_t layout) {
+  if (!x || !w || !q || !s) return MXG_ERR_NULL;
+  if (M < 1 || M > 65535 || K < 128 || K % 128 != 0 || K > MXG_MAX_K || ld_x < K ||
+      ld_x * M > ((int64_t)1 << 30) || !(eps >= 0.f) || eps > 3.0e38f ||
+      (layout != MXG_SCALES_ROW_MAJOR && layout != MXG_SCALES_128X4))
+    return MXG_ERR_SHAPE;
+  if (y && (ld_y < K || ld_y * M > ((int64_t)1 << 30))) return MXG_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(q) || ld_x % 8 != 0 ||
+      (y && (!aligned16(y) || ld_y % 8 != 0)))
+    return MXG_ERR_ALIGN;
+  return MXG_OK;
+}
+
 int validate_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* x, int64_t ld_x,
                   const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w_q,
                   const uint8_t* w_s, const uint16_t* out, size_t ws_bytes, const void* ws) {
@@ -401,6 +416,21 @@ int mxfp8_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_
   if (st != MXG_OK) return st;
   if ((st = check_device()) != MXG_OK) return st;
   return launched(mxg::launch_quantize(x, M, K, ld_x, q, s, (hipStream_t)stream));
+}
+
+size_t mxg_scale_bytes_128x4(int64_t M, int64_t K) {
+  if (M < 1 || K < 1) return 0;
+  return (size_t)((M + 127) / 128) * 128 * (size_t)((K + 127) / 128) * 4;
+}
+
+int mxfp8_rmsnorm_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
+                           const uint16_t* w, float eps, uint16_t* y, int64_t ld_y, uint8_t* q,
+                           uint8_t* s, int32_t scale_layout, void* stream) {
+  int st = validate_rmsnorm(x, M, K, ld_x, w, eps, y, ld_y, q, s, scale_layout);
+  if (st != MXG_OK) return st;
+  if ((st = check_device()) != MXG_OK) return st;
+  return launched(mxg::launch_rmsnorm_quantize(x, M, K, ld_x, w, eps, y, ld_y, q, s,
+                                               scale_layout, (hipStream_t)stream));
 }
 
 int mxg_hbm_read_probe(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K,

@@ -285,6 +285,30 @@ def rmsnorm_tolerance(y_ref: np.ndarray, K: int) -> np.ndarray:
     return (2.0 ** -8 + (K / 2 + 4) * 2.0 ** -24) * np.abs(y_ref) + 2.0 ** -133
 
 
+# ------------------------------------------------------- 128 x 4 scale tiles
+
+def scales_to_128x4(s: np.ndarray) -> np.ndarray:
+    """Row-major scale bytes [M, KB] (KB % 4 == 0) laid out in 128 x 4 tiles
+    (the F8_128x4 activation scales the [mxfp8] page's low-latency GEMM
+    reads; the pages do not print the layout): rows are padded to a multiple
+    of 128 and scale columns taken 4 at a time; tiles run along the columns
+    first, 512 bytes each; inside a tile, row r and column c sit at byte
+    (r % 32) * 16 + (r // 32) * 4 + c.  Padding bytes are 0.  Returns the
+    flat uint8 buffer.  Written as plain loops over the definition."""
+    s = np.asarray(s, dtype=np.uint8)
+    M, KB = s.shape
+    if KB % 4:
+        raise ValueError("the scale column count must be a multiple of 4")
+    row_tiles, col_tiles = (M + 127) // 128, KB // 4
+    out = np.zeros(row_tiles * col_tiles * 512, dtype=np.uint8)
+    for m in range(M):
+        for b in range(KB):
+            tile = (m // 128) * col_tiles + b // 4
+            r, c = m % 128, b % 4
+            out[tile * 512 + (r % 32) * 16 + (r // 32) * 4 + c] = s[m, b]
+    return out
+
+
 # ------------------------------------------------------------ compositions
 
 def linear_bf16(x_bf16: np.ndarray, w_q: np.ndarray, w_s: np.ndarray):

@@ -11,6 +11,9 @@ definition of the decode projections):
     once to BF16;
   * outlier variant: a Bernoulli(0.01) mask, drawn after x and W, multiplies
     the matching x entries by 100 in FP32 before the BF16 rounding;
+  * RMSNorm + requantize: rows x ~ N(0, 1) (optionally the leading K columns
+    of wider rows, as the chain's A output), a per-column gain
+    w = 1 + 0.1 * N(0, 1), eps = 1e-6 (the pages give none of these);
   * WO-A: attention output o ~ N(0, 1) of shape [M, 64 heads, 512], positions
     uniform in [0, 65536), and the rotary table cos/sin(pos * 10000^(-2i/64))
     for i = 0..31, computed in fp64 and rounded to FP32 (an input table, like
@@ -57,6 +60,22 @@ def gemm_case(M: int, N: int, K: int, seed: int = 0, outliers: bool = False):
         mask = torch.rand(M, K, generator=g) < 0.01
         x = torch.where(mask, x * 100.0, x)
     return {"x": x.to(torch.bfloat16), "w": w.to(torch.bfloat16)}
+
+
+RMSNORM_EPS = 1e-6
+
+
+def rmsnorm_case(M: int, K: int, seed: int = 0, ld: int | None = None, outliers: bool = False):
+    """x [M, ld] (the leading K columns are normalised) and gain w [K] in BF16;
+    draw order x, w, then the outlier mask (x100 on 1 % of x's entries)."""
+    ld = K if ld is None else ld
+    g = _gen(seed)
+    x = _normal(g, (M, ld), 1.0)
+    w = 1.0 + _normal(g, (K,), 0.1)
+    if outliers:
+        mask = torch.rand(M, ld, generator=g) < 0.01
+        x = torch.where(mask, x * 100.0, x)
+    return {"x": x.to(torch.bfloat16), "w": w.to(torch.bfloat16), "eps": RMSNORM_EPS}
 
 
 CHAIN_DIMS = {"A": (2048, 5120), "B": (8192, 1536), "C": (5120, 8192)}

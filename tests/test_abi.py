@@ -207,3 +207,30 @@ def test_wo_a_workspace_size(lib):
     without = lib.mxg_wo_a_workspace_bytes(ctypes.byref(p))
     assert with_z >= 65536 + 4 * 32768 + 4 * 1024
     assert without >= with_z + 2 * 4 * 8192
+
+
+def rmsnorm(lib, x=P(0), M=4, K=1536, ld_x=2048, w=P(1), eps=1e-6, y=P(2), ld_y=1536, q=P(3),
+            s=P(4), layout=0):
+    return lib.mxfp8_rmsnorm_quantize(x, M, K, ld_x, w, eps, y, ld_y, q, s, layout, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(w=None), 1), (dict(q=None), 1), (dict(s=None), 1),
+    (dict(M=0), 3), (dict(M=65536), 3), (dict(K=96, ld_x=96), 3), (dict(K=1600), 3),
+    (dict(K=16384 + 128, ld_x=20000), 3), (dict(ld_x=1024), 3), (dict(ld_y=1024), 3),
+    (dict(eps=-1.0), 3), (dict(eps=float("nan")), 3), (dict(eps=float("inf")), 3),
+    (dict(layout=2), 3), (dict(layout=-1), 3),
+    (dict(x=ctypes.c_void_p(A + 2)), 2), (dict(w=ctypes.c_void_p(A + 8)), 2),
+    (dict(q=ctypes.c_void_p(A + 4)), 2), (dict(y=ctypes.c_void_p(A + 2)), 2),
+    (dict(ld_x=2052), 2), (dict(ld_y=1540), 2),
+])
+def test_rmsnorm_quantize_rejects(lib, kw, status):
+    assert rmsnorm(lib, **kw) == status
+
+
+def test_scale_bytes_128x4(lib):
+    # ceil(M/128)*128 rows times K/32 scale columns (K a multiple of 128)
+    assert lib.mxg_scale_bytes_128x4(1, 5120) == 128 * 160
+    assert lib.mxg_scale_bytes_128x4(128, 1536) == 128 * 48
+    assert lib.mxg_scale_bytes_128x4(129, 1536) == 256 * 48
+    assert lib.mxg_scale_bytes_128x4(0, 1536) == 0

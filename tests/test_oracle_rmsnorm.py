@@ -134,3 +134,37 @@ def test_planted_mistakes_are_caught():
              xv[k] / np.sqrt(np.mean(xv ** 2) + eps) * 0.5]
     for v in wrong:
         assert v != pytest.approx(val, rel=1e-6)
+
+
+# ---------------------------------------------------- 128 x 4 scale tiles
+# Parity unpinned against the real F8_128x4 producers (the pages name the
+# layout but do not print it); these pin the oracle's permutation to its own
+# stated structure: a tile holds exactly a 128-row x 4-column block, each
+# 16-byte line holds one row of each 32-row quarter, nothing is lost.
+
+def test_128x4_is_a_permutation_into_padded_tiles():
+    rng = np.random.default_rng(3)
+    for M, KB in ((1, 4), (5, 48), (48, 160), (130, 8)):
+        s = rng.integers(1, 256, (M, KB)).astype(np.uint8)
+        out = oracle.scales_to_128x4(s)
+        assert out.size == ((M + 127) // 128) * 128 * KB
+        assert np.count_nonzero(out) == M * KB          # every byte placed once
+        assert sorted(out[out != 0].tolist()) == sorted(s.ravel().tolist())
+
+
+def test_128x4_tile_contents():
+    M, KB = 130, 8
+    m_idx, b_idx = np.meshgrid(np.arange(M), np.arange(KB), indexing="ij")
+    # each byte names its (row, column) modulo 255, never 0
+    lo = oracle.scales_to_128x4(((m_idx * KB + b_idx) % 255 + 1).astype(np.uint8))
+    tiles = lo.reshape(-1, 512)
+    assert tiles.shape[0] == 2 * (KB // 4)
+    # tile 1 is rows 0..127, columns 4..7; its line 5 holds rows 5, 37, 69, 101
+    line = tiles[1][5 * 16:(5 + 1) * 16].reshape(4, 4)
+    for q in range(4):
+        m = 5 + 32 * q
+        assert list(line[q]) == [(m * KB + b) % 255 + 1 for b in range(4, 8)]
+    # the third row tile (rows 128, 129) starts at tile index 2 (columns 0..3)
+    assert list(tiles[2][0:4]) == [(128 * KB + b) % 255 + 1 for b in range(4)]
+    assert list(tiles[2][16:20]) == [(129 * KB + b) % 255 + 1 for b in range(4)]
+    assert not tiles[2][32:].any()                      # padding rows 130..255
