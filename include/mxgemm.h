@@ -246,6 +246,14 @@ typedef struct {
  * wB.K % 128 == 0.  out_a/out_b/out_c are BF16 [M, N] row-major, b_q/b_s
  * [M, wB.K] / [M, wB.K/32] (written).  The workspace rules of mxfp8_gemm
  * apply, with mxg_chain_workspace_bytes() as the size.
+ *
+ * Optional norm ([step] page: _split_qkv_and_norm normalises those leading
+ * columns before wq_b): with norm_weight non-NULL (BF16 [wB.K], 16-byte
+ * aligned; norm_eps >= 0), out_a[:, 0:wB.K] is RMS-normalised as
+ * mxfp8_rmsnorm_quantize does and the BF16 result is what is requantized;
+ * it is also written to b_bf16 ([M, wB.K] BF16) when that is non-NULL.
+ * This takes one more launch between A and B (on either path selection,
+ * the three-launch form runs).  norm_weight NULL: the plain requantize.
  */
 typedef struct {
   int64_t M;
@@ -258,6 +266,9 @@ typedef struct {
   uint16_t *out_c;
   void *workspace;
   size_t workspace_bytes;
+  const uint16_t *norm_weight; /* optional RMSNorm gain [wB.K] (NULL: none)  */
+  float norm_eps;
+  uint16_t *b_bf16;            /* optional: the normalised BF16 [M, wB.K]  */
 } mxg_chain;
 
 int mxfp8_proj_chain(const mxg_chain *chain, void *stream);

@@ -36,7 +36,9 @@ class MxgChain(ctypes.Structure):
                 ("out_b", ctypes.c_void_p),
                 ("c_q", ctypes.c_void_p), ("c_s", ctypes.c_void_p),
                 ("out_c", ctypes.c_void_p),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
+                ("b_bf16", ctypes.c_void_p)]
 
 
 class MxgWoA(ctypes.Structure):
@@ -298,10 +300,13 @@ def _w(w: PackedWeight) -> MxgWeight:
 
 def mxfp8_proj_chain(a_q: torch.Tensor, a_s: torch.Tensor, wA: PackedWeight, wB: PackedWeight,
                      c_q: torch.Tensor, c_s: torch.Tensor, wC: PackedWeight, outs=None,
-                     workspace: torch.Tensor | None = None, stream=None):
-    """Three projections in one launch: A on (a_q, a_s); the leading wB.K
-    columns of A's output requantized to MXFP8 as B's input; C on (c_q, c_s).
-    Returns (out_a, b_q, b_s, out_b, out_c)."""
+                     workspace: torch.Tensor | None = None, norm_weight: torch.Tensor | None = None,
+                     norm_eps: float = 0.0, b_bf16: torch.Tensor | None = None, stream=None):
+    """Three projections back to back: A on (a_q, a_s); the leading wB.K
+    columns of A's output (RMS-normalised with norm_weight / norm_eps when
+    given, the normalised BF16 copied to b_bf16 when given) requantized to
+    MXFP8 as B's input; C on (c_q, c_s).  Returns (out_a, b_q, b_s, out_b,
+    out_c)."""
     M = a_q.shape[0]
     dev = a_q.device
     _expect(a_q, torch.uint8, "a_q", (M, wA.K))
@@ -320,9 +325,15 @@ def mxfp8_proj_chain(a_q: torch.Tensor, a_s: torch.Tensor, wA: PackedWeight, wB:
     _expect(b_s, torch.uint8, "b_s", (M, wB.K // 32))
     _expect(out_b, torch.bfloat16, "out_b", (M, wB.N))
     _expect(out_c, torch.bfloat16, "out_c", (M, wC.N))
+    if norm_weight is not None:
+        _expect(norm_weight, torch.bfloat16, "norm_weight", (wB.K,))
+    if b_bf16 is not None:
+        _expect(b_bf16, torch.bfloat16, "b_bf16", (M, wB.K))
     c = MxgChain(M, a_q.data_ptr(), a_s.data_ptr(), _w(wA), _w(wB), _w(wC), out_a.data_ptr(),
                  b_q.data_ptr(), b_s.data_ptr(), out_b.data_ptr(), c_q.data_ptr(), c_s.data_ptr(),
-                 out_c.data_ptr(), None, 0)
+                 out_c.data_ptr(), None, 0,
+                 norm_weight.data_ptr() if norm_weight is not None else None, float(norm_eps),
+                 b_bf16.data_ptr() if b_bf16 is not None else None)
     need = int(lib().mxg_chain_workspace_bytes(ctypes.byref(c)))
     if workspace is None:
         workspace = get_workspace(dev, need)

@@ -102,6 +102,9 @@ int validate_chain(const mxg_chain* c, size_t need) {
                         c->out_a, c->b_q, c->b_s, c->out_b, c->c_q, c->c_s, c->out_c};
   for (const void* p : ptrs)
     if (!aligned16(p)) return MXG_ERR_ALIGN;
+  if (c->norm_weight && (!(c->norm_eps >= 0.f) || c->norm_eps > 3.0e38f)) return MXG_ERR_SHAPE;
+  if ((c->norm_weight && !aligned16(c->norm_weight)) || (c->b_bf16 && !aligned16(c->b_bf16)))
+    return MXG_ERR_ALIGN;
   if (!c->workspace || c->workspace_bytes < need) return MXG_ERR_WORKSPACE;
   if (!aligned16(c->workspace)) return MXG_ERR_ALIGN;
   return MXG_OK;
@@ -185,6 +188,15 @@ int chain_direct(const mxg_chain& c, hipStream_t stream) {
   hipError_t e = mxg::launch_gemm(a, stream);
   if (e != hipSuccess) return MXG_ERR_DEVICE;
   GemmArgs b{c.out_a, c.wA.N, c.b_q, c.b_s, c.wB.q, c.wB.s, c.out_b, M, (int)c.wB.N, (int)c.wB.K};
+  if (c.norm_weight) {
+    // RMSNorm + requantize of A's leading columns by their own launch; B
+    // then reads the MXFP8 codes.
+    e = mxg::launch_rmsnorm_quantize(c.out_a, M, c.wB.K, c.wA.N, c.norm_weight, c.norm_eps,
+                                     c.b_bf16, c.wB.K, c.b_q, c.b_s, 0, stream);
+    if (e != hipSuccess) return MXG_ERR_DEVICE;
+    b.x = nullptr;
+    b.ld_x = 0;
+  }
   set_ksplit(b, c.workspace, mxg::kGemmPartOffset);
   if ((e = mxg::launch_gemm(b, stream)) != hipSuccess) return MXG_ERR_DEVICE;
   GemmArgs cc{nullptr, 0, const_cast<uint8_t*>(c.c_q), const_cast<uint8_t*>(c.c_s), c.wC.q,
@@ -478,7 +490,7 @@ int mxfp8_proj_chain(const mxg_chain* c, void* stream) {
   int st = validate_chain(c, mxg_chain_workspace_bytes(c));
   if (st != MXG_OK) return st;
   if ((st = check_device()) != MXG_OK) return st;
-  if (!chain_on_stage_kernel()) return chain_direct(*c, (hipStream_t)stream);
+  if (!chain_on_stage_kernel() || c->norm_weight) return chain_direct(*c, (hipStream_t)stream);
   const int G = mxg::stage_grid();
   if (G <= 0) return MXG_ERR_DEVICE;
   mxg::ProgramBuilder pb = chain_program(*c, G);

@@ -326,18 +326,23 @@ class ChainResult:
         self.A, self.b_q, self.b_s, self.B, self.C = A, b_q, b_s, B, C
 
 
-def chain(a_q, a_s, wA, b_cols: int, wB, c_q, c_s, wC) -> ChainResult:
+def chain(a_q, a_s, wA, b_cols: int, wB, c_q, c_s, wC, norm=None) -> ChainResult:
     """Back-to-back projections in the decode step's order ([step]
     AttentionStep.run: fused_wqa_wkv on the MXFP8 layer input, its leading
     columns requantized to MXFP8 for wq_b, and wo_b on its own MXFP8 input).
 
-    A = gemm(a, wA) -> BF16; B's input = quantize(A.bf16[:, :b_cols]);
-    B = gemm(that, wB); C = gemm(c, wC) on C's own (fresh) MXFP8 input.
-    Reading: the pages' split + norm of A's output is not part of this chain;
-    the requantize is plain.  ``wX`` are (codes, scales) pairs.
+    A = gemm(a, wA) -> BF16; B's input = quantize(A.bf16[:, :b_cols]), or with
+    ``norm = (gain BF16 bits [b_cols], eps)`` the quantize of the BF16
+    RMSNorm of those columns (_split_qkv_and_norm); B = gemm(that, wB);
+    C = gemm(c, wC) on C's own (fresh) MXFP8 input.  ``wX`` are (codes,
+    scales) pairs.
     """
     A = gemm(a_q, a_s, *wA)
-    b_q, b_s = quantize(np.ascontiguousarray(A.bf16[:, :b_cols]))
+    lead = np.ascontiguousarray(A.bf16[:, :b_cols])
+    if norm is None:
+        b_q, b_s = quantize(lead)
+    else:
+        _, _, b_q, b_s = rmsnorm_quantize(lead, norm[0], norm[1])
     B = gemm(b_q, b_s, *wB)
     C = gemm(c_q, c_s, *wC)
     return ChainResult(A, b_q, b_s, B, C)

@@ -133,6 +133,16 @@ def test_chain_rejects_before_launch(lib):
     bad = mx.MxgChain.from_buffer_copy(c)
     bad.a_q = A + 8
     assert lib.mxfp8_proj_chain(ctypes.byref(bad), None) == 2
+    # the optional norm: a negative or non-finite eps, misaligned gain or copy
+    for field, value, status in (("norm_eps", -1.0, 3), ("norm_eps", float("nan"), 3),
+                                 ("norm_eps", float("inf"), 3), ("norm_weight", A + 2, 2)):
+        bad = mx.MxgChain.from_buffer_copy(c)
+        bad.norm_weight = A * 16
+        setattr(bad, field, value)
+        assert lib.mxfp8_proj_chain(ctypes.byref(bad), None) == status, field
+    bad = mx.MxgChain.from_buffer_copy(c)
+    bad.norm_weight, bad.b_bf16 = A * 16, A + 4
+    assert lib.mxfp8_proj_chain(ctypes.byref(bad), None) == 2
 
 
 def test_struct_layouts_match_the_header(tmp_path):

@@ -121,3 +121,50 @@ def test_chain_rejects_bad_shapes():
                                   torch.empty(2, 3, dtype=torch.uint8, device="cuda"),
                                   torch.empty(2, 384, dtype=torch.bfloat16, device="cuda"),
                                   torch.empty(2, 320, dtype=torch.bfloat16, device="cuda")))
+
+
+def run_chain_norm(M, dims=None, seed=0):
+    """The chain with the RMSNorm of A's leading columns before the
+    requantize: every stage is checked on the GPU's own input to it, and B
+    end to end on rows whose codes match the oracle's."""
+    case = synth.chain_case(M, seed=seed, dims=dims)
+    d = case["dims"]
+    b_cols = d["B"][1]
+    nc = synth.rmsnorm_case(1, b_cols, seed=seed + 1)
+    w_bits, eps = synth.bits(nc["w"]), nc["eps"]
+    g, o = _prep(case)
+    ref = oracle.chain(*o["x_a"], o["w_a"], b_cols, o["w_b"], *o["x_c"], o["w_c"],
+                       norm=(w_bits, eps))
+    say(f"chain+norm M={M} dims={d} seed={seed}")
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    b_bf16 = torch.empty(M, b_cols, dtype=torch.bfloat16, device="cuda")
+    out_a, b_q, b_s, out_b, out_c = mx.mxfp8_proj_chain(
+        *g["x_a"], g["w_a"], g["w_b"], *g["x_c"], g["w_c"], workspace=ws,
+        norm_weight=dev_bf16(w_bits), norm_eps=eps, b_bf16=b_bf16)
+    torch.cuda.synchronize()
+    check_gemm(out_a, ref.A, "A")
+    check_gemm(out_c, ref.C, "C")
+    lead = np.ascontiguousarray(host_bits(out_a)[:, :b_cols])
+    yref = oracle.rmsnorm(lead, w_bits, eps)
+    yb = host_bits(b_bf16)
+    assert np.all(np.abs(oracle.bf16_value(yb) - yref) <= oracle.rmsnorm_tolerance(yref, b_cols))
+    vq, vs = oracle.quantize(yb)
+    gq, gs = host_u8(b_q), host_u8(b_s)
+    assert np.array_equal(gq, vq) and np.array_equal(gs, vs), "requant must quantize the norm"
+    check_gemm(out_b, oracle.gemm(gq, gs, o["w_b"][0], o["w_b"][1]), "B (stage-wise)")
+    same = np.all(gq == ref.b_q, axis=1) & np.all(gs == ref.b_s, axis=1)
+    if same.any():
+        got = oracle.bf16_value(host_bits(out_b)[same])
+        assert np.all(np.abs(got - ref.B.ref[same]) <= ref.B.tolerance()[same])
+    assert 1.0 - np.mean(gq == ref.b_q) < 0.02
+
+
+@pytest.mark.parametrize("M", [1, 17, 48])
+def test_chain_with_norm_small(M, chain_path):
+    # with a norm the three-launch form runs on either path selection
+    run_chain_norm(M, dims=SMALL, seed=M)
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_chain_with_norm_full_size(M):
+    run_chain_norm(M)
