@@ -194,10 +194,12 @@ def stream_ceiling(dev, stream, reps: int = 600):
     return {"us": us, "bytes": b, "GBs": b / (us * 1e-6) / 1e9}
 
 
-def chain_case(dev, stream, M: int, reps: int = 200):
+def chain_case(dev, stream, M: int, reps: int = 200, norm: bool = False):
     """The three-projection chain (A 2048x5120, requantize 1536 columns, B
     8192x1536, C 5120x8192), weights rotated over copies; the library's
-    default chain path unless MXG_CHAIN_PATH says otherwise."""
+    default chain path unless MXG_CHAIN_PATH says otherwise.  norm: the
+    1536 columns are RMS-normalised before the requantize (one more launch;
+    the gain's 3 KB and the normalised BF16 are counted)."""
     case = synth.chain_case(M, seed=0)
     w = {k: mx.PackedWeight.from_bf16(case[k].to(dev)) for k in ("w_a", "w_b", "w_c")}
     per = sum(mx_bytes(v.N, v.K) for v in w.values())
@@ -211,18 +213,40 @@ def chain_case(dev, stream, M: int, reps: int = 200):
             torch.empty(M, 8192, dtype=torch.bfloat16, device=dev),
             torch.empty(M, 5120, dtype=torch.bfloat16, device=dev))
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
+    gain = synth.rmsnorm_case(1, 1536, seed=1)["w"].to(dev) if norm else None
 
     def call(i):
         cw = cop[i % n]
-        mx.mxfp8_proj_chain(*a, cw["w_a"], cw["w_b"], *c, cw["w_c"], outs=outs, workspace=ws)
+        mx.mxfp8_proj_chain(*a, cw["w_a"], cw["w_b"], *c, cw["w_c"], outs=outs, workspace=ws,
+                            norm_weight=gain, norm_eps=synth.RMSNORM_EPS)
     with torch.cuda.stream(stream):
         for i in range(10):
             call(i)
     us = time_graph(call, reps, stream) * 1e3 / reps
     b = per + mx_bytes(M, 5120) + mx_bytes(M, 8192) + 2 * M * (2048 + 8192 + 5120) \
-        + 2 * M * 1536 + mx_bytes(M, 1536)
+        + 2 * M * 1536 + mx_bytes(M, 1536) + (2 * 1536 if norm else 0)
     return {"us": round(us, 3), "GBs": round(b / (us * 1e-6) / 1e9, 1),
             "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def rmsnorm_case(dev, stream, M: int, K: int, ld: int, reps: int = 400):
+    """RMSNorm + MXFP8 of the leading K columns of BF16 rows of stride ld
+    (the chain's 1536 of 2048, or a 5120-wide layer input), writing the
+    normalised BF16 too.  A few KB per row: launch-bound, reported in us."""
+    case = synth.rmsnorm_case(M, K, seed=0, ld=ld)
+    x, w = case["x"].to(dev), case["w"].to(dev)
+    y = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    q = torch.empty(M, K, dtype=torch.uint8, device=dev)
+    s = torch.empty(M, K // 32, dtype=torch.uint8, device=dev)
+
+    def call(i):
+        mx.mxfp8_rmsnorm_quantize(x, w, case["eps"], K=K, y=y, q=q, s=s)
+    with torch.cuda.stream(stream):
+        for i in range(10):
+            call(i)
+    us = time_graph(call, reps, stream) * 1e3 / reps
+    b = 2 * M * K + 2 * K + 2 * M * K + mx_bytes(M, K)
+    return {"us": round(us, 3), "GBs": round(b / (us * 1e-6) / 1e9, 1)}
 
 
 def extra_cases(dev, stream):
@@ -259,6 +283,11 @@ def extra_cases(dev, stream):
             out[f"chain M{M} (one stage-kernel launch)"] = chain_case(dev, stream, M)
     finally:
         del os.environ["MXG_CHAIN_PATH"]
+    for M in (1, 8, 32):
+        out[f"chain+norm M{M}"] = chain_case(dev, stream, M, norm=True)
+    for M in (1, 8, 48):
+        for K, ld in ((1536, 2048), (5120, 5120)):
+            out[f"rmsnorm+quantize M{M} K{K}"] = rmsnorm_case(dev, stream, M, K, ld)
     for M in (1, 4, 16):
         out[f"wo_a+wo_b M{M}"] = wo_a_case(dev, stream, M)
     os.environ["MXG_WOA_PATH"] = "stage"
