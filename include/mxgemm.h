@@ -214,6 +214,24 @@ int mxfp8_gemm(int64_t M, int64_t N, int64_t K, const uint16_t *x_bf16,
 size_t mxg_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
+ * mxfp8_gemm_ex -- mxfp8_gemm on MXFP8 activations whose scale bytes come in
+ * the given layout ([mxfp8] module text: the low-latency and cute-dsl
+ * backends read the same F8_128x4 activation scales), so a tensor written by
+ * mxfp8_rmsnorm_quantize with MXG_SCALES_128X4, or by another producer of
+ * that layout, needs no repack.
+ *   a_s              MXG_SCALES_ROW_MAJOR: [M, K/32], exactly as mxfp8_gemm;
+ *                    MXG_SCALES_128X4: mxg_scale_bytes_128x4(M, K) bytes in
+ *                    128 x 4 tiles (offsets as in mxfp8_rmsnorm_quantize)
+ *   other arguments  as mxfp8_gemm with x_bf16 = NULL (a_q is [M, K])
+ * With MXG_SCALES_ROW_MAJOR this is mxfp8_gemm.  With MXG_SCALES_128X4 the
+ * direct kernels always serve the call, and the result equals mxfp8_gemm's
+ * on the same scales in row-major order, bit for bit.  Status as above.
+ */
+int mxfp8_gemm_ex(int64_t M, int64_t N, int64_t K, const uint8_t *a_q, const uint8_t *a_s,
+                  int32_t a_scale_layout, const uint8_t *w_q, const uint8_t *w_s, uint16_t *out,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * A packed MXFP8 weight (mxfp8_pack_weights order) and its shape [N, K].
  */
 typedef struct {

@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.mxfp8_pack_weights.restype = ctypes.c_int
         L.mxfp8_gemm.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
         L.mxfp8_gemm.restype = ctypes.c_int
+        L.mxfp8_gemm_ex.argtypes = [i64, i64, i64, vp, vp, ctypes.c_int32, vp, vp, vp, vp, sz, vp]
+        L.mxfp8_gemm_ex.restype = ctypes.c_int
         L.mxg_gemm_workspace_bytes.argtypes = [i64, i64, i64]
         L.mxg_gemm_workspace_bytes.restype = sz
         L.mxfp8_proj_chain.argtypes = [ctypes.POINTER(MxgChain), vp]
@@ -291,6 +293,35 @@ def mxfp8_gemm(a_q: torch.Tensor, a_s: torch.Tensor, w: PackedWeight,
     wsz = workspace.numel() * workspace.element_size()
     _check(lib().mxfp8_gemm(M, N, K, _ptr(x), ld_x, _ptr(a_q), _ptr(a_s), _ptr(w.q), _ptr(w.s),
                             _ptr(out), _ptr(workspace), wsz, _stream(stream)))
+    return out
+
+
+def mxfp8_gemm_ex(a_q: torch.Tensor, a_s: torch.Tensor, w: PackedWeight, a_scale_layout: int,
+                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+    """mxfp8_gemm on MXFP8 activations a_q [M, K] whose scales a_s are
+    row-major [M, K/32] (SCALES_ROW_MAJOR) or a flat buffer of
+    scale_bytes_128x4(M, K) bytes in 128 x 4 tiles (SCALES_128X4)."""
+    M, K = a_q.shape
+    N = w.N
+    if w.K != K:
+        raise ValueError(f"weight K {w.K} != activation K {K}")
+    _expect(a_q, torch.uint8, "a_q", (M, K))
+    if a_scale_layout == SCALES_128X4:
+        _expect(a_s, torch.uint8, "a_s")
+        if a_s.numel() < scale_bytes_128x4(M, K):
+            raise ValueError("a_s holds fewer than scale_bytes_128x4(M, K) bytes")
+    else:
+        _expect(a_s, torch.uint8, "a_s", (M, K // 32))
+    if out is None:
+        out = torch.empty(M, N, dtype=torch.bfloat16, device=a_q.device)
+    _expect(out, torch.bfloat16, "out", (M, N))
+    ws_bytes = int(lib().mxg_gemm_workspace_bytes(M, N, K))
+    if workspace is None:
+        workspace = get_workspace(a_q.device, ws_bytes)
+    wsz = workspace.numel() * workspace.element_size()
+    _check(lib().mxfp8_gemm_ex(M, N, K, _ptr(a_q), _ptr(a_s), int(a_scale_layout), _ptr(w.q),
+                               _ptr(w.s), _ptr(out), _ptr(workspace), wsz, _stream(stream)))
     return out
 
 

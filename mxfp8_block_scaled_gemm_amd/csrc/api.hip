@@ -485,6 +485,24 @@ int mxfp8_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* x_bf16, int64_t 
   return launched(mxg::launch_gemm(a, (hipStream_t)stream));
 }
 
+int mxfp8_gemm_ex(int64_t M, int64_t N, int64_t K, const uint8_t* a_q, const uint8_t* a_s,
+                  int32_t a_scale_layout, const uint8_t* w_q, const uint8_t* w_s, uint16_t* out,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (a_scale_layout == MXG_SCALES_ROW_MAJOR)
+    return mxfp8_gemm(M, N, K, nullptr, 0, const_cast<uint8_t*>(a_q), const_cast<uint8_t*>(a_s),
+                      w_q, w_s, out, workspace, workspace_bytes, stream);
+  if (a_scale_layout != MXG_SCALES_128X4) return MXG_ERR_SHAPE;
+  int st = validate_gemm(M, N, K, nullptr, 0, a_q, a_s, w_q, w_s, out, workspace_bytes,
+                         workspace);
+  if (st != MXG_OK) return st;
+  if ((st = check_device()) != MXG_OK) return st;
+  GemmArgs a{nullptr, 0, const_cast<uint8_t*>(a_q), const_cast<uint8_t*>(a_s), w_q, w_s, out,
+             (int)M, (int)N, (int)K};
+  a.a_sf128 = true;
+  set_ksplit(a, workspace, mxg::kGemmPartOffset);
+  return launched(mxg::launch_gemm(a, (hipStream_t)stream));
+}
+
 int mxfp8_proj_chain(const mxg_chain* c, void* stream) {
   if (!c) return MXG_ERR_NULL;
   int st = validate_chain(c, mxg_chain_workspace_bytes(c));

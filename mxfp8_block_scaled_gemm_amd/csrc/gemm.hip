@@ -50,6 +50,13 @@ __device__ __forceinline__ int xcd_tile(int b, int tiles) {
   return 4 * (xcd + 8 * (k >> 2)) + (k & 3);
 }
 
+// Byte offset of the dword holding the scales of blocks [4 q, 4 q + 4) of
+// activation row m: row-major at row stride ldas, or (sf128) in 128 x 4
+// tiles, where those four bytes are contiguous at tile q (rows < 128 here).
+__device__ __forceinline__ int act_scale_dword(int m, int q, int ldas, bool sf128) {
+  return sf128 ? q * 512 + (m & 31) * 16 + (m >> 5) * 4 : m * ldas + 4 * q;
+}
+
 // Quantize one whole 32-element BF16 block held by this lane (4 x 16 bytes)
 // to its 32 E4M3 codes (2 x 16 bytes) and its exponent.  One lane per block
 // keeps the per-block work (amax, exponent, scale) to one copy, where lanes
@@ -114,14 +121,15 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
       const int row = c / cpr, col = (c - row * cpr) * 16;
       st[i] = buf_ld16(ra, c >= 0 ? (uint32_t)(row * lda + col) : kOutOfRange);
     }
-    const auto rs = make_rsrc(p.a_s + (grp >> 5), (uint32_t)((M - 1) * ldas + KB));
+    const auto rs = make_rsrc(p.a_s + (grp >> 5),
+                              (uint32_t)(p.a_sf128 ? 128 * KB : (M - 1) * ldas + KB));
     const int nsc = (M * KB) >> 2, spr = KB >> 2;
 #pragma unroll
     for (int i = 0; i < SCR; ++i) {
       const int c = tid + i * kThreads;
       const int row = c / spr, col = (c - row * spr) * 4;
       sc[i] = __builtin_amdgcn_raw_buffer_load_b32(
-          rs, c < nsc ? row * ldas + col : (int)kOutOfRange, 0, 0);
+          rs, c < nsc ? act_scale_dword(row, col >> 2, ldas, p.a_sf128) : (int)kOutOfRange, 0, 0);
     }
   } else {
     const auto rx = make_rsrc(p.x, (uint32_t)(((M - 1) * p.ld_x + K) * 2));
@@ -285,7 +293,8 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p) {
   const int64_t grp = p.group_tiles ? (int64_t)(tg * T / p.group_tiles) * p.a_group : 0;
   const int lda = (int)p.lda, ldas = lda >> 5;
   const auto ra = make_rsrc(p.a_q + grp, (uint32_t)((M - 1) * lda + K));
-  const auto rs = make_rsrc(p.a_s + (grp >> 5), (uint32_t)((M - 1) * ldas + (K >> 5)));
+  const auto rs = make_rsrc(p.a_s + (grp >> 5),
+                            (uint32_t)(p.a_sf128 ? 128 * (K >> 5) : (M - 1) * ldas + (K >> 5)));
   // Chunk c: steps [k0 + 16c, k0 + 16c + 16) within the part.
   auto stage_load = [&](int c, v4i (&st)[CHL], uint32_t& sc) {
     const int nsc_steps = min(16, ns - 16 * c);
@@ -300,7 +309,8 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p) {
     const int nsc = M * nsc_steps;
     const int row = tid / nsc_steps, cd = tid - row * nsc_steps;
     sc = __builtin_amdgcn_raw_buffer_load_b32(
-        rs, tid < nsc ? row * ldas + (k0 + 16 * c + cd) * 4 : (int)kOutOfRange, 0, 0);
+        rs, tid < nsc ? act_scale_dword(row, k0 + 16 * c + cd, ldas, p.a_sf128) : (int)kOutOfRange,
+        0, 0);
   };
   auto stage_park = [&](int c, const v4i (&st)[CHL], uint32_t sc) {
     const int nsc_steps = min(16, ns - 16 * c);
@@ -790,6 +800,8 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
   if (a.lda == 0) a.lda = a.K;
   const bool fq = a.x != nullptr;
   if (fq && (a.group_tiles != 0 || a.lda != a.K)) return hipErrorInvalidValue;
+  if (a.a_sf128 && (fq || a.group_tiles != 0 || a.lda != a.K || a.M > 128))
+    return hipErrorInvalidValue;
   const int S = a.K / 128;
   const Plan pl = choose_plan(a.M, a.N, a.K, a.group_tiles, device_cus());
   // One full-K tile per workgroup with the whole activation in LDS unless

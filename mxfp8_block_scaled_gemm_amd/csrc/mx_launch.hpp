@@ -29,6 +29,9 @@ struct GemmArgs {
   uint32_t* ctr = nullptr;
   float* part = nullptr;
   int P = 1, Sp = 0;     // K split of the 2D kernel (set by the launcher)
+  // Activation scales in 128 x 4 tiles instead of row-major (MXFP8 input,
+  // no grouping, lda == K).
+  bool a_sf128 = false;
 };
 
 // Bytes of FP32 partials the GEMM of this shape needs (0: no K split); the

@@ -244,3 +244,19 @@ def test_scale_bytes_128x4(lib):
     assert lib.mxg_scale_bytes_128x4(128, 1536) == 128 * 48
     assert lib.mxg_scale_bytes_128x4(129, 1536) == 256 * 48
     assert lib.mxg_scale_bytes_128x4(0, 1536) == 0
+
+
+def gemm_ex(lib, M=4, N=1024, K=2048, a_q=P(1), a_s=P(2), layout=1, w_q=P(3), w_s=P(4),
+            out=P(5), ws=P(7), ws_bytes=1 << 30):
+    return lib.mxfp8_gemm_ex(M, N, K, a_q, a_s, layout, w_q, w_s, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a_s=None), 1), (dict(a_q=None), 1), (dict(layout=0, out=None), 1),
+    (dict(layout=2), 3), (dict(layout=-1), 3), (dict(M=0), 3), (dict(M=49), 3),
+    (dict(K=1000), 3), (dict(layout=0, M=49), 3),
+    (dict(a_q=ctypes.c_void_p(A + 8)), 2), (dict(a_s=ctypes.c_void_p(A + 4)), 2),
+    (dict(ws=None), 4),
+])
+def test_gemm_ex_rejects(lib, kw, status):
+    assert gemm_ex(lib, **kw) == status

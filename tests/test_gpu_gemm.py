@@ -283,3 +283,52 @@ def test_one_row_both_wave_counts(N, K, waves, monkeypatch):
     else:
         monkeypatch.delenv("MXG_M16_WAVES", raising=False)
     run_case(1, N, K, seed=K + 7)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 256, 1024), (5, 512, 2048), (16, 256, 1024),
+                                   (17, 2064, 1664), (33, 512, 16384), (48, 4096, 5120),
+                                   (8, 5120, 8192)])
+@pytest.mark.parametrize("kernel", ["routed", "m16", "2d"])
+def test_scales_in_128x4_tiles(M, N, K, kernel, monkeypatch):
+    """Activation scales in 128 x 4 tiles (the oracle's permutation of the
+    row-major scales) give the row-major call's output bit for bit, on each
+    direct kernel, and stay within tolerance of the oracle."""
+    monkeypatch.setenv("MXG_GEMM_PATH", "direct")
+    if kernel == "routed":
+        monkeypatch.delenv("MXG_DIRECT_KERNEL", raising=False)
+    else:
+        monkeypatch.setenv("MXG_DIRECT_KERNEL", kernel)
+    case = synth.gemm_case(M, N, K, seed=M + N)
+    oa_q, oa_s = oracle.quantize(synth.bits(case["x"]))
+    ow_q, ow_s = oracle.quantize(synth.bits(case["w"]))
+    ref = oracle.gemm(oa_q, oa_s, ow_q, ow_s)
+    say(f"gemm 128x4 scales M={M} N={N} K={K} kernel={kernel}")
+    w = mx.PackedWeight.from_rows(dev_u8(ow_q), dev_u8(ow_s))
+    a_q = dev_u8(oa_q)
+    row = mx.mxfp8_gemm(a_q, dev_u8(oa_s), w)
+    tiled = mx.mxfp8_gemm_ex(a_q, dev_u8(oracle.scales_to_128x4(oa_s)), w, mx.SCALES_128X4)
+    torch.cuda.synchronize()
+    assert torch.equal(row.view(torch.int16), tiled.view(torch.int16))
+    check_gemm(tiled, ref, f"128x4 M={M}")
+
+
+@pytest.mark.parametrize("M", [1, 8, 48])
+def test_rmsnorm_128x4_output_feeds_the_gemm(M):
+    """Producer to consumer with no repack: mxfp8_rmsnorm_quantize writes
+    128 x 4 scales, mxfp8_gemm_ex reads them; equal bit for bit to the
+    row-major pair, and within tolerance of the oracle on the same codes."""
+    K, N = 1536, 8192
+    nc = synth.rmsnorm_case(M, K, seed=M)
+    x, g = nc["x"].cuda(), nc["w"].cuda()
+    ow_q, ow_s = oracle.quantize(synth.bits(synth.gemm_case(1, N, K, seed=3)["w"]))
+    w = mx.PackedWeight.from_rows(dev_u8(ow_q), dev_u8(ow_s))
+    say(f"rmsnorm 128x4 -> gemm M={M}")
+    _, q1, s1 = mx.mxfp8_rmsnorm_quantize(x, g, nc["eps"], scale_layout=mx.SCALES_128X4)
+    _, q0, s0 = mx.mxfp8_rmsnorm_quantize(x, g, nc["eps"])
+    tiled = mx.mxfp8_gemm_ex(q1, s1, w, mx.SCALES_128X4)
+    row = mx.mxfp8_gemm(q0, s0, w)
+    torch.cuda.synchronize()
+    assert torch.equal(q0, q1)
+    assert np.array_equal(host_u8(s1), oracle.scales_to_128x4(host_u8(s0)))
+    assert torch.equal(row.view(torch.int16), tiled.view(torch.int16))
+    check_gemm(tiled, oracle.gemm(host_u8(q0), host_u8(s0), ow_q, ow_s), f"norm->gemm M={M}")
