@@ -275,6 +275,27 @@ def extra_cases(dev, stream):
                                      "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         del copies
         torch.cuda.empty_cache()
+    # more than 48 rows (48-row blocks over the same weight in one launch)
+    N, K = 4096, 5120
+    copies = weight_copies(N, K, dev)
+    for M in (64, 128, 256):
+        x = synth.gemm_case(M, 16, K, seed=0)["x"].to(dev)
+        aq, as_ = mx.mxfp8_quantize(x)
+        o = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+
+        def call(i):
+            mx.mxfp8_gemm(aq, as_, copies[i % len(copies)], out=o)
+        with torch.cuda.stream(stream):
+            for i in range(20):
+                call(i)
+        us = time_graph(call, 200, stream) * 1e3 / 200
+        b = gemm_bytes(M, N, K, False)
+        out[f"rows above 48: M{M} N{N} K{K}"] = {
+            "us": round(us, 3), "GBs": round(b / (us * 1e-6) / 1e9, 1),
+            "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "TFLOPs": round(2 * M * N * K / (us * 1e-6) / 1e12, 1)}
+    del copies
+    torch.cuda.empty_cache()
     for M in (1, 8, 32):
         out[f"chain M{M}"] = chain_case(dev, stream, M)
     os.environ["MXG_CHAIN_PATH"] = "stage"

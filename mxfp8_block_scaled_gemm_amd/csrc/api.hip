@@ -70,7 +70,7 @@ int validate_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* x, int64_t ld
                   const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w_q,
                   const uint8_t* w_s, const uint16_t* out, size_t ws_bytes, const void* ws) {
   if (!a_q || !a_s || !w_q || !w_s || !out) return MXG_ERR_NULL;
-  if (M < 1 || M > MXG_MAX_ROWS || N < 16 || N % 16 != 0 || K < 128 || K % 128 != 0 ||
+  if (M < 1 || M > MXG_MAX_GEMM_ROWS || N < 16 || N % 16 != 0 || K < 128 || K % 128 != 0 ||
       N > (int64_t)1 << 24 || K > MXG_MAX_K)
     return MXG_ERR_SHAPE;
   if (N * K > ((int64_t)1 << 31) - 1) return MXG_ERR_SHAPE;
@@ -115,9 +115,9 @@ int validate_chain(const mxg_chain* c, size_t need) {
 // than the stage kernel for every single-GEMM shape; the stage kernel serves
 // the multi-stage programs.  MXG_GEMM_PATH ("stage" / "direct") forces a
 // choice (tests use it to cover both).
-bool use_stage_kernel(int, int, int, bool) {
+bool use_stage_kernel(int M, int, int, bool) {
   const char* force = std::getenv("MXG_GEMM_PATH");
-  return force && std::strcmp(force, "stage") == 0;
+  return M <= MXG_MAX_ROWS && force && std::strcmp(force, "stage") == 0;
 }
 
 mxg::ProgramBuilder gemm_program(int M, int N, int K, const uint16_t* x, int ld_x, uint8_t* a_q,
@@ -391,12 +391,12 @@ const char* mxg_strerror(int status) {
 int mxg_version(void) { return 100; }
 
 size_t mxg_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M < 1 || M > MXG_MAX_ROWS || N < 16 || N % 16 || K < 128 || K % 128 || K > MXG_MAX_K)
+  if (M < 1 || M > MXG_MAX_GEMM_ROWS || N < 16 || N % 16 || K < 128 || K % 128 || K > MXG_MAX_K)
     return mxg::kCtrBytes;
   size_t need = std::max(mxg::kCtrBytes,
                          direct_need((int)M, (int)N, (int)K, mxg::kGemmPartOffset));
   const int G = mxg::stage_grid();
-  if (G > 0) {
+  if (G > 0 && M <= MXG_MAX_ROWS) {
     mxg::ProgramBuilder pb = gemm_program((int)M, (int)N, (int)K, nullptr, 0, nullptr, nullptr,
                                           nullptr, nullptr, nullptr, nullptr, G);
     need = std::max(need, pb.workspace_bytes());

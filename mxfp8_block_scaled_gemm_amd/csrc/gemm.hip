@@ -35,6 +35,7 @@
 namespace mxg {
 
 constexpr int kM16Waves = 16;   // waves per workgroup of the GEMM kernels
+constexpr int kRowBlock = 48;   // activation rows one 2D-kernel workgroup serves
 
 __host__ __device__ constexpr int act_ld(int K) { return K + 16; }          // LDS bytes per code row
 __host__ __device__ constexpr int scale_ld(int K) { return (K >> 5) + 4; }  // LDS bytes per scale row
@@ -52,9 +53,11 @@ __device__ __forceinline__ int xcd_tile(int b, int tiles) {
 
 // Byte offset of the dword holding the scales of blocks [4 q, 4 q + 4) of
 // activation row m: row-major at row stride ldas, or (sf128) in 128 x 4
-// tiles, where those four bytes are contiguous at tile q (rows < 128 here).
-__device__ __forceinline__ int act_scale_dword(int m, int q, int ldas, bool sf128) {
-  return sf128 ? q * 512 + (m & 31) * 16 + (m >> 5) * 4 : m * ldas + 4 * q;
+// tiles (S = K/128 tiles per 128 rows), where those four bytes are
+// contiguous.  With sf128, m counts from the tensor's first row.
+__device__ __forceinline__ int act_scale_dword(int m, int q, int ldas, bool sf128, int S) {
+  return sf128 ? ((m >> 7) * S + q) * 512 + (m & 31) * 16 + ((m & 127) >> 5) * 4
+               : m * ldas + 4 * q;
 }
 
 // Quantize one whole 32-element BF16 block held by this lane (4 x 16 bytes)
@@ -129,7 +132,8 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
       const int c = tid + i * kThreads;
       const int row = c / spr, col = (c - row * spr) * 4;
       sc[i] = __builtin_amdgcn_raw_buffer_load_b32(
-          rs, c < nsc ? act_scale_dword(row, col >> 2, ldas, p.a_sf128) : (int)kOutOfRange, 0, 0);
+          rs, c < nsc ? act_scale_dword(row, col >> 2, ldas, p.a_sf128, S) : (int)kOutOfRange, 0,
+          0);
     }
   } else {
     const auto rx = make_rsrc(p.x, (uint32_t)(((M - 1) * p.ld_x + K) * 2));
@@ -264,7 +268,21 @@ typedef unsigned v4u32 __attribute__((ext_vector_type(4)));
 // go to the workspace and the last of the P workgroups of a tile group to
 // arrive adds them in part order (deterministic) and stores BF16.
 template <int MB, int T, int SPW, int NB, int CHM, bool FQ>
-__global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
+  // Row block blockIdx.y: rows [48 y, 48 y + 48) of the activations and the
+  // output, with their own K-split partials and tile counters (a GEMM of more
+  // than 48 rows is a grid of 48-row GEMMs over the same weight).
+  const int row0 = kRowBlock * (int)blockIdx.y;
+  GemmArgs p = p0;
+  p.M = min(p0.M - row0, kRowBlock);
+  p.a_q += (int64_t)row0 * p0.lda;
+  if (!p0.a_sf128) p.a_s += (int64_t)row0 * (p0.lda >> 5);
+  p.out += (int64_t)row0 * p0.N;
+  if (p0.part) p.part += (int64_t)blockIdx.y * (p0.N >> 4) * p0.P * MB * 64 * 4;
+  if (p0.ctr) p.ctr += (int64_t)blockIdx.y * ((p0.N >> 4) / T);
+  // Row index of this block's first row in the scale addressing: row-major
+  // scales were offset above; 128 x 4 tiles are addressed from the first row.
+  const int srow0 = p0.a_sf128 ? row0 : 0;
   // Registers per thread per K chunk: CHM 16-byte code chunks, or with BF16
   // input (M <= 16) one whole 32-element block per thread (64 per row).
   constexpr int CHL = FQ ? 4 : CHM;
@@ -294,7 +312,8 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p) {
   const int lda = (int)p.lda, ldas = lda >> 5;
   const auto ra = make_rsrc(p.a_q + grp, (uint32_t)((M - 1) * lda + K));
   const auto rs = make_rsrc(p.a_s + (grp >> 5),
-                            (uint32_t)(p.a_sf128 ? 128 * (K >> 5) : (M - 1) * ldas + (K >> 5)));
+                            (uint32_t)(p.a_sf128 ? ((p0.M + 127) >> 7) * 128 * (K >> 5)
+                                                 : (M - 1) * ldas + (K >> 5)));
   // Chunk c: steps [k0 + 16c, k0 + 16c + 16) within the part.
   auto stage_load = [&](int c, v4i (&st)[CHL], uint32_t& sc) {
     const int nsc_steps = min(16, ns - 16 * c);
@@ -309,7 +328,8 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p) {
     const int nsc = M * nsc_steps;
     const int row = tid / nsc_steps, cd = tid - row * nsc_steps;
     sc = __builtin_amdgcn_raw_buffer_load_b32(
-        rs, tid < nsc ? act_scale_dword(row, k0 + 16 * c + cd, ldas, p.a_sf128) : (int)kOutOfRange,
+        rs, tid < nsc ? act_scale_dword(srow0 + row, k0 + 16 * c + cd, ldas, p.a_sf128, S)
+                      : (int)kOutOfRange,
         0, 0);
   };
   auto stage_park = [&](int c, const v4i (&st)[CHL], uint32_t sc) {
@@ -627,10 +647,10 @@ int round_slots(int spw) {
 // MI355X (about 6.5 TB/s of weights streamed chip-wide; about 46 GB/s of
 // activations into one CU while every CU reads the same lines).  T = P = 1
 // also models the M <= 16 kernel (one full-K tile per workgroup).
-double plan_cost(int M, int N, int K, int T, int P, int cus) {
+double plan_cost(int M, int N, int K, int T, int P, int cus, int rb = 1) {
   const int tiles = N / 16, S = K / 128;
   const int Sp = (S + P - 1) / P;
-  const int groups = tiles / T, wgs = groups * P;
+  const int groups = tiles / T, wgs = groups * P * rb;
   const int rounds = (wgs + cus - 1) / cus;
   const int active = wgs < cus ? wgs : cus;
   const double wb = (double)T * Sp * 2112.0, ab = (double)M * Sp * 132.0;
@@ -639,6 +659,10 @@ double plan_cost(int M, int N, int K, int T, int P, int cus) {
 
 // The 2D plan of least modelled time.
 Plan choose_plan(int M, int N, int K, int group_tiles, int cus) {
+  // More than 48 rows: 48-row blocks, each with the plan's tile groups and
+  // K parts (and their own counters).
+  const int rb = (M + kRowBlock - 1) / kRowBlock;
+  if (M > kRowBlock) M = kRowBlock;
   const int tiles = N / 16, S = K / 128, MB = (M + 15) / 16;
   Plan best{0, 0, 0, 0, 1e30};
   for (int T : {1, 2, 4}) {
@@ -649,8 +673,8 @@ Plan choose_plan(int M, int N, int K, int group_tiles, int cus) {
       if ((P - 1) * Sp >= S) continue;                  // no empty part
       const int spw = round_slots((T * Sp + 15) / 16);
       if (spw == 0) continue;
-      if (P > 1 && (8192 + (size_t)(tiles / T) * 4 > 65536)) continue;
-      const double cost = plan_cost(M, N, K, T, P, cus);
+      if (P > 1 && (8192 + (size_t)rb * (tiles / T) * 4 > 65536)) continue;
+      const double cost = plan_cost(M, N, K, T, P, cus, rb);
       if (cost < best.cost) best = Plan{T, P, Sp, spw, cost};
     }
   }
@@ -679,9 +703,10 @@ hipError_t launch_2d(const GemmArgs& a, hipStream_t stream) {
   // The whole part's activations in registers (then in LDS at once) while
   // they fit beside the weight slots; otherwise chunk by chunk.
   constexpr bool kRegs = NCH * CHL * 4 + SPW * 9 + MB * 4 <= 120;
-  const size_t whole_lds = (size_t)a.M * (a.Sp * 128 + 16) + (size_t)a.M * (a.Sp * 4 + 4);
+  const int Mb = a.M < kRowBlock ? a.M : kRowBlock;      // rows of one row block
+  const size_t whole_lds = (size_t)Mb * (a.Sp * 128 + 16) + (size_t)Mb * (a.Sp * 4 + 4);
   const bool whole = kRegs && NCH > 1 && whole_lds <= 160 * 1024 - 64;
-  const int grid = (a.N / 16 / T) * a.P;
+  const dim3 grid((a.N / 16 / T) * a.P, (a.M + kRowBlock - 1) / kRowBlock);
   if (whole) {
     auto kern = gemm_2d_kernel<MB, T, SPW, (kRegs ? NCH : 1), CHM, FQ>;
     static bool configured = false;
@@ -693,9 +718,9 @@ hipError_t launch_2d(const GemmArgs& a, hipStream_t stream) {
       if (e != hipSuccess) return e;
       configured = true;
     }
-    size_t lds = gemm_2d_lds_bytes(a.M, MB);
+    size_t lds = gemm_2d_lds_bytes(Mb, MB);
     if (whole_lds > lds) lds = (whole_lds + 15) & ~(size_t)15;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kM16Waves * 64), lds, stream, a);
+    hipLaunchKernelGGL(kern, grid, dim3(kM16Waves * 64), lds, stream, a);
   } else {
     auto kern = gemm_2d_kernel<MB, T, SPW, 1, CHM, FQ>;
     static bool configured = false;
@@ -706,8 +731,7 @@ hipError_t launch_2d(const GemmArgs& a, hipStream_t stream) {
       if (e != hipSuccess) return e;
       configured = true;
     }
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kM16Waves * 64), gemm_2d_lds_bytes(a.M, MB), stream,
-                       a);
+    hipLaunchKernelGGL(kern, grid, dim3(kM16Waves * 64), gemm_2d_lds_bytes(Mb, MB), stream, a);
   }
   return hipGetLastError();
 }
@@ -735,7 +759,7 @@ hipError_t launch_2d_t(const GemmArgs& a, int T, int spw, hipStream_t stream) {
 // staging registers); the caller quantizes the others first.
 template <bool FQ>
 hipError_t launch_2d_mb(const GemmArgs& a, int T, int spw, hipStream_t stream) {
-  const int mb = (a.M + 15) / 16;
+  const int mb = a.M > kRowBlock ? 3 : (a.M + 15) / 16;
   if (mb == 1) return launch_2d_t<1, FQ>(a, T, spw, stream);
   if constexpr (FQ) {
     return hipErrorInvalidValue;
@@ -749,12 +773,15 @@ hipError_t launch_2d_mb(const GemmArgs& a, int T, int spw, hipStream_t stream) {
 
 size_t gemm_partial_bytes(int M, int N, int K, int group_tiles) {
   const Plan pl = choose_plan(M, N, K, group_tiles, device_cus());
-  return pl.P > 1 ? (size_t)(N / 16) * pl.P * ((M + 15) / 16) * 64 * 16 : 0;
+  const int rb = (M + kRowBlock - 1) / kRowBlock;
+  const int MB = M > kRowBlock ? 3 : (M + 15) / 16;
+  return pl.P > 1 ? (size_t)rb * (N / 16) * pl.P * MB * 64 * 16 : 0;
 }
 
 int gemm_counter_words(int M, int N, int K, int group_tiles) {
   const Plan pl = choose_plan(M, N, K, group_tiles, device_cus());
-  return pl.P > 1 ? N / 16 / pl.T : 0;
+  const int rb = (M + kRowBlock - 1) / kRowBlock;
+  return pl.P > 1 ? rb * (N / 16 / pl.T) : 0;
 }
 
 // MXG_DIRECT_KERNEL ("m16" / "2d") forces the kernel where both apply
@@ -800,8 +827,23 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
   if (a.lda == 0) a.lda = a.K;
   const bool fq = a.x != nullptr;
   if (fq && (a.group_tiles != 0 || a.lda != a.K)) return hipErrorInvalidValue;
-  if (a.a_sf128 && (fq || a.group_tiles != 0 || a.lda != a.K || a.M > 128))
-    return hipErrorInvalidValue;
+  if (a.a_sf128 && (fq || a.group_tiles != 0 || a.lda != a.K)) return hipErrorInvalidValue;
+  if (a.M > kRowBlock) {
+    // More than 48 rows: a grid of 48-row blocks on the 2D kernel, MXFP8
+    // input (BF16 input is quantized by its own launch first).
+    if (a.group_tiles != 0) return hipErrorInvalidValue;
+    if (fq) {
+      hipError_t e = launch_quantize(a.x, a.M, a.K, a.ld_x, a.a_q, a.a_s, stream);
+      if (e != hipSuccess) return e;
+      a.x = nullptr;
+    }
+    const Plan pl = choose_plan(a.M, a.N, a.K, 0, device_cus());
+    if (pl.T == 0) return hipErrorInvalidValue;
+    a.P = pl.P;
+    a.Sp = pl.Sp;
+    if (pl.P > 1 && (a.ctr == nullptr || a.part == nullptr)) return hipErrorInvalidValue;
+    return launch_2d_mb<false>(a, pl.T, pl.SPW, stream);
+  }
   const int S = a.K / 128;
   const Plan pl = choose_plan(a.M, a.N, a.K, a.group_tiles, device_cus());
   // One full-K tile per workgroup with the whole activation in LDS unless

@@ -61,7 +61,7 @@ def gemm(lib, M=4, N=1024, K=2048, x=None, ld_x=0, a_q=P(1), a_s=P(2), w_q=P(3),
 
 @pytest.mark.parametrize("kw,status", [
     (dict(a_q=None), 1), (dict(w_s=None), 1), (dict(out=None), 1),
-    (dict(M=0), 3), (dict(M=49), 3), (dict(M=-1), 3),
+    (dict(M=0), 3), (dict(M=257), 3), (dict(M=-1), 3),
     (dict(K=100), 3), (dict(K=64), 3), (dict(K=0), 3), (dict(K=16384 + 128, N=128), 3),
     (dict(N=8), 3), (dict(N=1000), 3),
     (dict(x=P(6), ld_x=1024), 3),
@@ -253,8 +253,8 @@ def gemm_ex(lib, M=4, N=1024, K=2048, a_q=P(1), a_s=P(2), layout=1, w_q=P(3), w_
 
 @pytest.mark.parametrize("kw,status", [
     (dict(a_s=None), 1), (dict(a_q=None), 1), (dict(layout=0, out=None), 1),
-    (dict(layout=2), 3), (dict(layout=-1), 3), (dict(M=0), 3), (dict(M=49), 3),
-    (dict(K=1000), 3), (dict(layout=0, M=49), 3),
+    (dict(layout=2), 3), (dict(layout=-1), 3), (dict(M=0), 3), (dict(M=257), 3),
+    (dict(K=1000), 3), (dict(layout=0, M=257), 3),
     (dict(a_q=ctypes.c_void_p(A + 8)), 2), (dict(a_s=ctypes.c_void_p(A + 4)), 2),
     (dict(ws=None), 4),
 ])

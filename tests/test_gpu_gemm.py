@@ -170,7 +170,7 @@ def test_rejected_call_writes_nothing():
     out = torch.full((M, N), 0x1234, dtype=torch.int16, device="cuda")
     say("gemm rejected call")
     L = mx.lib()
-    for m, k in ((0, K), (49, K), (M, 500)):
+    for m, k in ((0, K), (257, K), (M, 500)):
         st = L.mxfp8_gemm(m, N, k, None, 0, a_q.data_ptr(), a_s.data_ptr(), w_q.data_ptr(),
                           w_s.data_ptr(), out.data_ptr(), None, 0, None)
         assert st == 3
@@ -332,3 +332,55 @@ def test_rmsnorm_128x4_output_feeds_the_gemm(M):
     assert np.array_equal(host_u8(s1), oracle.scales_to_128x4(host_u8(s0)))
     assert torch.equal(row.view(torch.int16), tiled.view(torch.int16))
     check_gemm(tiled, oracle.gemm(host_u8(q0), host_u8(s0), ow_q, ow_s), f"norm->gemm M={M}")
+
+
+@pytest.mark.parametrize("M", [49, 64, 96, 100, 128, 200, 256])
+@pytest.mark.parametrize("fused", [False, True])
+def test_rows_above_48(M, fused, monkeypatch):
+    # More than 48 rows: a grid of 48-row blocks on the 2D kernel (BF16 input
+    # quantized by its own launch first); ragged last blocks included.
+    monkeypatch.delenv("MXG_GEMM_PATH", raising=False)
+    monkeypatch.delenv("MXG_DIRECT_KERNEL", raising=False)
+    run_case(M, 512, 2048, seed=M, fused=fused)
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 4096, 5120), (128, 5120, 8192), (256, 8192, 1536),
+                                   (97, 2064, 16384)])
+def test_rows_above_48_full_size(M, N, K):
+    run_case(M, N, K, seed=M + 1, outliers=True)
+
+
+@pytest.mark.parametrize("M", [64, 130, 256])
+def test_rows_above_48_with_128x4_scales(M):
+    # rows past 128 sit in the second row of 128 x 4 tiles
+    N, K = 1024, 2048
+    case = synth.gemm_case(M, N, K, seed=M + 2)
+    oa_q, oa_s = oracle.quantize(synth.bits(case["x"]))
+    ow_q, ow_s = oracle.quantize(synth.bits(case["w"]))
+    ref = oracle.gemm(oa_q, oa_s, ow_q, ow_s)
+    say(f"gemm 128x4 scales, rows above 48: M={M}")
+    w = mx.PackedWeight.from_rows(dev_u8(ow_q), dev_u8(ow_s))
+    row = mx.mxfp8_gemm(dev_u8(oa_q), dev_u8(oa_s), w)
+    tiled = mx.mxfp8_gemm_ex(dev_u8(oa_q), dev_u8(oracle.scales_to_128x4(oa_s)), w,
+                             mx.SCALES_128X4)
+    torch.cuda.synchronize()
+    assert torch.equal(row.view(torch.int16), tiled.view(torch.int16))
+    check_gemm(tiled, ref, f"128x4 M={M}")
+
+
+def test_rows_above_48_workspace_left_clean():
+    M, N, K = 150, 4096, 5120
+    w, _ = _weights(N, K, 0)
+    ws = torch.zeros(int(mx.lib().mxg_gemm_workspace_bytes(M, N, K)) + 4096, dtype=torch.uint8,
+                     device="cuda")
+    x = synth.gemm_case(M, 16, K, seed=9)["x"].cuda()
+    a_q = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+    a_s = torch.empty(M, K // 32, dtype=torch.uint8, device="cuda")
+    say(f"workspace hygiene, rows above 48: M={M}")
+    first = mx.mxfp8_gemm(a_q, a_s, w, x=x, workspace=ws).clone()
+    for _ in range(3):
+        o = mx.mxfp8_gemm(a_q, a_s, w, workspace=ws)
+        assert torch.equal(o.view(torch.int16), first.view(torch.int16))
+    torch.cuda.synchronize()
+    assert mx.workspace_error(ws) == 0
+    assert not ws[:65536].any(), "counters must be back to zero"
