@@ -664,10 +664,23 @@ Plan choose_plan(int M, int N, int K, int group_tiles, int cus) {
   const int rb = (M + kRowBlock - 1) / kRowBlock;
   if (M > kRowBlock) M = kRowBlock;
   const int tiles = N / 16, S = K / 128, MB = (M + 15) / 16;
+  // MXG_PLAN="T,P" restricts the choice to that plan where it is valid
+  // (tests and plan sweeps; ignored otherwise).
+  int wantT = 0, wantP = 0;
+  if (const char* e = std::getenv("MXG_PLAN")) {
+    const char* c = std::strchr(e, ',');
+    if (c) {
+      wantT = std::atoi(e);
+      wantP = std::atoi(c + 1);
+    }
+  }
   Plan best{0, 0, 0, 0, 1e30};
+  for (int pass = 0; pass < 2 && best.T == 0; ++pass)
   for (int T : {1, 2, 4}) {
     if (tiles % T || (group_tiles && group_tiles % T) || T * MB > 16) continue;
+    if (pass == 0 && wantT && T != wantT) continue;
     for (int P : {1, 2, 3, 4, 6, 8}) {
+      if (pass == 0 && wantP && P != wantP) continue;
       if (P > S) break;
       const int Sp = (S + P - 1) / P;
       if ((P - 1) * Sp >= S) continue;                  // no empty part

@@ -384,3 +384,14 @@ def test_rows_above_48_workspace_left_clean():
     torch.cuda.synchronize()
     assert mx.workspace_error(ws) == 0
     assert not ws[:65536].any(), "counters must be back to zero"
+
+
+@pytest.mark.parametrize("plan", ["1,1", "2,1", "4,1", "2,2", "4,2", "1,4", "4,4", "2,8"])
+@pytest.mark.parametrize("M", [17, 48, 100])
+def test_every_2d_plan(M, plan, monkeypatch):
+    # MXG_PLAN forces the 2D kernel's (tiles per workgroup, K parts) plan:
+    # every plan, with and without K split, one or several row blocks.
+    monkeypatch.setenv("MXG_GEMM_PATH", "direct")
+    monkeypatch.setenv("MXG_DIRECT_KERNEL", "2d")
+    monkeypatch.setenv("MXG_PLAN", plan)
+    run_case(M, 512, 2048, seed=M + len(plan))
