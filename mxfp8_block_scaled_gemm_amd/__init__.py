@@ -17,7 +17,8 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxgemm.so")
-MAX_ROWS = 48
+MAX_ROWS = 48          # chain and WO-A (MXG_MAX_ROWS)
+MAX_GEMM_ROWS = 256    # mxfp8_gemm / mxfp8_gemm_ex (MXG_MAX_GEMM_ROWS)
 
 _lib = None
 

@@ -16,6 +16,12 @@ Sources ("pages"): vLLM API documentation pages for
 ``...attention.step`` ([step]), ``vllm.models.deepseek_v41.nvidia.ops.cute_dsl``
 ([cute]) and ``vllm.models.deepseek_v41.nvidia.ops.o_proj`` ([o_proj]).
 
+Parity unpinned (the pages show no outputs to compare against, and print
+neither formula nor layout): fidelity to the real model's rotary convention,
+to the scale rule its quantizer used, to its RMSNorm rounding, and to the byte
+order of its F8_128x4 scales.  Each function here is pinned to what its own
+definition fixes (tests/test_oracle_*.py, tests/golden/).
+
 Array conventions: BF16 tensors are numpy ``uint16`` bit patterns, E4M3 codes and
 E8M0 scale bytes are ``uint8``; everything is row-major and C-contiguous unless a
 row stride is passed.
