@@ -64,7 +64,7 @@ extern "C" {
 #define MXG_ERR_DEVICE 5    /* current device is not gfx950, or a launch failed */
 
 #define MXG_MAX_ROWS 48       /* rows of the chain, WO-A and the low-latency GEMM range */
-#define MXG_MAX_GEMM_ROWS 256 /* rows of mxfp8_gemm / mxfp8_gemm_ex (above 48: row blocks) */
+#define MXG_MAX_GEMM_ROWS 256 /* rows of mxfp8_gemm / mxfp8_gemm_ex (above 48: 64-row blocks) */
 #define MXG_MAX_K 16384     /* largest contraction of the GEMM entry points */
 
 /* Human-readable text of a status code (static storage; never NULL). */
@@ -183,7 +183,7 @@ int mxfp8_pack_weights(const uint8_t *w_q, const uint8_t *w_s, int64_t N, int64_
  *   M, N, K   1 <= M <= MXG_MAX_GEMM_ROWS, N % 16 == 0, K % 128 == 0,
  *             K <= MXG_MAX_K.  Up to 48 rows the low-latency kernels serve
  *             the call; above 48 ([mxfp8] module text: more rows go to
- *             another kernel there) it runs as a grid of 48-row blocks over
+ *             another kernel there) it runs as a grid of 64-row blocks over
  *             the same weight in one launch, with BF16 input quantized by
  *             its own launch first
  *   x_bf16    NULL: a_q/a_s are inputs.  Non-NULL: BF16 [M, ld_x] activations

@@ -35,7 +35,7 @@
 namespace mxg {
 
 constexpr int kM16Waves = 16;   // waves per workgroup of the GEMM kernels
-constexpr int kRowBlock = 48;   // activation rows one 2D-kernel workgroup serves
+constexpr int kRowBlock = 64;   // activation rows one 2D-kernel workgroup serves
 
 __host__ __device__ constexpr int act_ld(int K) { return K + 16; }          // LDS bytes per code row
 __host__ __device__ constexpr int scale_ld(int K) { return (K >> 5) + 4; }  // LDS bytes per scale row
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
 
 typedef unsigned v4u32 __attribute__((ext_vector_type(4)));
 
-// ------------------------------------------------- 2D tiling (any M <= 48)
+// ------------------------------------- 2D tiling (any M; 64-row blocks above 48)
 //
 // When one full-K weight tile per workgroup does not suit the shape (rows
 // above 16: every workgroup would pull all M*K activation bytes through its
@@ -269,9 +269,9 @@ typedef unsigned v4u32 __attribute__((ext_vector_type(4)));
 // arrive adds them in part order (deterministic) and stores BF16.
 template <int MB, int T, int SPW, int NB, int CHM, bool FQ>
 __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
-  // Row block blockIdx.y: rows [48 y, 48 y + 48) of the activations and the
+  // Row block blockIdx.y: rows [64 y, 64 y + 64) of the activations and the
   // output, with their own K-split partials and tile counters (a GEMM of more
-  // than 48 rows is a grid of 48-row GEMMs over the same weight).
+  // than 64 rows is a grid of 64-row GEMMs over the same weight).
   const int row0 = kRowBlock * (int)blockIdx.y;
   GemmArgs p = p0;
   p.M = min(p0.M - row0, kRowBlock);
@@ -659,7 +659,7 @@ double plan_cost(int M, int N, int K, int T, int P, int cus, int rb = 1) {
 
 // The 2D plan of least modelled time.
 Plan choose_plan(int M, int N, int K, int group_tiles, int cus) {
-  // More than 48 rows: 48-row blocks, each with the plan's tile groups and
+  // More than 64 rows: 64-row blocks, each with the plan's tile groups and
   // K parts (and their own counters).
   const int rb = (M + kRowBlock - 1) / kRowBlock;
   if (M > kRowBlock) M = kRowBlock;
@@ -772,13 +772,14 @@ hipError_t launch_2d_t(const GemmArgs& a, int T, int spw, hipStream_t stream) {
 // staging registers); the caller quantizes the others first.
 template <bool FQ>
 hipError_t launch_2d_mb(const GemmArgs& a, int T, int spw, hipStream_t stream) {
-  const int mb = a.M > kRowBlock ? 3 : (a.M + 15) / 16;
+  const int mb = a.M > kRowBlock ? kRowBlock / 16 : (a.M + 15) / 16;
   if (mb == 1) return launch_2d_t<1, FQ>(a, T, spw, stream);
   if constexpr (FQ) {
     return hipErrorInvalidValue;
   } else {
     if (mb == 2) return launch_2d_t<2, FQ>(a, T, spw, stream);
-    return launch_2d_t<3, FQ>(a, T, spw, stream);
+    if (mb == 3) return launch_2d_t<3, FQ>(a, T, spw, stream);
+    return launch_2d_t<4, FQ>(a, T, spw, stream);
   }
 }
 
@@ -787,7 +788,7 @@ hipError_t launch_2d_mb(const GemmArgs& a, int T, int spw, hipStream_t stream) {
 size_t gemm_partial_bytes(int M, int N, int K, int group_tiles) {
   const Plan pl = choose_plan(M, N, K, group_tiles, device_cus());
   const int rb = (M + kRowBlock - 1) / kRowBlock;
-  const int MB = M > kRowBlock ? 3 : (M + 15) / 16;
+  const int MB = M > kRowBlock ? kRowBlock / 16 : (M + 15) / 16;
   return pl.P > 1 ? (size_t)rb * (N / 16) * pl.P * MB * 64 * 16 : 0;
 }
 
@@ -841,9 +842,10 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
   const bool fq = a.x != nullptr;
   if (fq && (a.group_tiles != 0 || a.lda != a.K)) return hipErrorInvalidValue;
   if (a.a_sf128 && (fq || a.group_tiles != 0 || a.lda != a.K)) return hipErrorInvalidValue;
-  if (a.M > kRowBlock) {
-    // More than 48 rows: a grid of 48-row blocks on the 2D kernel, MXFP8
-    // input (BF16 input is quantized by its own launch first).
+  if (a.M > 48) {
+    // More than 48 rows: the 2D kernel over 64-row blocks (one block up to
+    // 64 rows), MXFP8 input (BF16 input is quantized by its own launch
+    // first).
     if (a.group_tiles != 0) return hipErrorInvalidValue;
     if (fq) {
       hipError_t e = launch_quantize(a.x, a.M, a.K, a.ld_x, a.a_q, a.a_s, stream);

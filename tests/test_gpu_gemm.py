@@ -337,7 +337,7 @@ def test_rmsnorm_128x4_output_feeds_the_gemm(M):
 @pytest.mark.parametrize("M", [49, 64, 96, 100, 128, 200, 256])
 @pytest.mark.parametrize("fused", [False, True])
 def test_rows_above_48(M, fused, monkeypatch):
-    # More than 48 rows: a grid of 48-row blocks on the 2D kernel (BF16 input
+    # More than 48 rows: a grid of 64-row blocks on the 2D kernel (BF16 input
     # quantized by its own launch first); ragged last blocks included.
     monkeypatch.delenv("MXG_GEMM_PATH", raising=False)
     monkeypatch.delenv("MXG_DIRECT_KERNEL", raising=False)
