@@ -94,7 +94,14 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r = lane & 15;
   const int M = p.M, K = p.K, KB = K >> 5, S = K >> 7;
-  const int t = xcd_tile(blockIdx.x, p.N >> 4);
+  // With rsplit = 2 or 4 a workgroup takes rows [16/rsplit * part, ...) of
+  // weight tile t, so that a small N still gives every CU a workgroup: its
+  // lanes load only those rows' operand bytes (whole 128-byte lines of the
+  // packed tile) and the other lanes' A rows stay zero.
+  const int rsplit = p.rsplit, sh = rsplit == 1 ? 4 : (rsplit == 2 ? 3 : 2);
+  const int unit = xcd_tile(blockIdx.x, (p.N >> 4) * rsplit);
+  const int t = unit / rsplit, part = unit - t * rsplit;
+  const bool mine = (r >> sh) == part;                     // my A row is this workgroup's
   const int ldA = act_ld(K), ldS = scale_ld(K);
   uint8_t* s_act = smem;                                   // [M][ldA] codes
   uint8_t* s_scl = smem + M * ldA;                         // [M][ldS] scale bytes
@@ -162,7 +169,7 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const int s = wave + W * j;
-    const bool ok = j < my;
+    const bool ok = j < my && mine;
     wlo[j] = buf_ld16_nt(rw, ok ? (uint32_t)(s * 2048 + lane * 16) : kOutOfRange);
     whi[j] = buf_ld16_nt(rw, ok ? (uint32_t)(s * 2048 + 1024 + lane * 16) : kOutOfRange);
     wsc[j] = buf_ld8(rws, ok ? (uint32_t)(s * 64 + lane) : kOutOfRange);
@@ -243,7 +250,9 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
     uint2 o;
     o.x = f32_to_bf16(sum[0]) | (f32_to_bf16(sum[1]) << 16);
     o.y = f32_to_bf16(sum[2]) | (f32_to_bf16(sum[3]) << 16);
-    if (m < M) *reinterpret_cast<uint2*>(p.out + (int64_t)m * p.N + n) = o;
+    // output rows n .. n+3 are weight rows 4 (lane / 16) .. of the tile
+    if (m < M && ((4 * (lane >> 4)) >> sh) == part)
+      *reinterpret_cast<uint2*>(p.out + (int64_t)m * p.N + n) = o;
   }
 }
 
@@ -571,7 +580,7 @@ static hipError_t launch_m16(const GemmArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL(kern, dim3(a.N / 16), dim3(W * 64), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3(a.N / 16 * a.rsplit), dim3(W * 64), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -836,6 +845,20 @@ int m16_waves(int M, int K, bool fq) {
   return 0;
 }
 
+// Workgroups per 16-row weight tile in the M <= 16 kernel: 2 when the tile
+// count leaves at least half the CUs idle, else 1.  Measured on MI355X: 2.5-7 %
+// faster at N = 1024 and 2048 (e.g. BF16 M = 4, N 2048, K 5120: 4.97 against
+// 5.34 us); a split of 4 was slower wherever the tiles filled a quarter of
+// the chip or more.  MXG_M16_RSPLIT=1|2|4 forces the split (tests cover all
+// three).
+int m16_row_split(int N, int, bool) {
+  if (const char* e = std::getenv("MXG_M16_RSPLIT")) {
+    const int v = std::atoi(e);
+    if (v == 1 || v == 2 || v == 4) return v;
+  }
+  return (N / 16) * 2 <= device_cus() ? 2 : 1;
+}
+
 hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
   GemmArgs a = args;
   if (a.lda == 0) a.lda = a.K;
@@ -880,6 +903,7 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
     const int steps = (S + W - 1) / W;                     // weight steps per wave
     const int per = fq ? a.M * a.K / 32 : a.M * a.K / 16;  // 32-blocks, or 16-byte chunks
     const int ch = (per + W * 64 - 1) / (W * 64);
+    a.rsplit = m16_row_split(a.N, a.M, fq);
     if (!fq) return launch_m16_w<false>(a, W, steps, ch, stream);
     // In-kernel quantize while the weight stream is in flight when the
     // activation is small enough (every workgroup quantizes all of it, one

@@ -32,6 +32,9 @@ struct GemmArgs {
   // Activation scales in 128 x 4 tiles instead of row-major (MXFP8 input,
   // no grouping, lda == K).
   bool a_sf128 = false;
+  // M <= 16 kernel: workgroups per 16-row weight tile (1, 2 or 4; set by the
+  // launcher).
+  int rsplit = 1;
 };
 
 // Bytes of FP32 partials the GEMM of this shape needs (0: no K split); the

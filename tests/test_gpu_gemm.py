@@ -395,3 +395,16 @@ def test_every_2d_plan(M, plan, monkeypatch):
     monkeypatch.setenv("MXG_DIRECT_KERNEL", "2d")
     monkeypatch.setenv("MXG_PLAN", plan)
     run_case(M, 512, 2048, seed=M + len(plan))
+
+
+@pytest.mark.parametrize("rsplit", ["1", "2", "4"])
+@pytest.mark.parametrize("M,N,K,fused", [(1, 256, 1024, False), (5, 1024, 2048, True),
+                                         (16, 2048, 5120, False), (4, 2048, 5120, True),
+                                         (1, 1024, 4096, False), (3, 4096, 5120, True)])
+def test_weight_tile_row_split(M, N, K, fused, rsplit, monkeypatch):
+    # The M <= 16 kernel with each 16-row weight tile shared by 1, 2 or 4
+    # workgroups (rows 16/rsplit each).
+    monkeypatch.setenv("MXG_GEMM_PATH", "direct")
+    monkeypatch.setenv("MXG_DIRECT_KERNEL", "m16")
+    monkeypatch.setenv("MXG_M16_RSPLIT", rsplit)
+    run_case(M, N, K, seed=M + N + int(rsplit), fused=fused)
