@@ -278,17 +278,33 @@ typedef unsigned v4u32 __attribute__((ext_vector_type(4)));
 // arrive adds them in part order (deterministic) and stores BF16.
 template <int MB, int T, int SPW, int NB, int CHM, bool FQ>
 __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
-  // Row block blockIdx.y: rows [64 y, 64 y + 64) of the activations and the
-  // output, with their own K-split partials and tile counters (a GEMM of more
-  // than 64 rows is a grid of 64-row GEMMs over the same weight).
-  const int row0 = kRowBlock * (int)blockIdx.y;
+  // Row block y: rows [64 y, 64 y + 64) of the activations and the output,
+  // with their own K-split partials and tile counters (a GEMM of more than
+  // 64 rows is a grid of 64-row GEMMs over the same weight).  The grid is
+  // one-dimensional, X = tile groups x K parts per row block: workgroup id
+  // serves (x, y) with the RB row blocks of x dispatched 8 apart, i.e. to the
+  // same XCD (workgroups go to the 8 XCDs round robin) close in time, so the
+  // weight tiles they share are read from HBM once and from that L2 after.
+  const int X = (p0.N >> 4) / T * p0.P, RB = (p0.M + kRowBlock - 1) / kRowBlock;
+  int bx = blockIdx.x, by = 0;
+  if (RB > 1) {
+    if ((X & 7) == 0) {
+      const int id = blockIdx.x, within = id % (8 * RB);
+      bx = (id / (8 * RB)) * 8 + (within & 7);
+      by = within >> 3;
+    } else {
+      by = blockIdx.x / X;
+      bx = blockIdx.x - by * X;
+    }
+  }
+  const int row0 = kRowBlock * by;
   GemmArgs p = p0;
   p.M = min(p0.M - row0, kRowBlock);
   p.a_q += (int64_t)row0 * p0.lda;
   if (!p0.a_sf128) p.a_s += (int64_t)row0 * (p0.lda >> 5);
   p.out += (int64_t)row0 * p0.N;
-  if (p0.part) p.part += (int64_t)blockIdx.y * (p0.N >> 4) * p0.P * MB * 64 * 4;
-  if (p0.ctr) p.ctr += (int64_t)blockIdx.y * ((p0.N >> 4) / T);
+  if (p0.part) p.part += (int64_t)by * (p0.N >> 4) * p0.P * MB * 64 * 4;
+  if (p0.ctr) p.ctr += (int64_t)by * ((p0.N >> 4) / T);
   // Row index of this block's first row in the scale addressing: row-major
   // scales were offset above; 128 x 4 tiles are addressed from the first row.
   const int srow0 = p0.a_sf128 ? row0 : 0;
@@ -306,8 +322,8 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
   const int g = lane >> 4, r = lane & 15;
   const int M = p.M, K = p.K, S = K >> 7, Sp = p.Sp, P = p.P;
   const int ngroups = (p.N >> 4) / T;
-  const int q = blockIdx.x / ngroups;
-  const int tg = xcd_tile(blockIdx.x - q * ngroups, ngroups);
+  const int q = bx / ngroups;
+  const int tg = xcd_tile(bx - q * ngroups, ngroups);
   const int k0 = q * Sp, ns = min(Sp, S - k0);          // this part's steps
   const int nch = (ns + 15) >> 4;
   const int tt = wave % T, wi = wave / T;               // my tile, my index among its waves
@@ -728,7 +744,7 @@ hipError_t launch_2d(const GemmArgs& a, hipStream_t stream) {
   const int Mb = a.M < kRowBlock ? a.M : kRowBlock;      // rows of one row block
   const size_t whole_lds = (size_t)Mb * (a.Sp * 128 + 16) + (size_t)Mb * (a.Sp * 4 + 4);
   const bool whole = kRegs && NCH > 1 && whole_lds <= 160 * 1024 - 64;
-  const dim3 grid((a.N / 16 / T) * a.P, (a.M + kRowBlock - 1) / kRowBlock);
+  const dim3 grid((a.N / 16 / T) * a.P * ((a.M + kRowBlock - 1) / kRowBlock));
   if (whole) {
     auto kern = gemm_2d_kernel<MB, T, SPW, (kRegs ? NCH : 1), CHM, FQ>;
     static bool configured = false;
