@@ -35,9 +35,11 @@
  *   - Device pointers must be 16-byte aligned, and row strides must keep every
  *     row 16-byte aligned ([mxfp8] launch_low_latency passes 16-byte aligned
  *     operand pointers).
- *   - Row counts: 1 <= M <= MXG_MAX_ROWS for the GEMM entry points ([mxfp8]:
+ *   - Row counts: 1 <= M <= MXG_MAX_ROWS for the chain and WO-A ([mxfp8]:
  *     the low-latency kernel covers up to 48 rows with 16-, 32- or 48-row
- *     activation tiles; more rows go to another kernel).
+ *     activation tiles; more rows go to another kernel), and up to
+ *     MXG_MAX_GEMM_ROWS for mxfp8_gemm / mxfp8_gemm_ex, which serve rows
+ *     above 48 as 64-row blocks of another kernel shape.
  *   - K must be a multiple of 128 (at most MXG_MAX_K) and N a multiple of 16
  *     for the GEMMs ([mxfp8] mxfp8_eligible requires the weight's K to be a
  *     multiple of 128).
