@@ -219,6 +219,12 @@ def mxfp8_rmsnorm_quantize(x: torch.Tensor, w: torch.Tensor, eps: float, K: int 
             s = torch.zeros(scale_bytes_128x4(M, K), dtype=torch.uint8, device=x.device)
         else:
             s = torch.empty(M, K // 32, dtype=torch.uint8, device=x.device)
+    if scale_layout == SCALES_128X4:
+        _expect(s, torch.uint8, "s")
+        if s.numel() < scale_bytes_128x4(M, K):
+            raise ValueError("s holds fewer than scale_bytes_128x4(M, K) bytes")
+    else:
+        _expect(s, torch.uint8, "s", (M, K // 32))
     _check(lib().mxfp8_rmsnorm_quantize(_ptr(x), M, K, x.stride(0), _ptr(w), float(eps), _ptr(y),
                                         y.stride(0) if y is not None else 0, _ptr(q), _ptr(s),
                                         int(scale_layout), _stream(stream)))
