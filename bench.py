@@ -275,7 +275,7 @@ def extra_cases(dev, stream):
                                      "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         del copies
         torch.cuda.empty_cache()
-    # more than 48 rows (64-row blocks over the same weight in one launch)
+    # more than 48 rows (64-row blocks, or 64 x 64 tiles above 128 rows)
     N, K = 4096, 5120
     copies = weight_copies(N, K, dev)
     for M in (64, 128, 256):

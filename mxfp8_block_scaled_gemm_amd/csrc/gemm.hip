@@ -891,6 +891,14 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
       if (e != hipSuccess) return e;
       a.x = nullptr;
     }
+    // The 64 x 64-tile kernel above 128 rows, or above 64 rows at K >= 8192,
+    // where it measured faster than the row blocks (or equal): 20.6 against
+    // 28.8 us at M = 256, N 4096, K 5120; 30.7 against 35.5 at M = 128, N
+    // 5120, K 8192.  At 65-128 rows and smaller K its grid covers half the
+    // CUs or less and the row blocks win (M = 128, N 4096, K 5120: 16.5
+    // against 20.4 us).  MXG_DIRECT_KERNEL=2d keeps the row blocks.
+    if (a.M > 64 && (a.M > 128 || a.K >= 8192) && gemm_big_fits(a) && forced_kernel() != 2)
+      return launch_gemm_big(a, stream);
     const Plan pl = choose_plan(a.M, a.N, a.K, 0, device_cus());
     if (pl.T == 0) return hipErrorInvalidValue;
     a.P = pl.P;

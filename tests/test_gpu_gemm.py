@@ -408,3 +408,13 @@ def test_weight_tile_row_split(M, N, K, fused, rsplit, monkeypatch):
     monkeypatch.setenv("MXG_DIRECT_KERNEL", "m16")
     monkeypatch.setenv("MXG_M16_RSPLIT", rsplit)
     run_case(M, N, K, seed=M + N + int(rsplit), fused=fused)
+
+
+@pytest.mark.parametrize("M,N,K", [(129, 64, 128), (129, 512, 1024), (200, 1088, 2048),
+                                   (256, 4096, 5120), (100, 5120, 8192), (250, 320, 16384)])
+def test_big_tile_kernel(M, N, K, monkeypatch):
+    # The 64 x 64-tile kernel (above 128 rows, or above 64 at K >= 8192):
+    # ragged row tiles, a ragged last K chunk (K = 128), N not a multiple of
+    # 512 (no XCD grouping), the longest K.
+    monkeypatch.delenv("MXG_DIRECT_KERNEL", raising=False)
+    run_case(M, N, K, seed=M + K, outliers=True)
