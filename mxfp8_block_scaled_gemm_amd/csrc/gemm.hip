@@ -862,17 +862,18 @@ int m16_waves(int M, int K, bool fq) {
 }
 
 // Workgroups per 16-row weight tile in the M <= 16 kernel: 2 when the tile
-// count leaves at least half the CUs idle, else 1.  Measured on MI355X: 2.5-7 %
-// faster at N = 1024 and 2048 (e.g. BF16 M = 4, N 2048, K 5120: 4.97 against
-// 5.34 us); a split of 4 was slower wherever the tiles filled a quarter of
-// the chip or more.  MXG_M16_RSPLIT=1|2|4 forces the split (tests cover all
-// three).
-int m16_row_split(int N, int, bool) {
+// count leaves at least half the CUs idle and K >= 4096, else 1.  Measured on
+// MI355X: 2.5-7 % faster at N = 1024 and 2048 with K = 4096 or 5120 (e.g.
+// BF16 M = 4, N 2048, K 5120: 4.97 against 5.34 us), 2 % slower at K = 2048
+// (launch-bound); a split of 4 was slower wherever the tiles filled a quarter
+// of the chip or more.  MXG_M16_RSPLIT=1|2|4 forces the split (tests cover
+// all three).
+int m16_row_split(int N, int K, bool) {
   if (const char* e = std::getenv("MXG_M16_RSPLIT")) {
     const int v = std::atoi(e);
     if (v == 1 || v == 2 || v == 4) return v;
   }
-  return (N / 16) * 2 <= device_cus() ? 2 : 1;
+  return (N / 16) * 2 <= device_cus() && K >= 4096 ? 2 : 1;
 }
 
 hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
@@ -927,7 +928,7 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
     const int steps = (S + W - 1) / W;                     // weight steps per wave
     const int per = fq ? a.M * a.K / 32 : a.M * a.K / 16;  // 32-blocks, or 16-byte chunks
     const int ch = (per + W * 64 - 1) / (W * 64);
-    a.rsplit = m16_row_split(a.N, a.M, fq);
+    a.rsplit = m16_row_split(a.N, a.K, fq);
     if (!fq) return launch_m16_w<false>(a, W, steps, ch, stream);
     // In-kernel quantize while the weight stream is in flight when the
     // activation is small enough (every workgroup quantizes all of it, one
