@@ -899,7 +899,7 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
     // CUs or less and the row blocks win (M = 128, N 4096, K 5120: 16.5
     // against 20.4 us).  MXG_DIRECT_KERNEL=2d keeps the row blocks.
     if (a.M > 64 && (a.M > 128 || a.K >= 8192) && gemm_big_fits(a) && forced_kernel() != 2)
-      return launch_gemm_big(a, stream);
+      return launch_gemm_big(a, device_cus(), stream);
     const Plan pl = choose_plan(a.M, a.N, a.K, 0, device_cus());
     if (pl.T == 0) return hipErrorInvalidValue;
     a.P = pl.P;

@@ -1,9 +1,11 @@
 // MXFP8 GEMM for more than 64 activation rows ([mxfp8] page, module text:
 // above the low-latency row range the projections run on another kernel).
 //
-// A workgroup of 4 waves computes a 64 x 64 output tile over the whole K:
-// weight tiles 4 bx .. 4 bx + 3 (16 rows each, wave w streams tile 4 bx + w
-// from HBM straight into its MFMA A operands, packed order) against
+// A workgroup of 4 or 8 waves computes a 64 x 64 output tile over the whole
+// K: weight tiles 4 bx .. 4 bx + 3 (16 rows each; wave w, and with 8 waves
+// also wave w + 4, streams tile 4 bx + w from HBM straight into its MFMA A
+// operands, packed order; two waves of one tile take the even and the odd
+// K-steps of each chunk and add their sums at the end) against
 // activation rows 64 by .. 64 by + 63 (four 16-row MFMA B tiles, staged
 // through LDS in chunks of 4 K-steps, double-buffered).  Every weight step
 // a wave loads feeds four scaled MFMAs and every activation byte staged
@@ -21,8 +23,6 @@ namespace mxg {
 
 namespace {
 
-constexpr int kBigWaves = 4;
-constexpr int kBigThreads = kBigWaves * 64;
 constexpr int kCS = 4;                              // K-steps (128 wide) per chunk
 constexpr int kBigRows = 64;                        // activation rows per workgroup
 constexpr int kLdA = kCS * 128 + 16;                // LDS bytes per code row of a chunk
@@ -32,12 +32,17 @@ constexpr int kBufBytes = kBigRows * kLdA + kBigRows * kLdS;
 // pieces, and 64 rows x kCS*4 scale bytes in dwords.
 constexpr int kPiecesPerRow = kCS * 128 / 16;
 constexpr int kDwordsPerRow = kCS;
-constexpr int kStCodes = kBigRows * kPiecesPerRow / kBigThreads;
-constexpr int kStScales = kBigRows * kDwordsPerRow / kBigThreads;
-static_assert(kBigRows * kPiecesPerRow % kBigThreads == 0 &&
-              kBigRows * kDwordsPerRow % kBigThreads == 0, "staging must tile the chunk");
+constexpr int kScalePieces = kBigRows * kDwordsPerRow;   // dwords per chunk
 
-__global__ __launch_bounds__(kBigThreads) void gemm_big_kernel(GemmArgs p) {
+// WV = 4: one wave per weight tile; WV = 8: two per tile, taking the even
+// and the odd K-steps of each chunk (more loads in flight per workgroup).
+template <int WV>
+__global__ __launch_bounds__(WV * 64) void gemm_big_kernel(GemmArgs p) {
+  constexpr int kBigThreads = WV * 64;
+  constexpr int kHalves = WV / 4;                    // waves per weight tile
+  constexpr int kStCodes = kBigRows * kPiecesPerRow / kBigThreads;
+  constexpr int kStScales = (kScalePieces + kBigThreads - 1) / kBigThreads;
+  static_assert(kBigRows * kPiecesPerRow % kBigThreads == 0, "staging must tile the chunk");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -59,7 +64,7 @@ __global__ __launch_bounds__(kBigThreads) void gemm_big_kernel(GemmArgs p) {
   }
   const int row0 = by * kBigRows;
   const int Mb = min(M - row0, kBigRows);
-  const int tile = 4 * bx + wave;
+  const int tile = 4 * bx + (wave & 3), kh = wave >> 2;   // my tile; my share of each chunk's steps
 
   const auto ra = make_rsrc(p.a_q + (int64_t)row0 * K, (uint32_t)((Mb - 1) * K + K));
   const auto rs = make_rsrc(p.a_s + (int64_t)row0 * KB, (uint32_t)((Mb - 1) * KB + KB));
@@ -82,7 +87,7 @@ __global__ __launch_bounds__(kBigThreads) void gemm_big_kernel(GemmArgs p) {
     for (int i = 0; i < kStScales; ++i) {
       const int piece = tid + i * kBigThreads;
       const int row = piece / kDwordsPerRow, col = (piece % kDwordsPerRow) * 4;
-      const bool ok = row < Mb && (col >> 2) < ns;
+      const bool ok = piece < kScalePieces && row < Mb && (col >> 2) < ns;
       ss[i] = __builtin_amdgcn_raw_buffer_load_b32(
           rs, ok ? row * KB + kCS * 4 * c + col : (int)kOutOfRange, 0, 0);
     }
@@ -100,22 +105,23 @@ __global__ __launch_bounds__(kBigThreads) void gemm_big_kernel(GemmArgs p) {
     for (int i = 0; i < kStScales; ++i) {
       const int piece = tid + i * kBigThreads;
       const int row = piece / kDwordsPerRow, col = (piece % kDwordsPerRow) * 4;
-      *reinterpret_cast<uint32_t*>(scl + row * kLdS + col) = ss[i];
+      if (piece < kScalePieces) *reinterpret_cast<uint32_t*>(scl + row * kLdS + col) = ss[i];
     }
   };
 
   // Weight steps of chunk c for this wave's tile, in register set W.
-  v4i wlo[2][kCS], whi[2][kCS];
-  uint32_t wsc[2][kCS];
+  constexpr int kHS = kCS / kHalves;                 // my steps per chunk
+  v4i wlo[2][kHS], whi[2][kHS];
+  uint32_t wsc[2][kHS];
   auto weight_load = [&](auto set_tag, int c) {
     constexpr int W = decltype(set_tag)::value;
 #pragma unroll
-    for (int j = 0; j < kCS; ++j) {
-      const int s = kCS * c + j;
+    for (int jj = 0; jj < kHS; ++jj) {
+      const int s = kCS * c + kHalves * jj + kh;
       const bool ok = s < S;
-      wlo[W][j] = buf_ld16_nt(rw, ok ? (uint32_t)(s * 2048 + lane * 16) : kOutOfRange);
-      whi[W][j] = buf_ld16_nt(rw, ok ? (uint32_t)(s * 2048 + 1024 + lane * 16) : kOutOfRange);
-      wsc[W][j] = buf_ld8(rws, ok ? (uint32_t)(s * 64 + lane) : kOutOfRange);
+      wlo[W][jj] = buf_ld16_nt(rw, ok ? (uint32_t)(s * 2048 + lane * 16) : kOutOfRange);
+      whi[W][jj] = buf_ld16_nt(rw, ok ? (uint32_t)(s * 2048 + 1024 + lane * 16) : kOutOfRange);
+      wsc[W][jj] = buf_ld8(rws, ok ? (uint32_t)(s * 64 + lane) : kOutOfRange);
     }
   };
 
@@ -129,7 +135,8 @@ __global__ __launch_bounds__(kBigThreads) void gemm_big_kernel(GemmArgs p) {
     const uint8_t* scl = act + kBigRows * kLdA;
     const int ns = min(kCS, S - kCS * c);
 #pragma unroll
-    for (int j = 0; j < kCS; ++j) {
+    for (int jj = 0; jj < kHS; ++jj) {
+      const int j = kHalves * jj + kh;
       if (j < ns) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
@@ -137,8 +144,8 @@ __global__ __launch_bounds__(kBigThreads) void gemm_big_kernel(GemmArgs p) {
           const v4i blo = *reinterpret_cast<const v4i*>(a);
           const v4i bhi = *reinterpret_cast<const v4i*>(a + 64);
           const int bsc = scl[(16 * mt + r) * kLdS + 4 * j + g];
-          acc[mt] = mfma_mx16(cat8(wlo[W][j], whi[W][j]), cat8(blo, bhi), acc[mt], (int)wsc[W][j],
-                              bsc);
+          acc[mt] = mfma_mx16(cat8(wlo[W][jj], whi[W][jj]), cat8(blo, bhi), acc[mt],
+                              (int)wsc[W][jj], bsc);
         }
       }
     }
@@ -166,6 +173,20 @@ __global__ __launch_bounds__(kBigThreads) void gemm_big_kernel(GemmArgs p) {
     if (c + 1 < nch) chunk(std::integral_constant<int, 1>{}, c + 1);
   }
 
+  if constexpr (kHalves == 2) {
+    // The two halves of each tile's steps: waves 4..7 hand their sums to
+    // waves 0..3 through LDS (after the last chunk's reads), which add them.
+    __syncthreads();
+    v4f* red = reinterpret_cast<v4f*>(smem);            // [4 tiles][4 mt][64]
+    if (kh == 1) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) red[((wave & 3) * 4 + mt) * 64 + lane] = acc[mt];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt] += red[((wave & 3) * 4 + mt) * 64 + lane];
+  }
   // Lane (g, r) of acc[mt] holds out[row0 + 16 mt + r][16 tile + 4 g + i].
   const int n = 16 * tile + 4 * g;
 #pragma unroll
@@ -187,17 +208,27 @@ bool gemm_big_fits(const GemmArgs& a) {
          (a.lda == 0 || a.lda == a.K) && !a.a_sf128;
 }
 
-hipError_t launch_gemm_big(const GemmArgs& a, hipStream_t stream) {
+template <int WV>
+static hipError_t launch_big(const GemmArgs& a, int grid, hipStream_t stream) {
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_big_kernel,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_big_kernel<WV>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 2 * kBufBytes);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  const int grid = (a.N / 64) * ((a.M + kBigRows - 1) / kBigRows);
-  hipLaunchKernelGGL(gemm_big_kernel, dim3(grid), dim3(kBigThreads), 2 * kBufBytes, stream, a);
+  hipLaunchKernelGGL(gemm_big_kernel<WV>, dim3(grid), dim3(WV * 64), 2 * kBufBytes, stream, a);
   return hipGetLastError();
+}
+
+// Eight waves (two per weight tile) when the grid fits one workgroup per CU:
+// 17-20 % faster there (M = 256, N 4096, K 5120: 17.3 against 20.7 us); four
+// waves on larger grids, where two 4-wave workgroups share a CU but a single
+// 8-wave one does not (M = 256, N 8192, K 1536: 10.8 against 13.3 us).
+hipError_t launch_gemm_big(const GemmArgs& a, int cus, hipStream_t stream) {
+  const int grid = (a.N / 64) * ((a.M + kBigRows - 1) / kBigRows);
+  if (grid <= cus) return launch_big<8>(a, grid, stream);
+  return launch_big<4>(a, grid, stream);
 }
 
 }  // namespace mxg

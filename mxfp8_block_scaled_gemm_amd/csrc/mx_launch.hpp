@@ -55,7 +55,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 // 64 x 64-tile GEMM for more than 64 rows (gemm_big.hip): MXFP8 input,
 // N % 64 == 0, row-major activation scales.
 bool gemm_big_fits(const GemmArgs& a);
-hipError_t launch_gemm_big(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemm_big(const GemmArgs& a, int cus, hipStream_t stream);
 
 // RMSNorm + MXFP8 of BF16 rows (rmsnorm.hip); layout 1 = 128 x 4 scale tiles.
 hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,

@@ -411,10 +411,12 @@ def test_weight_tile_row_split(M, N, K, fused, rsplit, monkeypatch):
 
 
 @pytest.mark.parametrize("M,N,K", [(129, 64, 128), (129, 512, 1024), (200, 1088, 2048),
-                                   (256, 4096, 5120), (100, 5120, 8192), (250, 320, 16384)])
+                                   (256, 4096, 5120), (100, 5120, 8192), (250, 320, 16384),
+                                   (193, 8192, 2048), (200, 5184, 1536)])
 def test_big_tile_kernel(M, N, K, monkeypatch):
     # The 64 x 64-tile kernel (above 128 rows, or above 64 at K >= 8192):
     # ragged row tiles, a ragged last K chunk (K = 128), N not a multiple of
-    # 512 (no XCD grouping), the longest K.
+    # 512 (no XCD grouping), the longest K; grids up to one workgroup per CU
+    # (8 waves each) and beyond (4 waves each).
     monkeypatch.delenv("MXG_DIRECT_KERNEL", raising=False)
     run_case(M, N, K, seed=M + K, outliers=True)
