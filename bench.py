@@ -298,12 +298,6 @@ def extra_cases(dev, stream):
     torch.cuda.empty_cache()
     for M in (1, 8, 32):
         out[f"chain M{M}"] = chain_case(dev, stream, M)
-    os.environ["MXG_CHAIN_PATH"] = "stage"
-    try:
-        for M in (1, 8, 32):
-            out[f"chain M{M} (one stage-kernel launch)"] = chain_case(dev, stream, M)
-    finally:
-        del os.environ["MXG_CHAIN_PATH"]
     for M in (1, 8, 32):
         out[f"chain+norm M{M}"] = chain_case(dev, stream, M, norm=True)
     for M in (1, 8, 48):
@@ -311,12 +305,6 @@ def extra_cases(dev, stream):
             out[f"rmsnorm+quantize M{M} K{K}"] = rmsnorm_case(dev, stream, M, K, ld)
     for M in (1, 4, 16):
         out[f"wo_a+wo_b M{M}"] = wo_a_case(dev, stream, M)
-    os.environ["MXG_WOA_PATH"] = "stage"
-    try:
-        for M in (1, 4, 16):
-            out[f"wo_a+wo_b M{M} (one stage-kernel launch)"] = wo_a_case(dev, stream, M)
-    finally:
-        del os.environ["MXG_WOA_PATH"]
     return out
 
 

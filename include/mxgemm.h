@@ -204,10 +204,8 @@ int mxfp8_pack_weights(const uint8_t *w_q, const uint8_t *w_s, int64_t N, int64_
  *             must be zero-filled once when allocated; every call leaves its
  *             counters (the first 64 KiB) at zero again, and the partial
  *             sums after them need no clearing, so calls of any shape can
- *             share one workspace in turn.
- *             Byte offset 20 holds an error word that an in-kernel wait sets
- *             if it ever expires (it cannot in a correct launch).  Calls that
- *             share a workspace must not overlap (issue them on one stream).
+ *             share one workspace in turn.  Calls that share a workspace must
+ *             not overlap (issue them on one stream).
  *
  * Small-row GEMMs are bound by the weight stream from HBM; the library picks
  * the kernel and the K split per shape.  Results do not depend on the choice
@@ -261,12 +259,9 @@ typedef struct {
  * (C included).  Weights never depend on the previous stage, and the pages
  * overlap the next weight read with the previous kernel ([mxfp8] page: the
  * low-latency kernel loads its weights before its grid dependency wait).
- * The default runs the three stages as three launches in stream order (each
- * stage's weight read starts when the previous launch ends); a persistent
- * one-launch form, whose stages stream their weights ahead of the
- * dependency wait, is selected with MXG_CHAIN_PATH=stage in the
- * environment.  Both give the same results to the tolerance of
- * mxfp8_gemm; the three launches are the faster on MI355X.
+ * The stages run as three launches in stream order (each stage's weight
+ * read starts when the previous launch ends): on MI355X a dependency between
+ * workgroups of one persistent launch measured slower than a launch boundary.
  *
  * Shapes: 1 <= M <= 48; each weight N % 16 == 0, K % 128 == 0; wB.K <= wA.N,
  * wB.K % 128 == 0.  out_a/out_b/out_c are BF16 [M, N] row-major, b_q/b_s
@@ -278,8 +273,8 @@ typedef struct {
  * aligned; norm_eps >= 0), out_a[:, 0:wB.K] is RMS-normalised as
  * mxfp8_rmsnorm_quantize does and the BF16 result is what is requantized;
  * it is also written to b_bf16 ([M, wB.K] BF16) when that is non-NULL.
- * This takes one more launch between A and B (on either path selection,
- * the three-launch form runs).  norm_weight NULL: the plain requantize.
+ * This takes one more launch between A and B.  norm_weight NULL: the plain
+ * requantize.
  */
 typedef struct {
   int64_t M;

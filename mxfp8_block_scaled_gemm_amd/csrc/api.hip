@@ -9,7 +9,6 @@
 #include <cstring>
 
 #include "mx_launch.hpp"
-#include "mx_stages.hpp"
 #include "mxgemm.h"
 
 namespace {
@@ -66,18 +65,28 @@ int validate_rmsnorm(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, cons
   return MXG_OK;
 }
 
-int validate_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* x, int64_t ld_x,
-                  const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w_q,
-                  const uint8_t* w_s, const uint16_t* out, size_t ws_bytes, const void* ws) {
+bool gemm_shape_ok(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && M <= MXG_MAX_GEMM_ROWS && N >= 16 && N % 16 == 0 && K >= 128 && K % 128 == 0 &&
+         N <= ((int64_t)1 << 24) && K <= MXG_MAX_K && N * K <= ((int64_t)1 << 31) - 1;
+}
+
+int validate_gemm_args(int64_t M, int64_t N, int64_t K, const uint16_t* x, int64_t ld_x,
+                       const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w_q,
+                       const uint8_t* w_s, const uint16_t* out) {
   if (!a_q || !a_s || !w_q || !w_s || !out) return MXG_ERR_NULL;
-  if (M < 1 || M > MXG_MAX_GEMM_ROWS || N < 16 || N % 16 != 0 || K < 128 || K % 128 != 0 ||
-      N > (int64_t)1 << 24 || K > MXG_MAX_K)
-    return MXG_ERR_SHAPE;
-  if (N * K > ((int64_t)1 << 31) - 1) return MXG_ERR_SHAPE;
+  if (!gemm_shape_ok(M, N, K)) return MXG_ERR_SHAPE;
   if (x && (ld_x < K || ld_x * M > ((int64_t)1 << 30))) return MXG_ERR_SHAPE;
   if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(w_q) || !aligned16(w_s) ||
       !aligned16(out) || (x && (!aligned16(x) || ld_x % 8 != 0)))
     return MXG_ERR_ALIGN;
+  return MXG_OK;
+}
+
+int validate_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* x, int64_t ld_x,
+                  const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w_q,
+                  const uint8_t* w_s, const uint16_t* out, size_t ws_bytes, const void* ws) {
+  const int st = validate_gemm_args(M, N, K, x, ld_x, a_q, a_s, w_q, w_s, out);
+  if (st != MXG_OK) return st;
   const size_t need = mxg_gemm_workspace_bytes(M, N, K);
   if (need > 0 && (!ws || ws_bytes < need)) return MXG_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return MXG_ERR_ALIGN;
@@ -110,55 +119,6 @@ int validate_chain(const mxg_chain* c, size_t need) {
   return MXG_OK;
 }
 
-// Kernel choice for a single GEMM: the direct kernels (one 16-row weight
-// tile per workgroup, the whole weight stream issued at once) measure faster
-// than the stage kernel for every single-GEMM shape; the stage kernel serves
-// the multi-stage programs.  MXG_GEMM_PATH ("stage" / "direct") forces a
-// choice (tests use it to cover both).
-bool use_stage_kernel(int M, int, int, bool) {
-  const char* force = std::getenv("MXG_GEMM_PATH");
-  return M <= MXG_MAX_ROWS && force && std::strcmp(force, "stage") == 0;
-}
-
-mxg::ProgramBuilder gemm_program(int M, int N, int K, const uint16_t* x, int ld_x, uint8_t* a_q,
-                                 uint8_t* a_s, const uint8_t* w_q, const uint8_t* w_s,
-                                 uint16_t* out, uint8_t* ws, int G) {
-  mxg::ProgramBuilder pb(M, G, ws);
-  const int i = pb.add_gemm(N, K, w_q, w_s, -1, out, N, x ? mxg::kActBf16 : mxg::kActMx);
-  mxg::StageDesc& d = pb.stage(i);
-  if (x) {
-    d.x = x;
-    d.ld_x = ld_x;
-    d.q = a_q;
-    d.s = a_s;
-    d.ldq = K;
-  } else {
-    d.aq = a_q;
-    d.as = a_s;
-  }
-  return pb;
-}
-
-mxg::ProgramBuilder chain_program(const mxg_chain& c, int G) {
-  mxg::ProgramBuilder pb((int)c.M, G, reinterpret_cast<uint8_t*>(c.workspace));
-  const int a = pb.add_gemm((int)c.wA.N, (int)c.wA.K, c.wA.q, c.wA.s, -1, c.out_a, (int)c.wA.N);
-  pb.stage(a).aq = c.a_q;
-  pb.stage(a).as = c.a_s;
-  // B quantizes the leading wB.K columns of A's output while staging them.
-  const int b = pb.add_gemm((int)c.wB.N, (int)c.wB.K, c.wB.q, c.wB.s, a, c.out_b, (int)c.wB.N,
-                            mxg::kActBf16);
-  mxg::StageDesc& sb = pb.stage(b);
-  sb.x = c.out_a;
-  sb.ld_x = c.wA.N;
-  sb.q = c.b_q;
-  sb.s = c.b_s;
-  sb.ldq = c.wB.K;
-  const int cc = pb.add_gemm((int)c.wC.N, (int)c.wC.K, c.wC.q, c.wC.s, b, c.out_c, (int)c.wC.N);
-  pb.stage(cc).aq = c.c_q;
-  pb.stage(cc).as = c.c_s;
-  return pb;
-}
-
 // K-split state of a direct GEMM in workspace ws, partials from part_off on.
 void set_ksplit(GemmArgs& a, void* ws, size_t part_off) {
   uint8_t* w = reinterpret_cast<uint8_t*>(ws);
@@ -170,14 +130,6 @@ void set_ksplit(GemmArgs& a, void* ws, size_t part_off) {
 size_t direct_need(int M, int N, int K, size_t part_off, int group_tiles = 0) {
   const size_t pb = mxg::gemm_partial_bytes(M, N, K, group_tiles);
   return pb ? part_off + pb : 0;
-}
-
-// Chain kernel choice: by default three direct launches in stream order (B
-// quantizes A's output while staging it); MXG_CHAIN_PATH=stage runs the
-// whole chain as one stage-kernel launch.
-bool chain_on_stage_kernel() {
-  const char* force = std::getenv("MXG_CHAIN_PATH");
-  return force && std::strcmp(force, "stage") == 0;
 }
 
 int chain_direct(const mxg_chain& c, hipStream_t stream) {
@@ -258,75 +210,18 @@ int validate_wo_a(const mxg_wo_a* p) {
   return MXG_OK;
 }
 
-// WO-A kernel choice: MXG_WOA_PATH=stage runs the rotary + grouped
-// projection (and wo_b) as one stage-kernel launch; otherwise three direct
-// launches.
-bool wo_a_on_stage_kernel() {
-  const char* force = std::getenv("MXG_WOA_PATH");
-  return force && std::strcmp(force, "stage") == 0;
-}
-
-mxg::ProgramBuilder wo_a_program(const mxg_wo_a& p, int G) {
-  uint8_t* ws = reinterpret_cast<uint8_t*>(p.workspace);
-  const WoALayout l = wo_a_layout(p);
-  const int M = (int)p.M, H = p.n_heads, D = p.head_dim, Gr = p.n_groups;
-  const int GR = (int)p.wa.N, R = GR / Gr, Kg = (int)p.wa.K;
-  uint16_t* z = p.z ? p.z : (ws ? reinterpret_cast<uint16_t*>(ws + l.z) : nullptr);
-  mxg::ProgramBuilder pb(M, G, ws, l.end);
-  const int a = pb.add_gemm(GR, Kg, p.wa.q, p.wa.s, -1, z, GR, mxg::kActRope, D, p.nope_dim);
-  mxg::StageDesc& sa = pb.stage(a);
-  sa.group_tiles = R / 16;
-  sa.x = p.o;
-  sa.ld_x = p.ld_row;
-  sa.ld_head = p.ld_head;
-  sa.positions = p.positions;
-  sa.cos_sin = p.cos_sin;
-  sa.max_pos = p.max_pos;
-  sa.q = ws ? ws + l.xq : nullptr;
-  sa.s = ws ? ws + l.xs : nullptr;
-  sa.ldq = (int64_t)H * D;
-  if (p.wb.q) {
-    const int b = pb.add_gemm((int)p.wb.N, (int)p.wb.K, p.wb.q, p.wb.s, a, p.out, (int)p.wb.N,
-                              mxg::kActBf16);
-    mxg::StageDesc& sb = pb.stage(b);
-    sb.x = z;
-    sb.ld_x = GR;
-    sb.q = p.z_q;
-    sb.s = p.z_s;
-    sb.ldq = GR;
-  }
-  return pb;
-}
-
-// Workspace bytes of WO-A on either path.
+// Workspace bytes of WO-A: the rotated input's codes (and z when the caller
+// keeps none), then the K-split partials of either GEMM.
 size_t wo_a_need(const mxg_wo_a& p) {
   const WoALayout l = wo_a_layout(p);
   size_t need = l.end;
   const int R = (int)p.wa.N / p.n_groups;
   need = std::max(need, direct_need((int)p.M, (int)p.wa.N, (int)p.wa.K, l.end, R / 16));
   if (p.wb.q) need = std::max(need, direct_need((int)p.M, (int)p.wb.N, (int)p.wb.K, l.end));
-  const int G = mxg::stage_grid();
-  if (G > 0) {
-    mxg_wo_a probe = p;
-    probe.workspace = nullptr;
-    need = std::max(need, wo_a_program(probe, G).workspace_bytes());
-  }
   return need;
 }
 
-int run_program(mxg::ProgramBuilder& pb, hipStream_t stream);
-
 int wo_a_run(const mxg_wo_a& p, hipStream_t stream) {
-  if (wo_a_on_stage_kernel()) {
-    const int G = mxg::stage_grid();
-    if (G <= 0) return MXG_ERR_DEVICE;
-    mxg::ProgramBuilder pb = wo_a_program(p, G);
-    const int st = run_program(pb, stream);
-    if (st != MXG_OK || p.wb.q) return st;
-    const WoALayout l = wo_a_layout(p);
-    uint16_t* z = p.z ? p.z : reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(p.workspace) + l.z);
-    return launched(mxg::launch_quantize(z, p.M, p.wa.N, p.wa.N, p.z_q, p.z_s, stream));
-  }
   uint8_t* ws = reinterpret_cast<uint8_t*>(p.workspace);
   const WoALayout l = wo_a_layout(p);
   const int M = (int)p.M, H = p.n_heads, D = p.head_dim, G = p.n_groups;
@@ -354,11 +249,6 @@ int wo_a_run(const mxg_wo_a& p, hipStream_t stream) {
     return launched(mxg::launch_gemm(gb, stream));
   }
   return launched(mxg::launch_quantize(z, M, GR, GR, p.z_q, p.z_s, stream));
-}
-
-int run_program(mxg::ProgramBuilder& pb, hipStream_t stream) {
-  if (!pb.finish()) return MXG_ERR_SHAPE;
-  return launched(mxg::launch_program(pb.program(), pb.mb(), stream));
 }
 
 int validate_pack(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K,
@@ -391,17 +281,8 @@ const char* mxg_strerror(int status) {
 int mxg_version(void) { return 100; }
 
 size_t mxg_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M < 1 || M > MXG_MAX_GEMM_ROWS || N < 16 || N % 16 || K < 128 || K % 128 || K > MXG_MAX_K)
-    return mxg::kCtrBytes;
-  size_t need = std::max(mxg::kCtrBytes,
-                         direct_need((int)M, (int)N, (int)K, mxg::kGemmPartOffset));
-  const int G = mxg::stage_grid();
-  if (G > 0 && M <= MXG_MAX_ROWS) {
-    mxg::ProgramBuilder pb = gemm_program((int)M, (int)N, (int)K, nullptr, 0, nullptr, nullptr,
-                                          nullptr, nullptr, nullptr, nullptr, G);
-    need = std::max(need, pb.workspace_bytes());
-  }
-  return need;
+  if (!gemm_shape_ok(M, N, K)) return mxg::kCtrBytes;
+  return std::max(mxg::kCtrBytes, direct_need((int)M, (int)N, (int)K, mxg::kGemmPartOffset));
 }
 
 size_t mxg_chain_workspace_bytes(const mxg_chain* c) {
@@ -412,13 +293,6 @@ size_t mxg_chain_workspace_bytes(const mxg_chain* c) {
   size_t need = mxg::kCtrBytes;
   for (const mxg_weight* w : {&c->wA, &c->wB, &c->wC})
     need = std::max(need, direct_need(M, (int)w->N, (int)w->K, mxg::kGemmPartOffset));
-  const int G = mxg::stage_grid();
-  if (G > 0) {
-    mxg_chain probe = *c;
-    probe.workspace = nullptr;
-    mxg::ProgramBuilder pb = chain_program(probe, G);
-    need = std::max(need, pb.workspace_bytes());
-  }
   return need;
 }
 
@@ -473,13 +347,6 @@ int mxfp8_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* x_bf16, int64_t 
                          workspace);
   if (st != MXG_OK) return st;
   if ((st = check_device()) != MXG_OK) return st;
-  if (use_stage_kernel((int)M, (int)N, (int)K, x_bf16 != nullptr)) {
-    const int G = mxg::stage_grid();
-    if (G <= 0) return MXG_ERR_DEVICE;
-    mxg::ProgramBuilder pb = gemm_program((int)M, (int)N, (int)K, x_bf16, (int)ld_x, a_q, a_s,
-                                          w_q, w_s, out, reinterpret_cast<uint8_t*>(workspace), G);
-    return run_program(pb, (hipStream_t)stream);
-  }
   GemmArgs a{x_bf16, ld_x, a_q, a_s, w_q, w_s, out, (int)M, (int)N, (int)K};
   set_ksplit(a, workspace, mxg::kGemmPartOffset);
   return launched(mxg::launch_gemm(a, (hipStream_t)stream));
@@ -508,11 +375,7 @@ int mxfp8_proj_chain(const mxg_chain* c, void* stream) {
   int st = validate_chain(c, mxg_chain_workspace_bytes(c));
   if (st != MXG_OK) return st;
   if ((st = check_device()) != MXG_OK) return st;
-  if (!chain_on_stage_kernel() || c->norm_weight) return chain_direct(*c, (hipStream_t)stream);
-  const int G = mxg::stage_grid();
-  if (G <= 0) return MXG_ERR_DEVICE;
-  mxg::ProgramBuilder pb = chain_program(*c, G);
-  return run_program(pb, (hipStream_t)stream);
+  return chain_direct(*c, (hipStream_t)stream);
 }
 
 size_t mxg_wo_a_workspace_bytes(const mxg_wo_a* p) {

@@ -42,10 +42,18 @@ struct GemmArgs {
 size_t gemm_partial_bytes(int M, int N, int K, int group_tiles = 0);
 int gemm_counter_words(int M, int N, int K, int group_tiles = 0);
 
-// Workspace offsets of the direct kernels' K-split state (the first 64 KiB
-// of every workspace are counters, zero between calls).
+// Workspace layout.  The first 64 KiB are the counter region:
+//   word kCtrError (byte 20)  error word: an in-kernel wait that expired, or a
+//                             WO-A position outside its angle table
+//   kGemmCtrOffset ..         K-split tile counters (one word per tile group)
+// Every counter is back at zero when a call ends, so calls of any shape can
+// share one zero-filled workspace in turn.  K-split FP32 partial sums (and
+// WO-A's rotated input) follow from kGemmPartOffset; they need no clearing.
+constexpr int kCtrError = 5;
+constexpr size_t kCtrBytes = 8192;            // smallest workspace any call needs
+constexpr size_t kCtrRegionBytes = 64 * 1024;
 constexpr size_t kGemmCtrOffset = 8192;
-constexpr size_t kGemmPartOffset = 64 * 1024;
+constexpr size_t kGemmPartOffset = kCtrRegionBytes;
 
 hipError_t launch_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
                            uint8_t* q, uint8_t* s, hipStream_t stream);

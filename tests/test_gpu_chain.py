@@ -1,5 +1,4 @@
-"""GPU parity of mxfp8_proj_chain (three projections back to back: three
-direct-kernel launches, or one stage-kernel launch with MXG_CHAIN_PATH=stage)
+"""GPU parity of mxfp8_proj_chain (three projections back to back)
 against the oracle's chain, in the decode step's order: A on the MXFP8 layer input,
 the leading columns of A's output requantized for B, C on its own input.
 
@@ -25,11 +24,10 @@ pytestmark = pytest.mark.gpu
 SMALL = {"A": (256, 512), "B": (384, 128), "C": (320, 640)}
 
 
-@pytest.fixture(params=["direct", "stage"])
+@pytest.fixture(params=["direct"])
 def chain_path(request, monkeypatch):
-    """Both chain implementations; single GEMMs follow the same choice."""
+    """The chain's implementations (selected with MXG_CHAIN_PATH)."""
     monkeypatch.setenv("MXG_CHAIN_PATH", request.param)
-    monkeypatch.setenv("MXG_GEMM_PATH", request.param)
     return request.param
 
 
@@ -95,7 +93,7 @@ def test_chain_deterministic_and_equal_to_separate_calls(M, chain_path):
         again = mx.mxfp8_proj_chain(*g["x_a"], g["w_a"], g["w_b"], *g["x_c"], g["w_c"], workspace=ws)
         for a, b in zip(first, again):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
-    # the same GEMMs issued one by one through the stage kernel give the same bits
+    # the same GEMMs issued one by one give the same bits
     out_a = mx.mxfp8_gemm(*g["x_a"], g["w_a"], workspace=ws)
     b_q, b_s = mx.mxfp8_quantize(out_a, K=g["w_b"].K)
     out_b = mx.mxfp8_gemm(b_q, b_s, g["w_b"], workspace=ws)

@@ -17,13 +17,11 @@ from helpers import check_gemm, dev_bf16, dev_u8, host_bits, host_u8, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=["stage", "direct", "direct-m16", "direct-2d"])
+@pytest.fixture(params=["direct", "direct-m16", "direct-2d"])
 def path(request, monkeypatch):
-    """Run a test through the persistent stage kernel and the direct kernels:
-    as routed, and with the M <= 16 kernel or the 2D-tiled kernel forced
-    wherever it applies."""
+    """Run a test through the direct kernels: as routed, and with the M <= 16
+    kernel or the 2D-tiled kernel forced wherever it applies."""
     kind, _, kernel = request.param.partition("-")
-    monkeypatch.setenv("MXG_GEMM_PATH", kind)
     if kernel:
         monkeypatch.setenv("MXG_DIRECT_KERNEL", kernel)
     else:
@@ -212,14 +210,11 @@ def test_pack_is_the_documented_permutation(N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(8, 4096, 5120), (4, 5120, 8192), (33, 2048, 5120)])
-@pytest.mark.parametrize("kind", ["stage", "direct"])
-def test_workspace_left_clean(M, N, K, kind, monkeypatch):
-    """Repeated calls (stage kernel: distributed quantize, K-split tiles;
-    direct kernels: K-split tiles) on one workspace keep
-    working: every counter is reset by the call that used it (a stale tile
-    counter would make the next call's wait expire and set the error word),
-    and the results stay bitwise identical."""
-    monkeypatch.setenv("MXG_GEMM_PATH", kind)
+def test_workspace_left_clean(M, N, K, monkeypatch):
+    """Repeated calls (K-split tiles) on one workspace keep working: every
+    counter is reset by the call that used it (a stale tile counter would
+    make the next call's last-arrival test wrong), and the results stay
+    bitwise identical."""
     monkeypatch.delenv("MXG_DIRECT_KERNEL", raising=False)
     w, _ = _weights(N, K, 0)
     ws = torch.zeros(int(mx.lib().mxg_gemm_workspace_bytes(M, N, K)) + 4096, dtype=torch.uint8,
@@ -276,7 +271,6 @@ def test_one_row_both_wave_counts(N, K, waves, monkeypatch):
     # One MXFP8 row: the M <= 16 kernel runs with 4 waves per workgroup
     # (up to 16 weight steps per wave) except at K = 5120; forcing 16 waves
     # covers the other split on the same shapes.
-    monkeypatch.setenv("MXG_GEMM_PATH", "direct")
     monkeypatch.setenv("MXG_DIRECT_KERNEL", "m16")
     if waves == "16":
         monkeypatch.setenv("MXG_M16_WAVES", "16")
@@ -293,7 +287,6 @@ def test_scales_in_128x4_tiles(M, N, K, kernel, monkeypatch):
     """Activation scales in 128 x 4 tiles (the oracle's permutation of the
     row-major scales) give the row-major call's output bit for bit, on each
     direct kernel, and stay within tolerance of the oracle."""
-    monkeypatch.setenv("MXG_GEMM_PATH", "direct")
     if kernel == "routed":
         monkeypatch.delenv("MXG_DIRECT_KERNEL", raising=False)
     else:
@@ -339,7 +332,6 @@ def test_rmsnorm_128x4_output_feeds_the_gemm(M):
 def test_rows_above_48(M, fused, monkeypatch):
     # More than 48 rows: a grid of 64-row blocks on the 2D kernel (BF16 input
     # quantized by its own launch first); ragged last blocks included.
-    monkeypatch.delenv("MXG_GEMM_PATH", raising=False)
     monkeypatch.delenv("MXG_DIRECT_KERNEL", raising=False)
     run_case(M, 512, 2048, seed=M, fused=fused)
 
@@ -391,7 +383,6 @@ def test_rows_above_48_workspace_left_clean():
 def test_every_2d_plan(M, plan, monkeypatch):
     # MXG_PLAN forces the 2D kernel's (tiles per workgroup, K parts) plan:
     # every plan, with and without K split, one or several row blocks.
-    monkeypatch.setenv("MXG_GEMM_PATH", "direct")
     monkeypatch.setenv("MXG_DIRECT_KERNEL", "2d")
     monkeypatch.setenv("MXG_PLAN", plan)
     run_case(M, 512, 2048, seed=M + len(plan))
@@ -404,7 +395,6 @@ def test_every_2d_plan(M, plan, monkeypatch):
 def test_weight_tile_row_split(M, N, K, fused, rsplit, monkeypatch):
     # The M <= 16 kernel with each 16-row weight tile shared by 1, 2 or 4
     # workgroups (rows 16/rsplit each).
-    monkeypatch.setenv("MXG_GEMM_PATH", "direct")
     monkeypatch.setenv("MXG_DIRECT_KERNEL", "m16")
     monkeypatch.setenv("MXG_M16_RSPLIT", rsplit)
     run_case(M, N, K, seed=M + N + int(rsplit), fused=fused)

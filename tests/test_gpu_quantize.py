@@ -96,7 +96,6 @@ def test_exhaustive_bf16_values_fused_in_gemm(shift, monkeypatch):
     """The quantize fused into the M <= 16 GEMM kernel (one 32-block per
     lane) on the same blocks as above: every finite BF16 value, the codes
     and scales it writes out must equal the oracle's."""
-    monkeypatch.setenv("MXG_GEMM_PATH", "direct")
     monkeypatch.setenv("MXG_DIRECT_KERNEL", "m16")
     say(f"fused quantize exhaustive shift={shift}")
     b = np.arange(65536, dtype=np.uint32).astype(np.uint16)

@@ -24,10 +24,9 @@ pytestmark = pytest.mark.gpu
 SMALL = dict(n_heads=16, head_dim=512, nope=448, n_groups=2, rank=256, n_out=384)
 
 
-@pytest.fixture(params=["direct", "stage"], autouse=True)
+@pytest.fixture(params=["direct"], autouse=True)
 def woa_path(request, monkeypatch):
-    """Every test runs on both WO-A implementations (three direct launches,
-    or one stage-kernel launch)."""
+    """Every test runs on each WO-A implementation (MXG_WOA_PATH)."""
     monkeypatch.setenv("MXG_WOA_PATH", request.param)
     return request.param
 
