@@ -220,6 +220,29 @@ int mxfp8_gemm(int64_t M, int64_t N, int64_t K, const uint16_t *x_bf16,
 size_t mxg_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
+ * mxfp8_gemm_noalloc -- mxfp8_gemm for callers that cannot allocate device
+ * memory: code being captured into a HIP graph, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same operation, arguments (less the
+ * workspace), kernels and results as mxfp8_gemm.  The cross-workgroup
+ * counters and K-split partial sums that mxfp8_gemm keeps in the caller's
+ * workspace live instead in a library-owned device array of
+ * MXG_NOALLOC_SCRATCH_BYTES bytes, one per GPU the library runs on, held
+ * until the process ends.  The call itself allocates nothing.
+ *   - Shapes whose mxg_gemm_workspace_bytes() exceeds
+ *     MXG_NOALLOC_SCRATCH_BYTES are rejected with MXG_ERR_WORKSPACE before
+ *     anything is launched.
+ *   - Every call on one GPU uses that GPU's one array and each call leaves
+ *     its counters at zero for the next: calls issued in order (one stream,
+ *     or streams ordered by events) are safe; calls that may run at the same
+ *     time on one GPU race and give wrong results.
+ * Status as for mxfp8_gemm.
+ */
+#define MXG_NOALLOC_SCRATCH_BYTES (16u << 20)
+int mxfp8_gemm_noalloc(int64_t M, int64_t N, int64_t K, const uint16_t *x_bf16,
+                       int64_t ld_x, uint8_t *a_q, uint8_t *a_s, const uint8_t *w_q,
+                       const uint8_t *w_s, uint16_t *out, void *stream);
+
+/*
  * mxfp8_gemm_ex -- mxfp8_gemm on MXFP8 activations whose scale bytes come in
  * the given layout ([mxfp8] module text: the low-latency and cute-dsl
  * backends read the same F8_128x4 activation scales), so a tensor written by

@@ -19,6 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxgemm.so")
 MAX_ROWS = 48          # chain and WO-A (MXG_MAX_ROWS)
 MAX_GEMM_ROWS = 256    # mxfp8_gemm / mxfp8_gemm_ex (MXG_MAX_GEMM_ROWS)
+NOALLOC_SCRATCH_BYTES = 16 << 20   # mxfp8_gemm_noalloc's device scratch (MXG_NOALLOC_SCRATCH_BYTES)
 
 _lib = None
 
@@ -90,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.mxfp8_pack_weights.restype = ctypes.c_int
         L.mxfp8_gemm.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
         L.mxfp8_gemm.restype = ctypes.c_int
+        L.mxfp8_gemm_noalloc.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp]
+        L.mxfp8_gemm_noalloc.restype = ctypes.c_int
         L.mxfp8_gemm_ex.argtypes = [i64, i64, i64, vp, vp, ctypes.c_int32, vp, vp, vp, vp, sz, vp]
         L.mxfp8_gemm_ex.restype = ctypes.c_int
         L.mxg_gemm_workspace_bytes.argtypes = [i64, i64, i64]
@@ -300,6 +303,33 @@ def mxfp8_gemm(a_q: torch.Tensor, a_s: torch.Tensor, w: PackedWeight,
     wsz = workspace.numel() * workspace.element_size()
     _check(lib().mxfp8_gemm(M, N, K, _ptr(x), ld_x, _ptr(a_q), _ptr(a_s), _ptr(w.q), _ptr(w.s),
                             _ptr(out), _ptr(workspace), wsz, _stream(stream)))
+    return out
+
+
+def mxfp8_gemm_noalloc(a_q: torch.Tensor, a_s: torch.Tensor, w: PackedWeight,
+                       out: torch.Tensor | None = None, x: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """mxfp8_gemm without a workspace: the library keeps the K-split state in
+    its own per-GPU device scratch (calls on one GPU must not overlap).  With
+    ``out`` given, nothing is allocated on this path."""
+    M, K = a_q.shape
+    N = w.N
+    if w.K != K:
+        raise ValueError(f"weight K {w.K} != activation K {K}")
+    _expect(a_q, torch.uint8, "a_q", (M, K))
+    _expect(a_s, torch.uint8, "a_s", (M, K // 32))
+    _expect(w.q, torch.uint8, "w.q", (N * K,))
+    _expect(w.s, torch.uint8, "w.s", (N * K // 32,))
+    if out is None:
+        out = torch.empty(M, N, dtype=torch.bfloat16, device=a_q.device)
+    _expect(out, torch.bfloat16, "out", (M, N))
+    ld_x = 0
+    if x is not None:
+        if x.dim() != 2 or x.dtype != torch.bfloat16 or x.stride(1) != 1 or x.shape[0] != M:
+            raise TypeError("x must be a bfloat16 [M, >=K] tensor with unit stride along K")
+        ld_x = x.stride(0)
+    _check(lib().mxfp8_gemm_noalloc(M, N, K, _ptr(x), ld_x, _ptr(a_q), _ptr(a_s), _ptr(w.q),
+                                    _ptr(w.s), _ptr(out), _stream(stream)))
     return out
 
 

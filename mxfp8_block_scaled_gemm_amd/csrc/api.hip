@@ -7,9 +7,14 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "mx_launch.hpp"
 #include "mxgemm.h"
+
+// Scratch of mxfp8_gemm_noalloc (see there): one copy per GPU.
+constexpr size_t kScratchBytes = MXG_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -262,6 +267,32 @@ int validate_pack(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K,
   return MXG_OK;
 }
 
+// ------------------------------------------------ allocation-free GEMM
+//
+// mxfp8_gemm_noalloc keeps the K-split state of mxfp8_gemm (counters and FP32
+// partial sums, laid out as in a caller's workspace) in this library-owned
+// array: one copy per GPU, zero at load like any static object, and every
+// call leaves its counters at zero again.  In host code the array's name is
+// only a stand-in for the symbol; its address on each device is taken once
+// with hipGetSymbolAddress while that device is current, and only that
+// pointer is handed to kernels.
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up once per device).
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MXG_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MXG_ERR_DEVICE;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return MXG_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -349,6 +380,20 @@ int mxfp8_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* x_bf16, int64_t 
   if ((st = check_device()) != MXG_OK) return st;
   GemmArgs a{x_bf16, ld_x, a_q, a_s, w_q, w_s, out, (int)M, (int)N, (int)K};
   set_ksplit(a, workspace, mxg::kGemmPartOffset);
+  return launched(mxg::launch_gemm(a, (hipStream_t)stream));
+}
+
+int mxfp8_gemm_noalloc(int64_t M, int64_t N, int64_t K, const uint16_t* x_bf16, int64_t ld_x,
+                       uint8_t* a_q, uint8_t* a_s, const uint8_t* w_q, const uint8_t* w_s,
+                       uint16_t* out, void* stream) {
+  int st = validate_gemm_args(M, N, K, x_bf16, ld_x, a_q, a_s, w_q, w_s, out);
+  if (st != MXG_OK) return st;
+  if (mxg_gemm_workspace_bytes(M, N, K) > kScratchBytes) return MXG_ERR_WORKSPACE;
+  if ((st = check_device()) != MXG_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != MXG_OK) return st;
+  GemmArgs a{x_bf16, ld_x, a_q, a_s, w_q, w_s, out, (int)M, (int)N, (int)K};
+  set_ksplit(a, ws, mxg::kGemmPartOffset);
   return launched(mxg::launch_gemm(a, (hipStream_t)stream));
 }
 

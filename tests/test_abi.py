@@ -74,6 +74,31 @@ def test_gemm_rejects(lib, kw, status):
     assert gemm(lib, **kw) == status
 
 
+def gemm_noalloc(lib, M=4, N=1024, K=2048, x=None, ld_x=0, a_q=P(1), a_s=P(2), w_q=P(3), w_s=P(4),
+                 out=P(5)):
+    return lib.mxfp8_gemm_noalloc(M, N, K, x, ld_x, a_q, a_s, w_q, w_s, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(a_q=None), 1), (dict(out=None), 1), (dict(M=0), 3), (dict(M=257), 3), (dict(K=100), 3),
+    (dict(N=1000), 3), (dict(x=P(6), ld_x=1024), 3), (dict(w_q=ctypes.c_void_p(A + 1)), 2),
+    (dict(x=P(6), ld_x=2052), 2),
+    # K-split state larger than the library's scratch: rejected before any device call
+    (dict(M=128, N=16384, K=8192), 4),
+])
+def test_gemm_noalloc_rejects(lib, kw, status):
+    assert gemm_noalloc(lib, **kw) == status
+
+
+def test_noalloc_scratch_limit_matches_header(lib):
+    import mxfp8_block_scaled_gemm_amd as mx
+    text = open(os.path.join(ROOT, "include", "mxgemm.h")).read()
+    m = re.search(r"#define MXG_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == mx.NOALLOC_SCRATCH_BYTES
+    assert lib.mxg_gemm_workspace_bytes(128, 16384, 8192) > mx.NOALLOC_SCRATCH_BYTES
+    assert lib.mxg_gemm_workspace_bytes(48, 4096, 5120) <= mx.NOALLOC_SCRATCH_BYTES
+
+
 @pytest.mark.parametrize("args,status", [
     ((None, 4, 64, 64, P(1), P(2)), 1),
     ((P(0), 0, 64, 64, P(1), P(2)), 3),
