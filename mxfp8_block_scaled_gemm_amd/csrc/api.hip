@@ -145,15 +145,12 @@ int chain_direct(const mxg_chain& c, hipStream_t stream) {
   hipError_t e = mxg::launch_gemm(a, stream);
   if (e != hipSuccess) return MXG_ERR_DEVICE;
   GemmArgs b{c.out_a, c.wA.N, c.b_q, c.b_s, c.wB.q, c.wB.s, c.out_b, M, (int)c.wB.N, (int)c.wB.K};
-  if (c.norm_weight) {
-    // RMSNorm + requantize of A's leading columns by their own launch; B
-    // then reads the MXFP8 codes.
-    e = mxg::launch_rmsnorm_quantize(c.out_a, M, c.wB.K, c.wA.N, c.norm_weight, c.norm_eps,
-                                     c.b_bf16, c.wB.K, c.b_q, c.b_s, 0, stream);
-    if (e != hipSuccess) return MXG_ERR_DEVICE;
-    b.x = nullptr;
-    b.ld_x = 0;
-  }
+  // B quantizes A's leading columns while staging them (RMS-normalising
+  // them first when a gain is given), or launches that step on its own
+  // first where its kernel cannot.
+  b.norm_w = c.norm_weight;
+  b.norm_eps = c.norm_eps;
+  b.norm_y = c.b_bf16;
   set_ksplit(b, c.workspace, mxg::kGemmPartOffset);
   if ((e = mxg::launch_gemm(b, stream)) != hipSuccess) return MXG_ERR_DEVICE;
   GemmArgs cc{nullptr, 0, const_cast<uint8_t*>(c.c_q), const_cast<uint8_t*>(c.c_s), c.wC.q,

@@ -82,13 +82,59 @@ __device__ __forceinline__ void quant_block32(const v4i* v, v4i& c0, v4i& c1, in
   c1 = v4i{(int)c[4], (int)c[5], (int)c[6], (int)c[7]};
 }
 
+// Fixed-order sum of `slices` partial 16 x 16 tiles parked in LDS as FP32
+// [slice][64 lanes][4] (slice i at red + i * stride floats), spread over 256
+// threads: thread t (t < 256) adds element t of every slice in slice order,
+// so each of the 256 sums is (((s0 + s1) + s2) + ...), the same order as one
+// wave adding whole slices.
+__device__ __forceinline__ float sum_slices(const float* red, int slices, int stride, int t) {
+  float v = red[t];
+  for (int i = 1; i < slices; ++i) v += red[i * stride + t];
+  return v;
+}
+
+// Element t of a 256-element tile sum is value t % 4 of D lane t / 4.  Each
+// lane quad gathers its four values as BF16 with DPP quad permutes; the
+// quad's first thread (t % 4 == 0) returns true with D lane t / 4's values
+// 0..3 in o.  All 64 lanes of each calling wave must take part (the permutes
+// read neighbouring lanes).
+__device__ __forceinline__ bool quad_bf16(float v, int t, uint2& o) {
+  const uint32_t h = f32_to_bf16(v);
+  const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+  const uint32_t pr = h | (nb << 16);                       // on even t: values (t, t + 1)
+  const uint32_t np = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pr, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+  o.x = pr;
+  o.y = np;
+  return (t & 3) == 0;
+}
+
 // ----------------------------------------------------------- M <= 16 rows
 //
 // W waves split K; SPW: weight steps a wave holds in registers (>= its step
 // count); CH: what each thread stages: 16-byte code chunks (>= M*K/16/(64W))
 // for MXFP8 input, whole 32-element blocks (>= M*K/32/(64W)) for BF16 input.
-template <int W, int SPW, int CH, bool FQ>
-__global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
+//
+// HALF: the weight has G < tiles <= 1.5 G tiles for a grid of G workgroups.
+// Workgroup b takes full tile xcd_tile(b, G) and, for b < 2 (tiles - G), half
+// (b & 1) of leftover tile G + b / 2: rows 8 (b & 1) .. + 8, whose operand
+// bytes are whole 128-byte lines of the packed tile, in an MFMA of its own
+// whose other A rows stay zero.  Every workgroup then streams one tile or one
+// and a half, with no sum across workgroups; slots [0, SPW/2) hold the full
+// tile's steps, slots [SPW/2, SPW) the half tile's.
+//
+// NRM (BF16 input, not HALF): the rows of x are RMS-normalised before the
+// quantize.  Every workgroup stages whole rows, so it computes each row's
+// factor 1 / sqrt(mean(x^2) + eps) itself: block sums of squares through LDS,
+// one wave per row adds them in block order, then y = BF16((x * r) * w) is
+// quantized as any BF16 input is.  It runs with 8 waves, built for two
+// workgroups per CU (at most 128 registers per lane): with 16 waves the norm
+// needs more than the 64 registers that two such workgroups per CU allow,
+// and with one workgroup per CU a weight of more tiles than CUs takes a
+// second round.
+template <int W, int SPW, int CH, bool FQ, bool HALF = false, bool NRM = false>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(NRM ? W / 2 : 1)))
+void gemm_m16_kernel(GemmArgs p) {
+  static_assert(!NRM || (FQ && !HALF), "the norm runs in the BF16 staging");
   constexpr int kThreads = W * 64;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -98,14 +144,21 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
   // weight tile t, so that a small N still gives every CU a workgroup: its
   // lanes load only those rows' operand bytes (whole 128-byte lines of the
   // packed tile) and the other lanes' A rows stay zero.
-  const int rsplit = p.rsplit, sh = rsplit == 1 ? 4 : (rsplit == 2 ? 3 : 2);
-  const int unit = xcd_tile(blockIdx.x, (p.N >> 4) * rsplit);
+  const int rsplit = HALF ? 1 : p.rsplit, sh = rsplit == 1 ? 4 : (rsplit == 2 ? 3 : 2);
+  const int G = gridDim.x;
+  const int unit = xcd_tile(blockIdx.x, HALF ? G : (p.N >> 4) * rsplit);
   const int t = unit / rsplit, part = unit - t * rsplit;
   const bool mine = (r >> sh) == part;                     // my A row is this workgroup's
+  // HALF: my half of a leftover tile (th), if I have one.
+  const int th = G + (blockIdx.x >> 1), hpart = blockIdx.x & 1;
+  const bool has_half = HALF && (int)blockIdx.x < 2 * ((p.N >> 4) - G);
+  const bool mine_h = has_half && (r >> 3) == hpart;
   const int ldA = act_ld(K), ldS = scale_ld(K);
   uint8_t* s_act = smem;                                   // [M][ldA] codes
   uint8_t* s_scl = smem + M * ldA;                         // [M][ldS] scale bytes
-  v4f* s_red = reinterpret_cast<v4f*>(smem + ((M * ldA + M * ldS + 15) & ~15));  // [W][64]
+  // Partial tiles [W][64] (HALF: [2][W][64] over the activations, written
+  // once every wave is past its MFMAs).
+  v4f* s_red = reinterpret_cast<v4f*>(HALF ? smem : smem + ((M * ldA + M * ldS + 15) & ~15));
 
   // 1. Activation staging loads (L2-resident, small): issued first so that
   //    waiting for them does not wait for the weight stream.
@@ -154,25 +207,41 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
         st[4 * i + k] = buf_ld16(rx, c >= 0 ? off + 16 * k : kOutOfRange);
     }
   }
+  // The norm's gain (K BF16 values), one 16-byte piece per thread (K <= 8 x
+  // threads), staged through LDS so that it holds no registers across the
+  // weight stream (two workgroups per CU need at most 64 per lane).
+  v4i gst = {0, 0, 0, 0};
+  if constexpr (NRM)
+    gst = buf_ld16(make_rsrc(p.norm_w, (uint32_t)(K * 2)),
+                   tid < (K >> 3) ? (uint32_t)(tid * 16) : kOutOfRange);
 
   // Keep the staging loads ahead of the weight stream: the load counter
   // drains in issue order, so the staging data can then be waited for
-  // while the weights are still in flight.
+  // while the weights are still in flight.  (An execution barrier here, so
+  // that every wave issues its staging loads before any wave's weights,
+  // measured slower on MI355X: the weight stream then starts later.)
   __builtin_amdgcn_sched_barrier(0);
 
   // 2. The weight stream: all of this wave's steps, packed tile order.
+  constexpr int SF = HALF ? SPW / 2 : SPW;                 // slots of the full tile
   const int my = S > wave ? (S - wave + W - 1) / W : 0;
   const auto rw = make_rsrc(p.w_q + (int64_t)t * S * 2048, (uint32_t)(S * 2048));
   const auto rws = make_rsrc(p.w_s + (int64_t)t * S * 64, (uint32_t)(S * 64));
+  const auto rwh = make_rsrc(p.w_q + (int64_t)th * S * 2048, has_half ? (uint32_t)(S * 2048) : 0u);
+  const auto rwsh = make_rsrc(p.w_s + (int64_t)th * S * 64, has_half ? (uint32_t)(S * 64) : 0u);
   v4i wlo[SPW], whi[SPW];
   uint32_t wsc[SPW];
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
-    const int s = wave + W * j;
-    const bool ok = j < my && mine;
-    wlo[j] = buf_ld16_nt(rw, ok ? (uint32_t)(s * 2048 + lane * 16) : kOutOfRange);
-    whi[j] = buf_ld16_nt(rw, ok ? (uint32_t)(s * 2048 + 1024 + lane * 16) : kOutOfRange);
-    wsc[j] = buf_ld8(rws, ok ? (uint32_t)(s * 64 + lane) : kOutOfRange);
+    const bool full = j < SF;
+    const int jj = full ? j : j - SF;
+    const int s = wave + W * jj;
+    const bool ok = jj < my && (full ? mine : mine_h);
+    const auto rq = full ? rw : rwh;
+    const auto rsc = full ? rws : rwsh;
+    wlo[j] = buf_ld16_nt(rq, ok ? (uint32_t)(s * 2048 + lane * 16) : kOutOfRange);
+    whi[j] = buf_ld16_nt(rq, ok ? (uint32_t)(s * 2048 + 1024 + lane * 16) : kOutOfRange);
+    wsc[j] = buf_ld8(rsc, ok ? (uint32_t)(s * 64 + lane) : kOutOfRange);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -199,6 +268,66 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
     }
   } else {
     const bool writer = blockIdx.x == 0;   // one workgroup writes the codes out
+    if constexpr (NRM) {
+      // Block sums of squares (each product and sum rounded on its own), then
+      // one wave per row adds its blocks in block order: lane l takes blocks
+      // l, l + 64, ... in order, then a fixed butterfly across the lanes.
+      float* s_ss = reinterpret_cast<float*>(s_red);       // [M][KB], then r [M]
+      float* s_r = s_ss + M * KB;
+      uint8_t* s_gain = reinterpret_cast<uint8_t*>(s_red) + W * 64 * sizeof(v4f);  // [K] BF16
+      if (tid < (K >> 3)) *reinterpret_cast<v4i*>(s_gain + tid * 16) = gst;
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int c = chunk(i);
+        if (c >= 0) {
+          float ss = 0.f;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const uint32_t u = (uint32_t)st[4 * i + k][h];
+              const float a = bf16_lo(u), b = bf16_hi(u);
+              ss = ss + a * a;
+              ss = ss + b * b;
+            }
+          s_ss[c] = ss;                                    // c = row * KB + block
+        }
+      }
+      __syncthreads();
+      if (wave < M) {
+        float t = 0.f;
+        for (int b = lane; b < KB; b += 64) t = t + s_ss[wave * KB + b];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) t = t + __shfl_xor(t, o);
+        if (lane == 0) s_r[wave] = 1.0f / __builtin_sqrtf(t / (float)K + p.norm_eps);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        const int c = chunk(i);
+        if (c >= 0) {
+          const float r = s_r[c / KB];
+          const uint8_t* gb = s_gain + (c - (c / KB) * KB) * 64;   // the block's 32 gains
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const v4i gk = *reinterpret_cast<const v4i*>(gb + 16 * k);
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const uint32_t xu = (uint32_t)st[4 * i + k][h], wu = (uint32_t)gk[h];
+              const float lo = (bf16_lo(xu) * r) * bf16_lo(wu);
+              const float hi = (bf16_hi(xu) * r) * bf16_hi(wu);
+              st[4 * i + k][h] = (int)(f32_to_bf16(lo) | (f32_to_bf16(hi) << 16));
+            }
+          }
+          if (writer && p.norm_y) {
+            const int row = c / KB, col = (c - row * KB) * 32;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              *reinterpret_cast<v4i*>(p.norm_y + (int64_t)row * K + col + 8 * k) = st[4 * i + k];
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = chunk(i);
@@ -221,12 +350,14 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
   __syncthreads();
 
   // 4. MFMAs as the weight steps land.
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  v4f acc = {0.f, 0.f, 0.f, 0.f}, acch = {0.f, 0.f, 0.f, 0.f};
   const bool live = r < M;
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
-    if (j < my) {
-      const int s = wave + W * j;
+    const bool full = j < SF;
+    const int jj = full ? j : j - SF;
+    if (jj < my && (full || has_half)) {                   // wave-uniform
+      const int s = wave + W * jj;
       v4i blo = {0, 0, 0, 0}, bhi = {0, 0, 0, 0};
       int bsc = 0;
       if (live) {
@@ -235,24 +366,37 @@ __global__ __launch_bounds__(W * 64) void gemm_m16_kernel(GemmArgs p) {
         bhi = *reinterpret_cast<const v4i*>(a + 64);
         bsc = s_scl[r * ldS + 4 * s + g];
       }
-      acc = mfma_mx16(cat8(wlo[j], whi[j]), cat8(blo, bhi), acc, (int)wsc[j], bsc);
+      if (full)
+        acc = mfma_mx16(cat8(wlo[j], whi[j]), cat8(blo, bhi), acc, (int)wsc[j], bsc);
+      else
+        acch = mfma_mx16(cat8(wlo[j], whi[j]), cat8(blo, bhi), acch, (int)wsc[j], bsc);
     }
   }
 
-  // 5. Sum the W K-slices in wave order; BF16 out.
+  // 5. Sum the W K-slices in wave order (spread over four waves per tile);
+  //    BF16 out.
+  if constexpr (HALF) __syncthreads();                     // activations no longer read
   s_red[wave * 64 + lane] = acc;
+  if constexpr (HALF) s_red[(W + wave) * 64 + lane] = acch;
   __syncthreads();
-  if (tid < 64) {
-    v4f sum = s_red[lane];
-#pragma unroll
-    for (int w = 1; w < W; ++w) sum += s_red[w * 64 + lane];
-    const int m = lane & 15, n = 16 * t + 4 * (lane >> 4);
-    uint2 o;
-    o.x = f32_to_bf16(sum[0]) | (f32_to_bf16(sum[1]) << 16);
-    o.y = f32_to_bf16(sum[2]) | (f32_to_bf16(sum[3]) << 16);
-    // output rows n .. n+3 are weight rows 4 (lane / 16) .. of the tile
-    if (m < M && ((4 * (lane >> 4)) >> sh) == part)
+  const float* redf = reinterpret_cast<const float*>(s_red);
+  uint2 o;
+  if (tid < 256 && quad_bf16(sum_slices(redf, W, 256, tid), tid, o)) {
+    const int l = tid >> 2;                                 // D lane of this output quad
+    const int m = l & 15, n = 16 * t + 4 * (l >> 4);
+    // output rows n .. n+3 are weight rows 4 (l / 16) .. of the tile
+    if (m < M && ((4 * (l >> 4)) >> sh) == part)
       *reinterpret_cast<uint2*>(p.out + (int64_t)m * p.N + n) = o;
+  }
+  if constexpr (HALF) {
+    const int t4 = tid - 256;
+    if (has_half && t4 >= 0 && t4 < 256 &&                 // wave-uniform
+        quad_bf16(sum_slices(redf + W * 256, W, 256, t4), t4, o)) {
+      const int l = t4 >> 2;
+      const int m = l & 15, n = 16 * th + 4 * (l >> 4);
+      if (m < M && ((4 * (l >> 4)) >> 3) == hpart)
+        *reinterpret_cast<uint2*>(p.out + (int64_t)m * p.N + n) = o;
+    }
   }
 }
 
@@ -525,17 +669,32 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
   }
   }
 
-  // 4. Per tile: sum its WPT partial tiles in wave order (wave tt*MB + mb
-  //    sums tile tt's row block mb).
+  // 4. Per (tile, row block) unit: sum its WPT partial tiles in wave order.
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) s_red[(wave * MB + mb) * 64 + lane] = acc[mb];
   __syncthreads();
+  if (P == 1 && T * MB <= kM16Waves / 4) {
+    // Few units: each spread over four waves (one of its 256 sums per thread).
+    const int u = wave >> 2, t4 = tid & 255, l = t4 >> 2;
+    if (u < T * MB) {                                   // wave-uniform
+      const int rt = u / MB, rmb = u - rt * MB;
+      const int m = 16 * rmb + (l & 15), n = 16 * (tg * T + rt) + 4 * (l >> 4);
+      uint2 o;
+      if (quad_bf16(sum_slices(reinterpret_cast<const float*>(s_red) + u * 256, WPT, T * MB * 256, t4),
+                    t4, o) &&
+          m < M)
+        *reinterpret_cast<uint2*>(p.out + (int64_t)m * p.N + n) = o;
+    }
+    return;
+  }
+  // Otherwise wave tt * MB + mb sums tile tt's row block mb.
   const bool red = wave < T * MB;
   const int rt = wave / MB, rmb = wave - rt * MB;        // tile and row block I sum
   v4f sum = {0.f, 0.f, 0.f, 0.f};
   if (red) {
+    sum = s_red[(rt * MB + rmb) * 64 + lane];
 #pragma unroll
-    for (int i = 0; i < WPT; ++i) sum += s_red[((rt + T * i) * MB + rmb) * 64 + lane];
+    for (int i = 1; i < WPT; ++i) sum += s_red[((rt + T * i) * MB + rmb) * 64 + lane];
   }
   const int otile = tg * T + rt;
   const int m = 16 * rmb + (lane & 15), n = 16 * otile + 4 * (lane >> 4);
@@ -564,8 +723,10 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
   __syncthreads();
   if (!s_last) return;
   if (red) {
-    v4f tot = {0.f, 0.f, 0.f, 0.f};
-    for (int qq = 0; qq < P; ++qq)
+    // the P parts' sums, added in part order
+    v4f tot = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rp, (int)(otile * pstride + (rmb * 64 + lane) * 16), 0, 16));
+    for (int qq = 1; qq < P; ++qq)
       tot += __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
                                          rp, (int)(otile * pstride + ((qq * MB + rmb) * 64 + lane) * 16),
                                          0, 16));
@@ -585,10 +746,19 @@ size_t gemm_m16_lds_bytes(int M, int K, int W) {
   return (size_t)((M * act_ld(K) + M * scale_ld(K) + 15) & ~15) + (size_t)W * 64 * sizeof(v4f);
 }
 
-template <int W, int SPW, int CH, bool FQ>
-static hipError_t launch_m16(const GemmArgs& a, hipStream_t stream) {
-  auto kern = gemm_m16_kernel<W, SPW, CH, FQ>;
-  const size_t lds = gemm_m16_lds_bytes(a.M, a.K, W);
+// HALF: the two sets of partial tiles overlay the activations.
+size_t gemm_m16_half_lds_bytes(int M, int K, int W) {
+  const size_t act = (size_t)((M * act_ld(K) + M * scale_ld(K) + 15) & ~15);
+  const size_t red = (size_t)2 * W * 64 * sizeof(v4f);
+  return act > red ? act : red;
+}
+
+template <int W, int SPW, int CH, bool FQ, bool HALF = false, bool NRM = false>
+static hipError_t launch_m16(const GemmArgs& a, int grid, hipStream_t stream) {
+  auto kern = gemm_m16_kernel<W, SPW, CH, FQ, HALF, NRM>;
+  const size_t lds = HALF  ? gemm_m16_half_lds_bytes(a.M, a.K, W)
+                     : NRM ? gemm_m16_lds_bytes(a.M, a.K, W) + (size_t)a.K * 2
+                           : gemm_m16_lds_bytes(a.M, a.K, W);
   static bool configured = false;   // raise the dynamic-LDS limit once per instance
   if (!configured) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -596,7 +766,7 @@ static hipError_t launch_m16(const GemmArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL(kern, dim3(a.N / 16 * a.rsplit), dim3(W * 64), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(W * 64), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -604,17 +774,63 @@ static hipError_t launch_m16(const GemmArgs& a, hipStream_t stream) {
 // 32-element blocks (BF16 input), rounded up to an instantiated count.
 template <int W, int SPW, bool FQ>
 static hipError_t launch_m16_ch(const GemmArgs& a, int ch, hipStream_t stream) {
+  const int grid = a.N / 16 * a.rsplit;
   if constexpr (FQ) {
-    if (ch <= 1) return launch_m16<W, SPW, 1, FQ>(a, stream);
-    if (ch <= 2) return launch_m16<W, SPW, 2, FQ>(a, stream);
+    if (ch <= 1) return launch_m16<W, SPW, 1, FQ>(a, grid, stream);
+    if (ch <= 2) return launch_m16<W, SPW, 2, FQ>(a, grid, stream);
   } else {
-    if (ch <= 2) return launch_m16<W, SPW, 2, FQ>(a, stream);
-    if (ch <= 4) return launch_m16<W, SPW, 4, FQ>(a, stream);
+    if (ch <= 2) return launch_m16<W, SPW, 2, FQ>(a, grid, stream);
+    if (ch <= 4) return launch_m16<W, SPW, 4, FQ>(a, grid, stream);
     if constexpr (W == 16) {
-      if (ch <= 8) return launch_m16<W, SPW, 8, FQ>(a, stream);
-      if (ch <= 16) return launch_m16<W, SPW, 16, FQ>(a, stream);
+      if (ch <= 8) return launch_m16<W, SPW, 8, FQ>(a, grid, stream);
+      if (ch <= 16) return launch_m16<W, SPW, 16, FQ>(a, grid, stream);
     }
   }
+  return hipErrorInvalidValue;
+}
+
+// HALF launches: 16 waves, one workgroup per CU (grid = G), SPW = 2 x the
+// full tile's slots.
+template <int SPW, bool FQ>
+static hipError_t launch_m16_half_ch(const GemmArgs& a, int G, int ch, hipStream_t stream) {
+  if constexpr (FQ) {
+    if (ch <= 1) return launch_m16<16, SPW, 1, FQ, true>(a, G, stream);
+    if (ch <= 2) return launch_m16<16, SPW, 2, FQ, true>(a, G, stream);
+  } else {
+    if (ch <= 2) return launch_m16<16, SPW, 2, FQ, true>(a, G, stream);
+    if (ch <= 4) return launch_m16<16, SPW, 4, FQ, true>(a, G, stream);
+    if constexpr (SPW < 8) {                               // 8 slots + 8 chunks would spill
+      if (ch <= 8) return launch_m16<16, SPW, 8, FQ, true>(a, G, stream);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool FQ>
+static hipError_t launch_m16_half(const GemmArgs& a, int G, int sf, int ch, hipStream_t stream) {
+  if (sf <= 1) return launch_m16_half_ch<2, FQ>(a, G, ch, stream);
+  if (sf <= 2) return launch_m16_half_ch<4, FQ>(a, G, ch, stream);
+  if (sf <= 3) return launch_m16_half_ch<6, FQ>(a, G, ch, stream);
+  if (sf <= 4) return launch_m16_half_ch<8, FQ>(a, G, ch, stream);
+  return hipErrorInvalidValue;
+}
+
+// The normalising BF16 staging: 8 waves, one workgroup per weight tile
+// (rsplit as chosen), up to two 32-blocks per thread, up to 4 weight steps
+// per wave (K <= 4096).
+constexpr int kNormWaves = 8;
+
+template <int SPW>
+static hipError_t launch_m16_norm_ch(const GemmArgs& a, int ch, hipStream_t stream) {
+  const int grid = a.N / 16 * a.rsplit;
+  if (ch <= 1) return launch_m16<kNormWaves, SPW, 1, true, false, true>(a, grid, stream);
+  if (ch <= 2) return launch_m16<kNormWaves, SPW, 2, true, false, true>(a, grid, stream);
+  return hipErrorInvalidValue;
+}
+
+static hipError_t launch_m16_norm(const GemmArgs& a, int spw, int ch, hipStream_t stream) {
+  if (spw <= 2) return launch_m16_norm_ch<2>(a, ch, stream);
+  if (spw <= 4) return launch_m16_norm_ch<4>(a, ch, stream);   // more would spill
   return hipErrorInvalidValue;
 }
 
@@ -823,14 +1039,28 @@ int gemm_counter_words(int M, int N, int K, int group_tiles) {
   return pl.P > 1 ? rb * (N / 16 / pl.T) : 0;
 }
 
-// MXG_DIRECT_KERNEL ("m16" / "2d") forces the kernel where both apply
-// (tests use it to cover both on the same shapes); 0 = choose.
+// MXG_DIRECT_KERNEL ("m16" / "2d" / "m16h") forces the kernel where it
+// applies (tests use it to cover each on the same shapes); 0 = choose.
 int forced_kernel() {
   const char* e = std::getenv("MXG_DIRECT_KERNEL");
   if (!e) return 0;
   if (std::strcmp(e, "m16") == 0) return 1;
   if (std::strcmp(e, "2d") == 0) return 2;
+  if (std::strcmp(e, "m16h") == 0) return 3;
   return 0;
+}
+
+// Whether the M <= 16 kernel's HALF form takes the shape: G < tiles <= 1.5 G
+// (one tile per workgroup plus half a leftover tile for some), at most 4
+// full-tile slots per wave (K <= 8192), the activation in LDS, no grouping.
+// MXFP8 input of at most 8 chunks per thread (4 with 8 weight slots, which
+// would spill with more), or BF16 input of at most two 32-blocks per thread
+// (M * K <= 65536).
+bool gemm_m16_half_fits(const GemmArgs& a, int G) {
+  const int tiles = a.N / 16, S = a.K / 128;
+  if (a.M > 16 || a.group_tiles != 0 || tiles <= G || 2 * (tiles - G) > G || S > 64) return false;
+  if (gemm_m16_half_lds_bytes(a.M, a.K, 16) > 160 * 1024) return false;
+  return a.x ? a.M * a.K <= 65536 : a.M * a.K / 16 <= (S > 48 ? 4 : 8) * 1024;
 }
 
 // Whether the M <= 16 kernel can stage this activation in LDS.
@@ -844,8 +1074,10 @@ bool gemm_m16_fits(int M, int K, int W) {
 // than 16 waves at K = 1536, 4096 and 8192 on MI355X, but 3 % slower at
 // K = 5120 (10 steps per wave against 2 or 3), which keeps 16.  With more
 // rows, or BF16 input, the activation staging and quantize spread over 16
-// waves win.  MXG_M16_WAVES=16 forces 16 waves for one row as well (tests
-// cover both); 0 is returned when the kernel cannot take the shape.
+// waves win (4 and 8 waves measured 0.2-0.9 us slower than 16 for BF16
+// input at N 4096, K 5120, M = 1..8).  MXG_M16_WAVES=16 forces 16 waves for
+// one row as well (tests cover both); 0 is returned when the kernel cannot
+// take the shape.
 int m16_waves(int M, int K, bool fq) {
   const int S = K / 128;
   const char* e = std::getenv("MXG_M16_WAVES");
@@ -874,6 +1106,16 @@ int m16_row_split(int N, int K, bool) {
     if (v == 1 || v == 2 || v == 4) return v;
   }
   return (N / 16) * 2 <= device_cus() && K >= 4096 ? 2 : 1;
+}
+
+// MXFP8 input of at most 4 rows on a weight of G < tiles <= 1.5 G tiles and
+// K >= 4096: two half-tile workgroups per tile (2 x tiles workgroups of 16
+// waves).  Measured on MI355X at N 5120, K 8192: 9.8-10.5 us at M = 1 and
+// 10.4-11.3 at M = 4, against 10.5-11.1 and 11.1-11.4 for the 2D kernel and
+// 11.2 and 11.6 for one tile plus half a leftover tile per workgroup.
+bool m16_half_tiles_wide(int M, int N, int K, bool fq) {
+  const int tiles = N / 16, G = device_cus();
+  return !fq && M <= 4 && K >= 4096 && tiles > G && 2 * (tiles - G) <= G;
 }
 
 hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
@@ -908,6 +1150,48 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
     return launch_2d_mb<false>(a, pl.T, pl.SPW, stream);
   }
   const int S = a.K / 128;
+  int force = forced_kernel();                             // tests: 1 = M <= 16, 2 = 2D, 3 = HALF
+  if (a.norm_w) {
+    // The norm runs in the M <= 16 kernel's BF16 staging when that kernel
+    // takes the shape with the quantize inside (16 waves, at most two
+    // 32-blocks per thread and M * K <= 65536 per CU round); otherwise
+    // RMSNorm + MXFP8 runs as its own launch and the GEMM reads the codes.
+    constexpr int NW = kNormWaves, NT = NW * 64;
+    const int per_cu = (a.N / 16 + device_cus() - 1) / device_cus();
+    const bool inline_ok = a.x && a.M <= 16 && (a.M * a.K / 32) * per_cu <= 2048 &&
+                           a.M * a.K / 32 <= 2 * NT && a.K <= 8 * NT && (S + NW - 1) / NW <= 4 &&
+                           gemm_m16_lds_bytes(a.M, a.K, NW) + (size_t)a.K * 2 <= 160 * 1024 &&
+                           force != 2 && force != 3;
+    if (inline_ok) {
+      GemmArgs b = a;
+      b.rsplit = m16_row_split(a.N, a.K, true);
+      return launch_m16_norm(b, (S + NW - 1) / NW, (a.M * a.K / 32 + NT - 1) / NT, stream);
+    }
+    hipError_t e = launch_rmsnorm_quantize(a.x, a.M, a.K, a.ld_x, a.norm_w, a.norm_eps, a.norm_y,
+                                           a.K, a.a_q, a.a_s, 0, stream);
+    if (e != hipSuccess) return e;
+    GemmArgs b = a;
+    b.x = nullptr;
+    b.norm_w = nullptr;
+    return launch_gemm(b, stream);
+  }
+  // A weight of G < tiles <= 1.5 G tiles with BF16 input: one tile per CU
+  // plus half a leftover tile for some, no sum across workgroups.  A read of
+  // the weight alone in this order takes 8.0 us on MI355X at N 5120, K 8192,
+  // against 8.9 us for one tile per workgroup (a second round on a quarter of
+  // the CUs) and 8.3 us for 640 half tiles; with BF16 input the GEMM measured
+  // 11.5 / 12.2 us at M = 1 / 4 against 12.3 / 13.4 for the next best form.
+  // (With MXFP8 input two half-tile workgroups per tile measured faster up to
+  // 4 rows, and the 2D kernel above; see m16_row_split.)
+  if ((force == 3 || (force == 0 && a.x)) && gemm_m16_half_fits(a, device_cus())) {
+    GemmArgs h = a;
+    h.rsplit = 1;
+    const int sf = (S + 15) / 16;
+    if (!a.x) return launch_m16_half<false>(h, device_cus(), sf, (a.M * a.K / 16 + 1023) / 1024,
+                                            stream);
+    return launch_m16_half<true>(h, device_cus(), sf, (a.M * a.K / 32 + 1023) / 1024, stream);
+  }
+  if (force == 3) force = 0;                               // HALF does not take the shape
   const Plan pl = choose_plan(a.M, a.N, a.K, a.group_tiles, device_cus());
   // One full-K tile per workgroup with the whole activation in LDS unless
   // the model gives a 2D plan at most 3/4 of its time: the M <= 16 kernel
@@ -922,13 +1206,17 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
   // double).
   const int per_cu = (a.N / 16 + device_cus() - 1) / device_cus();
   const bool fq_inline = fq && (a.M * a.K / 32) * per_cu <= 2048;
-  const int force = forced_kernel();                       // tests: 1 = M <= 16 kernel, 2 = 2D
-  const int W = m16_waves(a.M, a.K, fq && fq_inline);
-  if (W && (force == 1 || (force == 0 && m16_fast))) {
+  const bool wide_halves = force == 0 && m16_half_tiles_wide(a.M, a.N, a.K, fq) &&
+                           std::getenv("MXG_M16_WAVES") == nullptr &&
+                           std::getenv("MXG_M16_RSPLIT") == nullptr;
+  const int W = wide_halves && gemm_m16_fits(a.M, a.K, 16) && (S + 15) / 16 <= m16_max_spw(16)
+                    ? 16
+                    : m16_waves(a.M, a.K, fq && fq_inline);
+  if (W && (force == 1 || (force == 0 && (m16_fast || wide_halves)))) {
     const int steps = (S + W - 1) / W;                     // weight steps per wave
     const int per = fq ? a.M * a.K / 32 : a.M * a.K / 16;  // 32-blocks, or 16-byte chunks
     const int ch = (per + W * 64 - 1) / (W * 64);
-    a.rsplit = m16_row_split(a.N, a.K, fq);
+    a.rsplit = wide_halves ? 2 : m16_row_split(a.N, a.K, fq);
     if (!fq) return launch_m16_w<false>(a, W, steps, ch, stream);
     // In-kernel quantize while the weight stream is in flight when the
     // activation is small enough (every workgroup quantizes all of it, one

@@ -35,6 +35,13 @@ struct GemmArgs {
   // M <= 16 kernel: workgroups per 16-row weight tile (1, 2 or 4; set by the
   // launcher).
   int rsplit = 1;
+  // BF16 input only: RMS-normalise each row of x (gain norm_w [K], BF16;
+  // norm_eps inside the square root) before the quantize, as
+  // launch_rmsnorm_quantize does; the normalised BF16 rows are also written
+  // to norm_y [M, K] when it is non-null.
+  const uint16_t* norm_w = nullptr;
+  float norm_eps = 0.f;
+  uint16_t* norm_y = nullptr;
 };
 
 // Bytes of FP32 partials the GEMM of this shape needs (0: no K split); the

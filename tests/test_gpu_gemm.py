@@ -108,6 +108,36 @@ def test_wide_tiles_full_size_outliers(M, N, K, path):
     run_case(M, N, K, seed=0, outliers=True)
 
 
+@pytest.mark.parametrize("M,N,K,fused", [
+    (1, 5120, 8192, False), (4, 5120, 8192, True), (5, 5120, 8192, True), (8, 5120, 8192, False),
+    (3, 4112, 1024, False),    # one leftover tile: two workgroups take half of it
+    (16, 6144, 2048, False),   # every workgroup takes half a leftover tile
+    (13, 6144, 2048, True),
+    (7, 4352, 4096, False),
+])
+def test_half_tile_plan(M, N, K, fused, monkeypatch):
+    """Weights of G < tiles <= 1.5 G tiles (G = 256 CUs): one tile per
+    workgroup plus half a leftover tile for some.  Within tolerance of the
+    oracle, and bitwise equal to the one-tile-per-workgroup kernel with 16
+    waves, which gives every wave the same steps and sums them in the same
+    order."""
+    monkeypatch.setenv("MXG_DIRECT_KERNEL", "m16h")
+    run_case(M, N, K, seed=N + M, fused=fused)
+    case = synth.gemm_case(M, N, K, seed=N + M)
+    w, _ = _weights(N, K, 1)
+    x = case["x"].cuda()
+    aq = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+    as_ = torch.empty(M, K // 32, dtype=torch.uint8, device="cuda")
+    a_q, a_s = mx.mxfp8_quantize(x)
+    half = mx.mxfp8_gemm(aq, as_, w, x=x) if fused else mx.mxfp8_gemm(a_q, a_s, w)
+    monkeypatch.setenv("MXG_DIRECT_KERNEL", "m16")
+    monkeypatch.setenv("MXG_M16_WAVES", "16")
+    monkeypatch.setenv("MXG_M16_RSPLIT", "1")
+    one = mx.mxfp8_gemm(a_q, a_s, w)
+    torch.cuda.synchronize()
+    assert torch.equal(half.view(torch.int16), one.view(torch.int16))
+
+
 def test_one_hot_weights_bitwise():
     M, N, K = 9, 256, 1024
     rng = np.random.default_rng(0)
