@@ -5,16 +5,22 @@ A step is one pass of the decode-bucket workload: for each batch size M in
 multiplied by an MXFP8 weight [4096, 5120] (BF16 out), quantize and GEMM in
 one mxfp8_gemm launch.  Inputs are resident in HBM before the timed region.
 Weights rotate over enough identical copies (>= 512 MB) that no launch finds
-its weight in the 256 MB Infinity Cache.  The K timed steps are captured in a
-HIP graph (torch.cuda.CUDAGraph) and replayed once between HIP events on the
-launch stream.
+its weight in the 256 MB Infinity Cache.  The K timed steps are captured in
+one HIP graph (torch.cuda.CUDAGraph); the graph is replayed R >= 30 times,
+each replay (exactly K steps) bracketed by HIP events on the launch stream
+and a device synchronize, and the median replay gives the figures (the
+spread over the replays is reported beside it).
 
 Prints one JSON line: throughput in algorithmic GB/s (weights + weight scales
 + BF16 activations + the MXFP8 activations written + BF16 output, per step),
-the GEMM kernel's roofline against MI355X's 8 TB/s HBM peak, per-configuration
-latencies, and the CPU oracle's throughput on the same workload.
+the dominant kernel's roofline against MI355X's 8 TB/s HBM peak, the launch
+floor (a one-workgroup launch in the same graph timing), per-configuration
+latencies with the kernel launches per call and the MFMA activity from the
+committed counter profile, and the CPU oracle's throughput on the same
+workload (all host threads, and one).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cases] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--replays R]
+                    [--no-cases] [--no-cpu] [--only NAME] [--roofline-only]
 """
 from __future__ import annotations
 
@@ -38,6 +44,9 @@ MALL_BYTES = 256 << 20         # Infinity Cache
 ROTATE_BYTES = 512 << 20       # weight bytes cycled through before a copy is reused
 
 
+REPLAYS = 30                   # graph replays per timing; the median is reported
+MFMA_PEAK_FLOPS = 5.0e15       # MI355X dense FP8 (MXFP8) matrix peak
+CASES_PROFILE = os.path.join(ROOT, "profiles", "bench_cases_mfma_and_launches.md")
 ROOFLINE_PROFILE = os.path.join(ROOT, "profiles", "gemm_m16_kernel_fq_M1-2-4_N4096_K5120.md")
 ROOFLINE_KERNEL = "gemm_m16_kernel<16,3,1,true> (M=1,2,4 with BF16 input, N=4096 K=5120)"
 ROOFLINE_MS = (1, 2, 4)
@@ -45,19 +54,47 @@ ROOFLINE_SOURCES = [os.path.join(ROOT, "mxfp8_block_scaled_gemm_amd", "csrc", f)
                     for f in ("gemm.hip", "mx_device.hpp")]
 
 
-def profiled_traffic():
-    """HBM bytes per launch of the roofline kernel from its committed counter
-    summary (FETCH_SIZE + WRITE_SIZE, calibrated), or None when the kernel's
-    sources changed since the counters were taken."""
+def _sources_sha():
     import hashlib
+    return [hashlib.sha256(open(f, "rb").read()).hexdigest() for f in ROOFLINE_SOURCES]
+
+
+def profiled_roofline():
+    """From the roofline kernel's committed summary: HBM bytes per launch
+    (FETCH_SIZE + WRITE_SIZE, calibrated) and the kernel-trace average
+    duration in us, each None when the kernel's sources changed since."""
     try:
         fields = dict(l.split(":", 1) for l in open(ROOFLINE_PROFILE).read().splitlines()
-                      if l.startswith(("traffic_bytes_per_launch:", "sources_sha256:")))
-        want = fields["sources_sha256"].split()
-        have = [hashlib.sha256(open(f, "rb").read()).hexdigest() for f in ROOFLINE_SOURCES]
-        return int(fields["traffic_bytes_per_launch"]) if want == have else None
+                      if l.startswith(("traffic_bytes_per_launch:", "sources_sha256:",
+                                       "trace_avg_ns:")))
+        if fields["sources_sha256"].split() != _sources_sha():
+            return None, None
+        return (int(fields["traffic_bytes_per_launch"]),
+                float(fields["trace_avg_ns"]) / 1e3 if "trace_avg_ns" in fields else None)
     except (OSError, KeyError, ValueError):
-        return None
+        return None, None
+
+
+def profiled_cases():
+    """Per-case counters from the committed profile of every bench case:
+    {case: {"launches": kernel launches per call, "mops": F8 MFMA MOPS per
+    call, "busy": SQ_VALU_MFMA_BUSY_CYCLES per call}}, empty when the GEMM
+    sources changed since the profile was taken."""
+    out = {}
+    try:
+        text = open(CASES_PROFILE).read()
+        sha = [l.split(":", 1)[1].split() for l in text.splitlines() if l.startswith("sources_sha256:")]
+        if not sha or sha[0] != _sources_sha():
+            return {}
+        for line in text.splitlines():
+            if line.startswith("| `") and line.count("|") >= 6:
+                cells = [c.strip() for c in line.strip().strip("|").split("|")]
+                name = cells[0].strip("`")
+                out[name] = {"launches": int(cells[1]), "mops": float(cells[2]),
+                             "busy": float(cells[3])}
+    except (OSError, ValueError, IndexError):
+        return {}
+    return out
 
 
 def mx_bytes(rows: int, K: int) -> int:
@@ -79,21 +116,35 @@ def weight_copies(N: int, K: int, dev):
     return [w.clone() for _ in range(n)]
 
 
-def time_graph(fn, reps: int, stream) -> float:
-    """Capture fn(i) for i < reps into one graph, replay it once between
-    events; returns milliseconds for the reps calls."""
+def time_graph(fn, reps: int, stream, replays: int = None) -> dict:
+    """Capture fn(i) for i < reps into one graph and replay it `replays`
+    times, each replay between HIP events on `stream` followed by a device
+    synchronize.  Returns the median, minimum and maximum milliseconds of one
+    replay (reps calls)."""
+    replays = REPLAYS if replays is None else replays
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         for i in range(reps):
             fn(i)
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
-        start.record(stream)
-        g.replay()
-        end.record(stream)
+        g.replay()                                     # first replay: not timed
     torch.cuda.synchronize()
-    return start.elapsed_time(end)
+    times = []
+    for _ in range(replays):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            start.record(stream)
+            g.replay()
+            end.record(stream)
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end))
+    times.sort()
+    return {"ms": times[len(times) // 2], "min": times[0], "max": times[-1], "replays": replays}
+
+
+def per_call_us(t: dict, reps: int) -> dict:
+    return {k: t[k] * 1e3 / reps for k in ("ms", "min", "max")}
 
 
 def decode_bucket(dev, steps: int, warmup: int, stream):
@@ -119,30 +170,25 @@ def decode_bucket(dev, steps: int, warmup: int, stream):
         for i in range(warmup):
             step(i)
     torch.cuda.synchronize()
-    ms = time_graph(lambda i: step(warmup + i), steps, stream)
+    t = time_graph(lambda i: step(warmup + i), steps, stream)
     step_bytes = sum(gemm_bytes(M, N, K, True) for M in Ms)
-    launches = steps * len(Ms)
-    per_launch_s = ms * 1e-3 / launches
-    per_launch_bytes = step_bytes / len(Ms)
     per_m = {}
     for M in Ms:     # one graph per M, for the per-size latency
-        wq_list = copies
-
         def one(i, M=M):
             x, aq, as_, out = bufs[M]
-            mx.mxfp8_gemm(aq, as_, wq_list[i % len(wq_list)], out=out, x=x)
-        reps = 400
-        t = time_graph(one, reps, stream) * 1e3 / reps
-        per_m[str(M)] = {"us": round(t, 3),
-                         "GBs": round(gemm_bytes(M, N, K, True) / (t * 1e-6) / 1e9, 1)}
+            mx.mxfp8_gemm(aq, as_, copies[i % len(copies)], out=out, x=x)
+        u = per_call_us(time_graph(one, 400, stream), 400)
+        per_m[str(M)] = {"us": round(u["ms"], 3), "us_min": round(u["min"], 3),
+                         "us_max": round(u["max"], 3),
+                         "GBs": round(gemm_bytes(M, N, K, True) / (u["ms"] * 1e-6) / 1e9, 1)}
     return {
-        "ms_total": ms,
-        "ms_per_step": ms / steps,
+        "ms_per_step": t["ms"] / steps,
+        "ms_per_step_min": t["min"] / steps,
+        "ms_per_step_max": t["max"] / steps,
+        "replays": t["replays"],
         "step_bytes": step_bytes,
-        "GBs": step_bytes * steps / (ms * 1e-3) / 1e9,
-        "kernel_us": per_launch_s * 1e6,
-        "kernel_GBs": per_launch_bytes / per_launch_s / 1e9,
-        "per_launch_bytes": per_launch_bytes,
+        "GBs": step_bytes * steps / (t["ms"] * 1e-3) / 1e9,
+        "kernel_us": t["ms"] * 1e3 / (steps * len(Ms)),
         "per_m": per_m,
         "copies": len(copies),
     }
@@ -154,7 +200,7 @@ def roofline_kernel(dev, stream, reps: int = 200):
     GEMMs of the step (three of its four launches, about 70 % of its time).
     `reps` rounds of those three launches on rotated weights in one HIP
     graph, timed with HIP events on its launch stream; per launch: the mean
-    algorithmic bytes over the three, and the mean duration."""
+    algorithmic bytes over the three, and the median replay's mean duration."""
     N, K = 4096, 5120
     copies = weight_copies(N, K, dev)
     x8 = synth.gemm_case(8, N, K, seed=0)["x"].to(dev)
@@ -170,9 +216,10 @@ def roofline_kernel(dev, stream, reps: int = 200):
         for i in range(10):
             call(i)
     launches = reps * len(ROOFLINE_MS)
-    us = time_graph(call, reps, stream) * 1e3 / launches
+    u = per_call_us(time_graph(call, reps, stream), launches)
     b = sum(gemm_bytes(M, N, K, True) for M in ROOFLINE_MS) / len(ROOFLINE_MS)
-    return {"us": us, "bytes": b, "GBs": b / (us * 1e-6) / 1e9, "launches": launches}
+    return {"us": u["ms"], "us_min": u["min"], "us_max": u["max"], "bytes": b,
+            "GBs": b / (u["ms"] * 1e-6) / 1e9, "launches": launches}
 
 
 def stream_ceiling(dev, stream, reps: int = 600):
@@ -189,17 +236,52 @@ def stream_ceiling(dev, stream, reps: int = 600):
     with torch.cuda.stream(stream):
         for i in range(20):
             call(i)
-    us = time_graph(call, reps, stream) * 1e3 / reps
+    u = per_call_us(time_graph(call, reps, stream), reps)
     b = mx_bytes(N, K)
-    return {"us": us, "bytes": b, "GBs": b / (us * 1e-6) / 1e9}
+    return {"us": u["ms"], "bytes": b, "GBs": b / (u["ms"] * 1e-6) / 1e9}
+
+
+def launch_floor(dev, stream, reps: int = 600):
+    """The per-launch floor in the same graph timing: the read-only probe on
+    one 16 x 128 tile (one workgroup, 2 KiB), launched back to back."""
+    w = mx.PackedWeight.from_bf16(synth.gemm_case(1, 16, 128, seed=0)["w"].to(dev))
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def call(i):
+        mx.hbm_read_probe(w, sink)
+    with torch.cuda.stream(stream):
+        for i in range(20):
+            call(i)
+    return per_call_us(time_graph(call, reps, stream), reps)["ms"]
+
+
+def case_record(name: str, u: dict, nbytes: int, prof: dict, floor_us: float, **extra) -> dict:
+    """One bench case: median us per call (and the replays' spread), GB/s,
+    fraction of 8 TB/s, kernel launches per call and their floor, and MFMA
+    activity from the committed counter profile (null when not profiled for
+    the current sources)."""
+    rec = {"us": round(u["ms"], 3), "us_min": round(u["min"], 3), "us_max": round(u["max"], 3),
+           "GBs": round(nbytes / (u["ms"] * 1e-6) / 1e9, 1),
+           "frac": round(nbytes / (u["ms"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    rec.update(extra)
+    pc = prof.get(name)
+    if pc:
+        rec["launches"] = pc["launches"]
+        rec["launch_floor_us"] = round(pc["launches"] * floor_us, 3)
+        # issued scaled-MFMA FLOPs (one MOP = 512 flops) over the call's time
+        # against the dense FP8 peak, and the matrix-core busy fraction
+        rec["mfma_util"] = round(pc["mops"] * 512 / (u["ms"] * 1e-6) / MFMA_PEAK_FLOPS, 5)
+        rec["mfma_busy"] = round(pc["busy"] / (256 * 4 * u["ms"] * 1e-6 * 2.4e9), 5)
+    else:
+        rec["launches"] = rec["launch_floor_us"] = rec["mfma_util"] = rec["mfma_busy"] = None
+    return rec
 
 
 def chain_case(dev, stream, M: int, reps: int = 200, norm: bool = False):
     """The three-projection chain (A 2048x5120, requantize 1536 columns, B
-    8192x1536, C 5120x8192), weights rotated over copies; the library's
-    default chain path unless MXG_CHAIN_PATH says otherwise.  norm: the
-    1536 columns are RMS-normalised before the requantize (one more launch;
-    the gain's 3 KB and the normalised BF16 are counted)."""
+    8192x1536, C 5120x8192), weights rotated over copies.  norm: the 1536
+    columns are RMS-normalised before the requantize (the gain's 3 KB and the
+    normalised BF16 are counted).  Returns (per-call us, algorithmic bytes)."""
     case = synth.chain_case(M, seed=0)
     w = {k: mx.PackedWeight.from_bf16(case[k].to(dev)) for k in ("w_a", "w_b", "w_c")}
     per = sum(mx_bytes(v.N, v.K) for v in w.values())
@@ -214,19 +296,19 @@ def chain_case(dev, stream, M: int, reps: int = 200, norm: bool = False):
             torch.empty(M, 5120, dtype=torch.bfloat16, device=dev))
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
     gain = synth.rmsnorm_case(1, 1536, seed=1)["w"].to(dev) if norm else None
+    b_bf16 = torch.empty(M, 1536, dtype=torch.bfloat16, device=dev) if norm else None
 
     def call(i):
         cw = cop[i % n]
         mx.mxfp8_proj_chain(*a, cw["w_a"], cw["w_b"], *c, cw["w_c"], outs=outs, workspace=ws,
-                            norm_weight=gain, norm_eps=synth.RMSNORM_EPS)
+                            norm_weight=gain, norm_eps=synth.RMSNORM_EPS, b_bf16=b_bf16)
     with torch.cuda.stream(stream):
         for i in range(10):
             call(i)
-    us = time_graph(call, reps, stream) * 1e3 / reps
+    u = per_call_us(time_graph(call, reps, stream), reps)
     b = per + mx_bytes(M, 5120) + mx_bytes(M, 8192) + 2 * M * (2048 + 8192 + 5120) \
-        + 2 * M * 1536 + mx_bytes(M, 1536) + (2 * 1536 if norm else 0)
-    return {"us": round(us, 3), "GBs": round(b / (us * 1e-6) / 1e9, 1),
-            "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        + 2 * M * 1536 + mx_bytes(M, 1536) + ((2 * 1536 + 2 * M * 1536) if norm else 0)
+    return u, b
 
 
 def rmsnorm_case(dev, stream, M: int, K: int, ld: int, reps: int = 400):
@@ -244,68 +326,8 @@ def rmsnorm_case(dev, stream, M: int, K: int, ld: int, reps: int = 400):
     with torch.cuda.stream(stream):
         for i in range(10):
             call(i)
-    us = time_graph(call, reps, stream) * 1e3 / reps
-    b = 2 * M * K + 2 * K + 2 * M * K + mx_bytes(M, K)
-    return {"us": round(us, 3), "GBs": round(b / (us * 1e-6) / 1e9, 1)}
-
-
-def extra_cases(dev, stream):
-    """Latency of the other single-GEMM configurations (MXFP8 inputs)."""
-    out = {}
-    specs = [("single M4 N1024 K2048", [(4, 1024, 2048)], False)]
-    for (N, K) in ((4096, 5120), (5120, 8192), (8192, 1536)):
-        specs.append((f"wide N{N} K{K}", [(M, N, K) for M in (16, 32, 48)], True))
-    for name, shapes, outliers in specs:
-        N, K = shapes[0][1], shapes[0][2]
-        copies = weight_copies(N, K, dev)
-        for (M, _, _) in shapes:
-            x = synth.gemm_case(M, 16, K, seed=0, outliers=outliers)["x"].to(dev)
-            aq, as_ = mx.mxfp8_quantize(x)
-            o = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-
-            def call(i):
-                mx.mxfp8_gemm(aq, as_, copies[i % len(copies)], out=o)
-            with torch.cuda.stream(stream):
-                for i in range(20):
-                    call(i)
-            reps = 400
-            us = time_graph(call, reps, stream) * 1e3 / reps
-            b = gemm_bytes(M, N, K, False)
-            out[f"M{M} N{N} K{K}"] = {"us": round(us, 3), "GBs": round(b / (us * 1e-6) / 1e9, 1),
-                                     "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        del copies
-        torch.cuda.empty_cache()
-    # more than 48 rows (64-row blocks, or 64 x 64 tiles above 128 rows)
-    N, K = 4096, 5120
-    copies = weight_copies(N, K, dev)
-    for M in (64, 128, 256):
-        x = synth.gemm_case(M, 16, K, seed=0)["x"].to(dev)
-        aq, as_ = mx.mxfp8_quantize(x)
-        o = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-
-        def call(i):
-            mx.mxfp8_gemm(aq, as_, copies[i % len(copies)], out=o)
-        with torch.cuda.stream(stream):
-            for i in range(20):
-                call(i)
-        us = time_graph(call, 200, stream) * 1e3 / 200
-        b = gemm_bytes(M, N, K, False)
-        out[f"rows above 48: M{M} N{N} K{K}"] = {
-            "us": round(us, 3), "GBs": round(b / (us * 1e-6) / 1e9, 1),
-            "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "TFLOPs": round(2 * M * N * K / (us * 1e-6) / 1e12, 1)}
-    del copies
-    torch.cuda.empty_cache()
-    for M in (1, 8, 32):
-        out[f"chain M{M}"] = chain_case(dev, stream, M)
-    for M in (1, 8, 32):
-        out[f"chain+norm M{M}"] = chain_case(dev, stream, M, norm=True)
-    for M in (1, 8, 48):
-        for K, ld in ((1536, 2048), (5120, 5120)):
-            out[f"rmsnorm+quantize M{M} K{K}"] = rmsnorm_case(dev, stream, M, K, ld)
-    for M in (1, 4, 16):
-        out[f"wo_a+wo_b M{M}"] = wo_a_case(dev, stream, M)
-    return out
+    u = per_call_us(time_graph(call, reps, stream), reps)
+    return u, 2 * M * K + 2 * K + 2 * M * K + mx_bytes(M, K)
 
 
 def wo_a_case(dev, stream, M: int, reps: int = 200):
@@ -334,49 +356,140 @@ def wo_a_case(dev, stream, M: int, reps: int = 200):
     with torch.cuda.stream(stream):
         for i in range(10):
             call(i)
-    us = time_graph(call, reps, stream) * 1e3 / reps
+    u = per_call_us(time_graph(call, reps, stream), reps)
     H, D = d["n_heads"], d["head_dim"]
     b = per + 2 * M * H * D + 8 * M + 4 * M * (D - d["nope"]) + mx_bytes(M, G * R) + 2 * M * wb.N
-    return {"us": round(us, 3), "GBs": round(b / (us * 1e-6) / 1e9, 1),
-            "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    return u, b
 
 
-def cpu_baseline(min_seconds: float = 10.0):
+def gemm_case_timing(dev, stream, copies, M, N, K, outliers, reps):
+    x = synth.gemm_case(M, 16, K, seed=0, outliers=outliers)["x"].to(dev)
+    aq, as_ = mx.mxfp8_quantize(x)
+    o = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+
+    def call(i):
+        mx.mxfp8_gemm(aq, as_, copies[i % len(copies)], out=o)
+    with torch.cuda.stream(stream):
+        for i in range(20):
+            call(i)
+    return per_call_us(time_graph(call, reps, stream), reps)
+
+
+def case_names():
+    """Every bench case, in run order (names are stable keys of the JSON line
+    and of the committed counter profile)."""
+    names = ["single M4 N1024 K2048"]
+    for (N, K) in ((4096, 5120), (5120, 8192), (8192, 1536)):
+        names += [f"M{M} N{N} K{K}" for M in (16, 32, 48)]
+    names += [f"rows above 48: M{M} N4096 K5120" for M in (64, 128, 256)]
+    names += [f"chain M{M}" for M in (1, 8, 32)]
+    names += [f"chain+norm M{M}" for M in (1, 8, 32)]
+    names += [f"rmsnorm+quantize M{M} K{K}" for M in (1, 8, 48) for K in (1536, 5120)]
+    names += [f"wo_a+wo_b M{M}" for M in (1, 4, 16)]
+    return names
+
+
+def extra_cases(dev, stream, floor_us, only=None, reps=None):
+    """Latency of every other configuration: single GEMMs with MXFP8 inputs
+    (config 0, the wide tiles with outliers, rows above 48), the chain with
+    and without the norm, RMSNorm + MXFP8, WO-A + wo_b.  `only`: run the
+    cases whose name contains it (profiling one case at a time)."""
+    prof = profiled_cases()
+    out = {}
+    want = lambda name: only is None or only in name
+    r = lambda default: reps or default
+    specs = [("single M4 N1024 K2048", 4, 1024, 2048, False)]
+    for (N, K) in ((4096, 5120), (5120, 8192), (8192, 1536)):
+        specs += [(f"M{M} N{N} K{K}", M, N, K, True) for M in (16, 32, 48)]
+    specs += [(f"rows above 48: M{M} N4096 K5120", M, 4096, 5120, False) for M in (64, 128, 256)]
+    by_weight = {}
+    for spec in specs:
+        if want(spec[0]):
+            by_weight.setdefault((spec[2], spec[3]), []).append(spec)
+    for (N, K), group in by_weight.items():
+        copies = weight_copies(N, K, dev)
+        for (name, M, _, _, outliers) in group:
+            u = gemm_case_timing(dev, stream, copies, M, N, K, outliers, r(400 if M <= 48 else 200))
+            extra = {}
+            if M > 48:
+                extra["TFLOPs"] = round(2 * M * N * K / (u["ms"] * 1e-6) / 1e12, 1)
+            out[name] = case_record(name, u, gemm_bytes(M, N, K, False), prof, floor_us, **extra)
+        del copies
+        torch.cuda.empty_cache()
+    for M in (1, 8, 32):
+        if want(f"chain M{M}"):
+            u, b = chain_case(dev, stream, M, reps=r(200))
+            out[f"chain M{M}"] = case_record(f"chain M{M}", u, b, prof, floor_us)
+    for M in (1, 8, 32):
+        if want(f"chain+norm M{M}"):
+            u, b = chain_case(dev, stream, M, reps=r(200), norm=True)
+            out[f"chain+norm M{M}"] = case_record(f"chain+norm M{M}", u, b, prof, floor_us)
+    for M in (1, 8, 48):
+        for K, ld in ((1536, 2048), (5120, 5120)):
+            name = f"rmsnorm+quantize M{M} K{K}"
+            if want(name):
+                u, b = rmsnorm_case(dev, stream, M, K, ld, reps=r(400))
+                rec = case_record(name, u, b, prof, floor_us)
+                rec.pop("frac")          # launch-bound: a few KB per row
+                out[name] = rec
+    for M in (1, 4, 16):
+        if want(f"wo_a+wo_b M{M}"):
+            u, b = wo_a_case(dev, stream, M, reps=r(200))
+            out[f"wo_a+wo_b M{M}"] = case_record(f"wo_a+wo_b M{M}", u, b, prof, floor_us)
+    return out
+
+
+def cpu_baseline(min_seconds: float = 10.0, t1_seconds: float = 4.0):
     """The oracle (plain C, fp64) on the same decode-bucket step: quantize each
     M-row batch and run the GEMM against the full weight; repeated until
-    min_seconds have elapsed."""
+    min_seconds have elapsed with every host thread the process may use, then
+    the same step with one thread for t1_seconds."""
     import oracle
     N, K, Ms = 4096, 5120, (1, 2, 4, 8)
     case = synth.gemm_case(8, N, K, seed=0)
     wq, ws = oracle.quantize(synth.bits(case["w"]))       # weight quantize: not timed
     xb = synth.bits(case["x"])
-    threads = oracle.set_threads(len(os.sched_getaffinity(0)))
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        for M in Ms:
-            q, s = oracle.quantize(xb[:M])
-            oracle.gemm(q, s, wq, ws)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds:
-            break
     step_bytes = sum(gemm_bytes(M, N, K, True) for M in Ms)
+
+    def run(threads, seconds):
+        used = oracle.set_threads(threads)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            for M in Ms:
+                q, s = oracle.quantize(xb[:M])
+                oracle.gemm(q, s, wq, ws)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return used, reps, el
+    threads, reps, el = run(len(os.sched_getaffinity(0)), min_seconds)
+    _, reps1, el1 = run(1, t1_seconds)
     return {"value": round(step_bytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{reps} full decode-bucket steps (M=1,2,4,8; N=4096; K=5120) in {el:.1f} s, "
-                      f"{el / reps:.3f} s/step"}
+                      f"{el / reps:.3f} s/step",
+            "t1": {"value": round(step_bytes * reps1 / el1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                   "sample": f"{reps1} steps in {el1:.1f} s, {el1 / reps1:.3f} s/step"}}
 
 
 def main():
+    global REPLAYS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replays", type=int, default=REPLAYS,
+                    help="graph replays per timing (the median is reported)")
     ap.add_argument("--no-cases", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="run only the bench cases whose name contains this text (profiling)")
+    ap.add_argument("--reps", type=int, default=None,
+                    help="calls per captured graph in the cases (default per case)")
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the dominant kernel's timing (for profiler runs)")
     args = ap.parse_args()
+    REPLAYS = max(1, args.replays)
     if args.gpus != 1:
         print(f"bench.py: this library runs on one GPU only (asked for {args.gpus}); the "
               "multi-GPU sharding of the path is a design note, not a measured mode.",
@@ -396,11 +509,19 @@ def main():
         print(json.dumps({"roofline_kernel_us": roofline_kernel(dev, stream)["us"],
                           "calibration_bytes_each_way": 64 << 20}), flush=True)
         return
+    if args.only is not None:
+        floor = launch_floor(dev, stream)
+        print(json.dumps({"only": args.only, "launch_floor_us": round(floor, 3),
+                          "cases": extra_cases(dev, stream, floor, only=args.only,
+                                               reps=args.reps)}), flush=True)
+        return
     rec = decode_bucket(dev, args.steps, args.warmup, stream)
     roof = roofline_kernel(dev, stream)
     ceil = stream_ceiling(dev, stream)
-    cases = {} if args.no_cases else extra_cases(dev, stream)
+    floor = launch_floor(dev, stream)
+    cases = {} if args.no_cases else extra_cases(dev, stream, floor, reps=args.reps)
     cpu = None if args.no_cpu else cpu_baseline()
+    traffic, prof_us = profiled_roofline()
     line = {
         "metric": "µs per MXFP8 GEMM at M=1..48; achieved HBM GB/s vs 8 TB/s peak",
         "value": round(rec["GBs"], 1),
@@ -417,19 +538,29 @@ def main():
         "config": {"workload": "decode-bucket MXFP8 GEMM with fused bf16->MXFP8 quantize, "
                                "M in {1,2,4,8}, N=4096, K=5120",
                    "M": [1, 2, 4, 8], "N": 4096, "K": 5120,
-                   "weight_copies": rec["copies"], "timing": "HIP graph of K steps, HIP events"},
+                   "weight_copies": rec["copies"],
+                   "timing": f"median of {rec['replays']} replays of a HIP graph of the K steps, "
+                             "each between HIP events"},
+        "ms_per_step_min": round(rec["ms_per_step_min"], 5),
+        "ms_per_step_max": round(rec["ms_per_step_max"], 5),
         "us_per_gemm": rec["per_m"],
         "roofline": {"bound": "hbm", "kernel": ROOFLINE_KERNEL,
                      "achieved": round(roof["GBs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(roof["GBs"] / HBM_PEAK_GBS, 4),
                      "avg_launch_us": round(roof["us"], 3),
                      "bytes_per_launch": int(roof["bytes"]),
-                     "traffic": profiled_traffic()},
+                     "traffic": traffic,
+                     # the same kernel's average duration under the profiler's
+                     # kernel trace (committed summary), and the fraction it gives
+                     "profile_avg_launch_us": round(prof_us, 3) if prof_us else None,
+                     "frac_profile": (round(roof["bytes"] / (prof_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                      if prof_us else None)},
         "stream_ceiling": {"kernel": "hbm_read_kernel: the same weight copies read with the "
                                      "same load pattern, nothing else",
                            "us": round(ceil["us"], 3), "GBs": round(ceil["GBs"], 1),
                            "frac": round(ceil["GBs"] / HBM_PEAK_GBS, 4),
                            "roofline_vs_ceiling": round(roof["GBs"] / ceil["GBs"], 4)},
+        "launch_floor_us": round(floor, 3),
         "step_avg_launch_us": round(rec["kernel_us"], 3),
         "cases": cases,
         "cpu_baseline": cpu,
