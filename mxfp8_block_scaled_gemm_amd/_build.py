@@ -21,7 +21,8 @@ HIPCC_FLAGS = [
 
 
 def sources() -> list[str]:
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    """The HIP sources and the plain C++ host sources (argument checks)."""
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def build(verbose: bool = False) -> str:

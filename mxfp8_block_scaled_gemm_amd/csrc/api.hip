@@ -11,6 +11,7 @@
 
 #include "mx_launch.hpp"
 #include "mxgemm.h"
+#include "validate.hpp"
 
 // Scratch of mxfp8_gemm_noalloc (see there): one copy per GPU.
 constexpr size_t kScratchBytes = MXG_NOALLOC_SCRATCH_BYTES;
@@ -19,8 +20,7 @@ static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 namespace {
 
 using mxg::GemmArgs;
-
-inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+namespace check = mxg::check;
 
 // 0 = not checked yet, 1 = gfx950, 2 = something else.
 constexpr int kMaxDevices = 64;
@@ -46,82 +46,12 @@ int check_device() {
 
 int launched(hipError_t e) { return e == hipSuccess ? MXG_OK : MXG_ERR_DEVICE; }
 
-int validate_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint8_t* q,
-                      const uint8_t* s) {
-  if (!x || !q || !s) return MXG_ERR_NULL;
-  if (M < 1 || K < 32 || K % 32 != 0 || ld_x < K || M > (int64_t)1 << 31 || K > (int64_t)1 << 30)
-    return MXG_ERR_SHAPE;
-  if (!aligned16(x) || !aligned16(q) || ld_x % 8 != 0) return MXG_ERR_ALIGN;
-  return MXG_OK;
-}
-
-int validate_rmsnorm(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint16_t* w,
-                     float eps, const uint16_t* y, int64_t ld_y, const uint8_t* q,
-                     const uint8_t* s, int32_t layout) {
-  if (!x || !w || !q || !s) return MXG_ERR_NULL;
-  if (M < 1 || M > 65535 || K < 128 || K % 128 != 0 || K > MXG_MAX_K || ld_x < K ||
-      ld_x * M > ((int64_t)1 << 30) || !(eps >= 0.f) || eps > 3.0e38f ||
-      (layout != MXG_SCALES_ROW_MAJOR && layout != MXG_SCALES_128X4))
-    return MXG_ERR_SHAPE;
-  if (y && (ld_y < K || ld_y * M > ((int64_t)1 << 30))) return MXG_ERR_SHAPE;
-  if (!aligned16(x) || !aligned16(w) || !aligned16(q) || ld_x % 8 != 0 ||
-      (y && (!aligned16(y) || ld_y % 8 != 0)))
-    return MXG_ERR_ALIGN;
-  return MXG_OK;
-}
-
-bool gemm_shape_ok(int64_t M, int64_t N, int64_t K) {
-  return M >= 1 && M <= MXG_MAX_GEMM_ROWS && N >= 16 && N % 16 == 0 && K >= 128 && K % 128 == 0 &&
-         N <= ((int64_t)1 << 24) && K <= MXG_MAX_K && N * K <= ((int64_t)1 << 31) - 1;
-}
-
-int validate_gemm_args(int64_t M, int64_t N, int64_t K, const uint16_t* x, int64_t ld_x,
-                       const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w_q,
-                       const uint8_t* w_s, const uint16_t* out) {
-  if (!a_q || !a_s || !w_q || !w_s || !out) return MXG_ERR_NULL;
-  if (!gemm_shape_ok(M, N, K)) return MXG_ERR_SHAPE;
-  if (x && (ld_x < K || ld_x * M > ((int64_t)1 << 30))) return MXG_ERR_SHAPE;
-  if (!aligned16(a_q) || !aligned16(a_s) || !aligned16(w_q) || !aligned16(w_s) ||
-      !aligned16(out) || (x && (!aligned16(x) || ld_x % 8 != 0)))
-    return MXG_ERR_ALIGN;
-  return MXG_OK;
-}
-
 int validate_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* x, int64_t ld_x,
                   const uint8_t* a_q, const uint8_t* a_s, const uint8_t* w_q,
                   const uint8_t* w_s, const uint16_t* out, size_t ws_bytes, const void* ws) {
-  const int st = validate_gemm_args(M, N, K, x, ld_x, a_q, a_s, w_q, w_s, out);
+  const int st = check::gemm(M, N, K, x, ld_x, a_q, a_s, w_q, w_s, out);
   if (st != MXG_OK) return st;
-  const size_t need = mxg_gemm_workspace_bytes(M, N, K);
-  if (need > 0 && (!ws || ws_bytes < need)) return MXG_ERR_WORKSPACE;
-  if (ws && !aligned16(ws)) return MXG_ERR_ALIGN;
-  return MXG_OK;
-}
-
-bool weight_ok(const mxg_weight& w) {
-  return w.N >= 16 && w.N % 16 == 0 && w.K >= 128 && w.K % 128 == 0 && w.N <= ((int64_t)1 << 24) &&
-         w.K <= MXG_MAX_K && w.N * w.K <= ((int64_t)1 << 31) - 1;
-}
-
-int validate_chain(const mxg_chain* c, size_t need) {
-  if (!c) return MXG_ERR_NULL;
-  if (!c->a_q || !c->a_s || !c->wA.q || !c->wA.s || !c->wB.q || !c->wB.s || !c->wC.q ||
-      !c->wC.s || !c->out_a || !c->b_q || !c->b_s || !c->out_b || !c->c_q || !c->c_s ||
-      !c->out_c)
-    return MXG_ERR_NULL;
-  if (c->M < 1 || c->M > MXG_MAX_ROWS || !weight_ok(c->wA) || !weight_ok(c->wB) ||
-      !weight_ok(c->wC) || c->wB.K > c->wA.N)
-    return MXG_ERR_SHAPE;
-  const void* ptrs[] = {c->a_q, c->a_s, c->wA.q, c->wA.s, c->wB.q, c->wB.s, c->wC.q, c->wC.s,
-                        c->out_a, c->b_q, c->b_s, c->out_b, c->c_q, c->c_s, c->out_c};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return MXG_ERR_ALIGN;
-  if (c->norm_weight && (!(c->norm_eps >= 0.f) || c->norm_eps > 3.0e38f)) return MXG_ERR_SHAPE;
-  if ((c->norm_weight && !aligned16(c->norm_weight)) || (c->b_bf16 && !aligned16(c->b_bf16)))
-    return MXG_ERR_ALIGN;
-  if (!c->workspace || c->workspace_bytes < need) return MXG_ERR_WORKSPACE;
-  if (!aligned16(c->workspace)) return MXG_ERR_ALIGN;
-  return MXG_OK;
+  return check::workspace(ws, ws_bytes, mxg_gemm_workspace_bytes(M, N, K));
 }
 
 // K-split state of a direct GEMM in workspace ws, partials from part_off on.
@@ -177,39 +107,13 @@ WoALayout wo_a_layout(const mxg_wo_a& p) {
   return l;
 }
 
-bool wo_a_shape_ok(const mxg_wo_a& p) {
-  const int64_t H = p.n_heads, D = p.head_dim, nope = p.nope_dim, G = p.n_groups;
-  if (p.M < 1 || p.M > MXG_MAX_ROWS || H < 1 || G < 1 || H % G != 0 || H / G > 8) return false;
-  if (D < 64 || D % 32 != 0 || nope < 32 || nope >= D || nope % 32 != 0 || D > 4096) return false;
-  if (H * D > ((int64_t)1 << 20) || p.max_pos < 1 || p.max_pos > ((int64_t)1 << 31) / (D - nope))
-    return false;
-  if (p.ld_head < D || p.ld_row < (H - 1) * p.ld_head + D) return false;
-  if (((p.M - 1) * p.ld_row + H * p.ld_head) * 2 >= ((int64_t)1 << 31)) return false;
-  if (!weight_ok(p.wa) || p.wa.N % G != 0 || (p.wa.N / G) % 128 != 0 || p.wa.K != (H / G) * D)
-    return false;
-  if (p.wb.q && (!weight_ok(p.wb) || p.wb.K != p.wa.N)) return false;
-  return true;
-}
-
 size_t wo_a_need(const mxg_wo_a& p);
 
 int validate_wo_a(const mxg_wo_a* p) {
-  if (!p) return MXG_ERR_NULL;
-  if (!p->o || !p->positions || !p->cos_sin || !p->wa.q || !p->wa.s || !p->z_q || !p->z_s)
-    return MXG_ERR_NULL;
-  if (p->wb.q && (!p->wb.s || !p->out)) return MXG_ERR_NULL;
-  if (!wo_a_shape_ok(*p)) return MXG_ERR_SHAPE;
-  const void* ptrs[] = {p->o, p->cos_sin, p->wa.q, p->wa.s, p->z_q, p->z_s};
-  for (const void* q : ptrs)
-    if (!aligned16(q)) return MXG_ERR_ALIGN;
-  if ((reinterpret_cast<uintptr_t>(p->positions) & 7u) || p->ld_row % 8 || p->ld_head % 8)
-    return MXG_ERR_ALIGN;
-  if (p->z && !aligned16(p->z)) return MXG_ERR_ALIGN;
-  if (p->wb.q && (!aligned16(p->wb.q) || !aligned16(p->wb.s) || !aligned16(p->out)))
-    return MXG_ERR_ALIGN;
-  if (!p->workspace || p->workspace_bytes < wo_a_need(*p)) return MXG_ERR_WORKSPACE;
-  if (!aligned16(p->workspace)) return MXG_ERR_ALIGN;
-  return MXG_OK;
+  const int st = check::wo_a(p);
+  if (st != MXG_OK) return st;
+  if (!p->workspace) return MXG_ERR_WORKSPACE;
+  return check::workspace(p->workspace, p->workspace_bytes, wo_a_need(*p));
 }
 
 // Workspace bytes of WO-A: the rotated input's codes (and z when the caller
@@ -253,17 +157,6 @@ int wo_a_run(const mxg_wo_a& p, hipStream_t stream) {
   return launched(mxg::launch_quantize(z, M, GR, GR, p.z_q, p.z_s, stream));
 }
 
-int validate_pack(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K,
-                  const uint8_t* wp_q, const uint8_t* wp_s) {
-  if (!w_q || !w_s || !wp_q || !wp_s) return MXG_ERR_NULL;
-  if (N < 16 || N % 16 != 0 || K < 128 || K % 128 != 0 || N > (int64_t)1 << 24 ||
-      K > (int64_t)1 << 20 || N * K > ((int64_t)1 << 31) - 1)
-    return MXG_ERR_SHAPE;
-  if (!aligned16(w_q) || !aligned16(w_s) || !aligned16(wp_q) || !aligned16(wp_s))
-    return MXG_ERR_ALIGN;
-  return MXG_OK;
-}
-
 // ------------------------------------------------ allocation-free GEMM
 //
 // mxfp8_gemm_noalloc keeps the K-split state of mxfp8_gemm (counters and FP32
@@ -294,28 +187,14 @@ int scratch_address(void** out) {
 
 extern "C" {
 
-const char* mxg_strerror(int status) {
-  switch (status) {
-    case MXG_OK: return "success";
-    case MXG_ERR_NULL: return "a required pointer is NULL";
-    case MXG_ERR_ALIGN: return "a pointer or row stride is not 16-byte aligned";
-    case MXG_ERR_SHAPE: return "a size is out of range or sizes are inconsistent";
-    case MXG_ERR_WORKSPACE: return "workspace missing or too small";
-    case MXG_ERR_DEVICE: return "device is not gfx950, or the kernel launch failed";
-    default: return "unknown status";
-  }
-}
-
-int mxg_version(void) { return 100; }
-
 size_t mxg_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (!gemm_shape_ok(M, N, K)) return mxg::kCtrBytes;
+  if (!check::gemm_shape(M, N, K)) return mxg::kCtrBytes;
   return std::max(mxg::kCtrBytes, direct_need((int)M, (int)N, (int)K, mxg::kGemmPartOffset));
 }
 
 size_t mxg_chain_workspace_bytes(const mxg_chain* c) {
-  if (!c || c->M < 1 || c->M > MXG_MAX_ROWS || !weight_ok(c->wA) || !weight_ok(c->wB) ||
-      !weight_ok(c->wC))
+  if (!c || c->M < 1 || c->M > MXG_MAX_ROWS || !check::weight(c->wA) || !check::weight(c->wB) ||
+      !check::weight(c->wC))
     return mxg::kCtrBytes;
   const int M = (int)c->M;
   size_t need = mxg::kCtrBytes;
@@ -326,21 +205,16 @@ size_t mxg_chain_workspace_bytes(const mxg_chain* c) {
 
 int mxfp8_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, uint8_t* q, uint8_t* s,
                    void* stream) {
-  int st = validate_quantize(x, M, K, ld_x, q, s);
+  int st = check::quantize(x, M, K, ld_x, q, s);
   if (st != MXG_OK) return st;
   if ((st = check_device()) != MXG_OK) return st;
   return launched(mxg::launch_quantize(x, M, K, ld_x, q, s, (hipStream_t)stream));
 }
 
-size_t mxg_scale_bytes_128x4(int64_t M, int64_t K) {
-  if (M < 1 || K < 1) return 0;
-  return (size_t)((M + 127) / 128) * 128 * (size_t)((K + 127) / 128) * 4;
-}
-
 int mxfp8_rmsnorm_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
                            const uint16_t* w, float eps, uint16_t* y, int64_t ld_y, uint8_t* q,
                            uint8_t* s, int32_t scale_layout, void* stream) {
-  int st = validate_rmsnorm(x, M, K, ld_x, w, eps, y, ld_y, q, s, scale_layout);
+  int st = check::rmsnorm(x, M, K, ld_x, w, eps, y, ld_y, q, s, scale_layout);
   if (st != MXG_OK) return st;
   if ((st = check_device()) != MXG_OK) return st;
   return launched(mxg::launch_rmsnorm_quantize(x, M, K, ld_x, w, eps, y, ld_y, q, s,
@@ -349,20 +223,16 @@ int mxfp8_rmsnorm_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x
 
 int mxg_hbm_read_probe(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K,
                        uint32_t* sink, void* stream) {
-  if (!w_q || !w_s || !sink) return MXG_ERR_NULL;
-  if (N < 16 || N % 16 != 0 || N > ((int64_t)1 << 24) || K < 128 || K % 128 != 0 || K > 8192)
-    return MXG_ERR_SHAPE;
-  if (!aligned16(w_q) || !aligned16(w_s) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
-    return MXG_ERR_ALIGN;
-  int st = check_device();
+  int st = check::hbm_probe(w_q, w_s, N, K, sink);
   if (st != MXG_OK) return st;
+  if ((st = check_device()) != MXG_OK) return st;
   return launched(
       mxg::launch_hbm_read(w_q, w_s, (int)(N / 16), (int)(K / 128), sink, (hipStream_t)stream));
 }
 
 int mxfp8_pack_weights(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K,
                        uint8_t* wp_q, uint8_t* wp_s, void* stream) {
-  int st = validate_pack(w_q, w_s, N, K, wp_q, wp_s);
+  int st = check::pack(w_q, w_s, N, K, wp_q, wp_s);
   if (st != MXG_OK) return st;
   if ((st = check_device()) != MXG_OK) return st;
   return launched(mxg::launch_pack(w_q, w_s, N, K, wp_q, wp_s, (hipStream_t)stream));
@@ -383,7 +253,7 @@ int mxfp8_gemm(int64_t M, int64_t N, int64_t K, const uint16_t* x_bf16, int64_t 
 int mxfp8_gemm_noalloc(int64_t M, int64_t N, int64_t K, const uint16_t* x_bf16, int64_t ld_x,
                        uint8_t* a_q, uint8_t* a_s, const uint8_t* w_q, const uint8_t* w_s,
                        uint16_t* out, void* stream) {
-  int st = validate_gemm_args(M, N, K, x_bf16, ld_x, a_q, a_s, w_q, w_s, out);
+  int st = check::gemm(M, N, K, x_bf16, ld_x, a_q, a_s, w_q, w_s, out);
   if (st != MXG_OK) return st;
   if (mxg_gemm_workspace_bytes(M, N, K) > kScratchBytes) return MXG_ERR_WORKSPACE;
   if ((st = check_device()) != MXG_OK) return st;
@@ -413,15 +283,18 @@ int mxfp8_gemm_ex(int64_t M, int64_t N, int64_t K, const uint8_t* a_q, const uin
 }
 
 int mxfp8_proj_chain(const mxg_chain* c, void* stream) {
-  if (!c) return MXG_ERR_NULL;
-  int st = validate_chain(c, mxg_chain_workspace_bytes(c));
+  int st = check::chain(c);
   if (st != MXG_OK) return st;
+  if (!c->workspace) return MXG_ERR_WORKSPACE;
+  if ((st = check::workspace(c->workspace, c->workspace_bytes, mxg_chain_workspace_bytes(c))) !=
+      MXG_OK)
+    return st;
   if ((st = check_device()) != MXG_OK) return st;
   return chain_direct(*c, (hipStream_t)stream);
 }
 
 size_t mxg_wo_a_workspace_bytes(const mxg_wo_a* p) {
-  if (!p || !wo_a_shape_ok(*p)) return mxg::kCtrRegionBytes;
+  if (!p || !check::wo_a_shape(*p)) return mxg::kCtrRegionBytes;
   return wo_a_need(*p);
 }
 

@@ -38,27 +38,38 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mxoracle.c")
 _LIB = os.path.join(_HERE, "libmxoracle.so")
+# MXG_ORACLE_SANITIZE=1: load a build of the same source with AddressSanitizer
+# and UndefinedBehaviorSanitizer (the process must have the ASan runtime
+# preloaded; tests/test_sanitizers.py runs the oracle tests that way).
+_SAN = os.environ.get("MXG_ORACLE_SANITIZE") == "1"
+_LIB_SAN = os.path.join(_HERE, "libmxoracle_san.so")
 _lock = threading.Lock()
 _lib = None
 
 
-def build(force: bool = False) -> str:
-    """Compile mxoracle.c into libmxoracle.so (gcc, OpenMP, no FP contraction)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp%d" % os.getpid()
+def build(force: bool = False, sanitize: bool = False) -> str:
+    """Compile mxoracle.c into libmxoracle.so (gcc, OpenMP, no FP contraction),
+    or with sanitize into libmxoracle_san.so with ASan and UBSan (any UB report
+    aborts)."""
+    out = _LIB_SAN if sanitize else _LIB
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(_SRC):
+        tmp = out + ".tmp%d" % os.getpid()
+        flags = ["-O2"]
+        if sanitize:
+            flags = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                     "-fno-sanitize-recover=all"]
         subprocess.check_call(
-            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+            ["gcc", *flags, "-std=c11", "-fPIC", "-shared", "-fopenmp",
              "-ffp-contract=off", "-fno-fast-math", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, out)
+    return out
 
 
 def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build()
-            lib = ctypes.CDLL(_LIB)
+            lib = ctypes.CDLL(build(sanitize=_SAN))
             u8p = ctypes.POINTER(ctypes.c_uint8)
             u16p = ctypes.POINTER(ctypes.c_uint16)
             f64p = ctypes.POINTER(ctypes.c_double)
