@@ -138,25 +138,49 @@ def test_half_tile_plan(M, N, K, fused, monkeypatch):
     assert torch.equal(half.view(torch.int16), one.view(torch.int16))
 
 
-def test_one_hot_weights_bitwise():
-    M, N, K = 9, 256, 1024
-    rng = np.random.default_rng(0)
+def _force(monkeypatch, kernel):
+    if kernel:
+        monkeypatch.setenv("MXG_DIRECT_KERNEL", kernel)
+    else:
+        monkeypatch.delenv("MXG_DIRECT_KERNEL", raising=False)
+
+
+# Every kernel form: as routed, and the M <= 16 kernel, the 2D kernel and the
+# tile + half-tile form forced where they apply (N 5120 gives G < tiles <=
+# 1.5 G on 256 CUs); M = 130 runs the forms for more than 48 rows.
+KERNEL_FORMS = [None, "m16", "2d", "m16h"]
+BITWISE_SHAPES = [(9, 256, 1024), (9, 5120, 1024), (130, 256, 1024)]
+
+
+@pytest.mark.parametrize("kernel", KERNEL_FORMS)
+@pytest.mark.parametrize("M,N,K", BITWISE_SHAPES)
+def test_one_hot_weights_bitwise(M, N, K, kernel, monkeypatch):
+    """W has one 1.0 per row (code 0x38) in a block whose scale varies per
+    row (2^-3 .. 2^3); the other blocks' scales vary too but multiply zeros.
+    Each output is then one activation value times powers of two, exact in
+    BF16, so every kernel must match the oracle bit for bit."""
+    _force(monkeypatch, kernel)
+    rng = np.random.default_rng(M + N)
     x_bits = oracle.bf16_round(rng.standard_normal((M, K)))
     oa_q, oa_s = oracle.quantize(x_bits)
     kn = rng.integers(0, K, N)
     wq = np.zeros((N, K), np.uint8); wq[np.arange(N), kn] = 0x38
-    ws = np.full((N, K // 32), 127, np.uint8)
+    ws = rng.integers(124, 131, (N, K // 32)).astype(np.uint8)
     ref = oracle.gemm(oa_q, oa_s, wq, ws)
-    say("gemm one-hot")
+    say(f"gemm one-hot M={M} N={N} K={K} kernel={kernel}")
     out = mx.mxfp8_gemm(dev_u8(oa_q), dev_u8(oa_s), mx.PackedWeight.from_rows(dev_u8(wq), dev_u8(ws)))
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(out), ref.bf16)
 
 
-def test_weight_scale_plus_one_doubles_output_bitwise():
-    M, N, K = 6, 512, 2048
+@pytest.mark.parametrize("kernel", KERNEL_FORMS)
+@pytest.mark.parametrize("M,N,K", [(6, 512, 2048), (6, 5120, 1024), (130, 512, 1024)])
+def test_weight_scale_plus_one_doubles_output_bitwise(M, N, K, kernel, monkeypatch):
+    """Raising every weight scale byte by one doubles every output exactly,
+    whatever the kernel's summation order (the sums scale by a power of two)."""
+    _force(monkeypatch, kernel)
     case = synth.gemm_case(M, N, K, seed=3)
-    say("gemm scale+1 metamorphic")
+    say(f"gemm scale+1 metamorphic M={M} N={N} K={K} kernel={kernel}")
     a_q, a_s = mx.mxfp8_quantize(case["x"].cuda())
     w_q, w_s = mx.mxfp8_quantize(case["w"].cuda())
     out1 = mx.mxfp8_gemm(a_q, a_s, mx.PackedWeight.from_rows(w_q, w_s))
@@ -373,8 +397,11 @@ def test_rows_above_48_full_size(M, N, K):
 
 
 @pytest.mark.parametrize("M", [64, 130, 256])
-def test_rows_above_48_with_128x4_scales(M):
-    # rows past 128 sit in the second row of 128 x 4 tiles
+def test_rows_above_48_with_128x4_scales(M, monkeypatch):
+    # rows past 128 sit in the second row of 128 x 4 tiles; the row-major
+    # call runs on the same kernel as the 128 x 4 one (the 64-row blocks of
+    # the 2D kernel), so the two must agree bit for bit
+    monkeypatch.setenv("MXG_DIRECT_KERNEL", "2d")
     N, K = 1024, 2048
     case = synth.gemm_case(M, N, K, seed=M + 2)
     oa_q, oa_s = oracle.quantize(synth.bits(case["x"]))
