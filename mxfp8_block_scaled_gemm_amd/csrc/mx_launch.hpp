@@ -44,10 +44,8 @@ struct GemmArgs {
   uint16_t* norm_y = nullptr;
 };
 
-// Bytes of FP32 partials the GEMM of this shape needs (0: no K split); the
-// counters need gemm_counter_words() words.
+// Bytes of FP32 partials the GEMM of this shape needs (0: no K split).
 size_t gemm_partial_bytes(int M, int N, int K, int group_tiles = 0);
-int gemm_counter_words(int M, int N, int K, int group_tiles = 0);
 
 // Workspace layout.  The first 64 KiB are the counter region:
 //   word kCtrError (byte 20)  error word: an in-kernel wait that expired, or a

@@ -84,7 +84,7 @@ def gemm_noalloc(lib, M=4, N=1024, K=2048, x=None, ld_x=0, a_q=P(1), a_s=P(2), w
     (dict(N=1000), 3), (dict(x=P(6), ld_x=1024), 3), (dict(w_q=ctypes.c_void_p(A + 1)), 2),
     (dict(x=P(6), ld_x=2052), 2),
     # K-split state larger than the library's scratch: rejected before any device call
-    (dict(M=128, N=16384, K=8192), 4),
+    (dict(M=192, N=8192, K=16384), 4),
 ])
 def test_gemm_noalloc_rejects(lib, kw, status):
     assert gemm_noalloc(lib, **kw) == status
@@ -95,7 +95,7 @@ def test_noalloc_scratch_limit_matches_header(lib):
     text = open(os.path.join(ROOT, "include", "mxgemm.h")).read()
     m = re.search(r"#define MXG_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == mx.NOALLOC_SCRATCH_BYTES
-    assert lib.mxg_gemm_workspace_bytes(128, 16384, 8192) > mx.NOALLOC_SCRATCH_BYTES
+    assert lib.mxg_gemm_workspace_bytes(192, 8192, 16384) > mx.NOALLOC_SCRATCH_BYTES
     assert lib.mxg_gemm_workspace_bytes(48, 4096, 5120) <= mx.NOALLOC_SCRATCH_BYTES
 
 

@@ -159,10 +159,31 @@ def test_wo_a_position_out_of_range_sets_the_error_word():
     _, (wa, wb) = _weights(case)
     max_pos = case["cos_sin"].shape[0]
     pos = torch.tensor([5, max_pos], dtype=torch.int64, device="cuda")
-    ws = torch.zeros(8 << 20, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(32 << 20, dtype=torch.uint8, device="cuda")
     say("wo_a position out of range")
     mx.wo_a_fused_quantize(dev_bf16(synth.bits(case["o"])), pos,
                            torch.from_numpy(case["cos_sin"]).cuda(), wa, n_groups=d["n_groups"],
                            nope_dim=d["nope"], wb=wb, workspace=ws)
     torch.cuda.synchronize()
     assert mx.workspace_error(ws) & 2
+
+
+def test_wo_a_then_gemm_share_a_workspace():
+    # WO-A leaves its rotated input where a K-split GEMM keeps its partial
+    # sums, and its counters at zero: a K-split GEMM that follows on the same
+    # workspace gives the same bits as on a fresh one.
+    case, w = full_case()
+    _, ws = run_wo_a(case, w, 16)
+    assert not ws[:65536].any(), "counters must be back to zero"
+    M, N, K = 48, 4096, 5120
+    g = synth.gemm_case(M, N, K, seed=21)
+    wq, wsc = oracle.quantize(synth.bits(g["w"]))
+    pw = mx.PackedWeight.from_rows(dev_u8(wq), dev_u8(wsc))
+    aq, asc = oracle.quantize(synth.bits(g["x"]))
+    say(f"gemm M={M} N={N} K={K} after wo_a on one workspace")
+    shared = mx.mxfp8_gemm(dev_u8(aq), dev_u8(asc), pw, workspace=ws)
+    fresh = mx.mxfp8_gemm(dev_u8(aq), dev_u8(asc), pw,
+                          workspace=torch.zeros_like(ws))
+    torch.cuda.synchronize()
+    assert torch.equal(shared.view(torch.int16), fresh.view(torch.int16))
+    assert mx.workspace_error(ws) == 0
