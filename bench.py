@@ -54,9 +54,17 @@ ROOFLINE_SOURCES = [os.path.join(ROOT, "mxfp8_block_scaled_gemm_amd", "csrc", f)
                     for f in ("gemm.hip", "mx_device.hpp")]
 
 
-def _sources_sha():
+def _sources_sha(files=None):
     import hashlib
-    return [hashlib.sha256(open(f, "rb").read()).hexdigest() for f in ROOFLINE_SOURCES]
+    return [hashlib.sha256(open(f, "rb").read()).hexdigest() for f in (files or ROOFLINE_SOURCES)]
+
+
+def _library_sources():
+    """Every source of libmxgemm.so (kernels, launchers, host code), sorted."""
+    import glob
+    d = os.path.join(ROOT, "mxfp8_block_scaled_gemm_amd", "csrc")
+    return sorted(glob.glob(os.path.join(d, "*.hip")) + glob.glob(os.path.join(d, "*.hpp")) +
+                  glob.glob(os.path.join(d, "*.cpp")))
 
 
 def profiled_roofline():
@@ -78,13 +86,14 @@ def profiled_roofline():
 def profiled_cases():
     """Per-case counters from the committed profile of every bench case:
     {case: {"launches": kernel launches per call, "mops": F8 MFMA MOPS per
-    call, "busy": SQ_VALU_MFMA_BUSY_CYCLES per call}}, empty when the GEMM
-    sources changed since the profile was taken."""
+    call, "busy": SQ_VALU_MFMA_BUSY_CYCLES per call}}, empty when any source of
+    the library changed since the profile was taken (its `sources_sha256:`
+    line holds the SHA-256 of every csrc file, in sorted path order)."""
     out = {}
     try:
         text = open(CASES_PROFILE).read()
         sha = [l.split(":", 1)[1].split() for l in text.splitlines() if l.startswith("sources_sha256:")]
-        if not sha or sha[0] != _sources_sha():
+        if not sha or sha[0] != _sources_sha(_library_sources()):
             return {}
         for line in text.splitlines():
             if line.startswith("| `") and line.count("|") >= 6:
@@ -396,7 +405,9 @@ def extra_cases(dev, stream, floor_us, only=None, reps=None):
     cases whose name contains it (profiling one case at a time)."""
     prof = profiled_cases()
     out = {}
-    want = lambda name: only is None or only in name
+    # a case's exact name selects that case alone, other text every case containing it
+    exact = only in case_names()
+    want = lambda name: only is None or (name == only if exact else only in name)
     r = lambda default: reps or default
     specs = [("single M4 N1024 K2048", 4, 1024, 2048, False)]
     for (N, K) in ((4096, 5120), (5120, 8192), (8192, 1536)):
