@@ -460,9 +460,10 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
   // scales were offset above; 128 x 4 tiles are addressed from the first row.
   const int srow0 = p0.a_sf128 ? row0 : 0;
   // Registers per thread per K chunk: CHM 16-byte code chunks, or with BF16
-  // input (M <= 16) one whole 32-element block per thread (64 per row).
-  constexpr int CHL = FQ ? 4 : CHM;
-  static_assert(!FQ || MB == 1, "BF16 staging serves up to 16 rows");
+  // input (M <= 32) MB whole 32-element blocks per thread (64 per row).
+  constexpr int FQB = FQ ? MB : 0;                      // BF16 blocks per thread per chunk
+  constexpr int CHL = FQ ? 4 * FQB : CHM;
+  static_assert(!FQ || MB <= 2, "BF16 staging serves up to 32 rows");
   constexpr int W = kM16Waves, kT = W * 64, WPT = W / T;  // waves per tile
   constexpr int kLdA = 16 * 128 + 16;                   // LDS bytes per code row of a chunk
   constexpr int kLdS = 16 * 4 + 4;                      // LDS bytes per scale row of a chunk
@@ -526,37 +527,46 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
     }
   };
 
-  // BF16 input: the chunk's 32-element blocks (64 per row), one whole block
-  // per thread, quantized while parked; the first tile group's workgroups
-  // also write the codes out.
+  // BF16 input: the chunk's 32-element blocks (64 per row), FQB whole blocks
+  // per thread (block tid + f * threads), quantized while parked; the first
+  // tile group's workgroups also write the codes out.
   auto load_bf16 = [&](int c, v4i (&st)[CHL]) {
     const int nsc_steps = min(16, ns - 16 * c);
     const int col0 = (k0 + 16 * c) * 128;
     const auto rx = make_rsrc(p.x, (uint32_t)(((M - 1) * p.ld_x + K) * 2));
     const int bpr = nsc_steps * 4, nblk = M * bpr;
-    const int row = tid / bpr, cb = tid - row * bpr;
-    const uint32_t off = (uint32_t)(row * p.ld_x + col0 + cb * 32) * 2u;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) st[h] = buf_ld16(rx, tid < nblk ? off + 16 * h : kOutOfRange);
+    for (int f = 0; f < FQB; ++f) {
+      const int blk = tid + f * kT;
+      const int row = blk / bpr, cb = blk - row * bpr;
+      const uint32_t off = (uint32_t)(row * p.ld_x + col0 + cb * 32) * 2u;
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        st[4 * f + h] = buf_ld16(rx, blk < nblk ? off + 16 * h : kOutOfRange);
+    }
   };
   auto park_bf16 = [&](int c, const v4i (&st)[CHL], uint8_t* act, int ldA_, uint8_t* scl,
                        int ldS_) {
     const int nsc_steps = min(16, ns - 16 * c);
     const int bpr = nsc_steps * 4, nblk = M * bpr;
     const int col0 = (k0 + 16 * c) * 128;
-    if (tid < nblk) {
-      const int row = tid / bpr, cb = tid - row * bpr;
-      v4i c0, c1;
-      int e;
-      quant_block32(&st[0], c0, c1, e);
-      *reinterpret_cast<v4i*>(act + row * ldA_ + cb * 32) = c0;
-      *reinterpret_cast<v4i*>(act + row * ldA_ + cb * 32 + 16) = c1;
-      scl[row * ldS_ + cb] = (uint8_t)(e + 127);
-      if (tg == 0) {
-        uint8_t* qo = p.a_q + (int64_t)row * K + col0 + cb * 32;
-        *reinterpret_cast<v4i*>(qo) = c0;
-        *reinterpret_cast<v4i*>(qo + 16) = c1;
-        p.a_s[((int64_t)row * K + col0 + cb * 32) >> 5] = (uint8_t)(e + 127);
+#pragma unroll
+    for (int f = 0; f < FQB; ++f) {
+      const int blk = tid + f * kT;
+      if (blk < nblk) {
+        const int row = blk / bpr, cb = blk - row * bpr;
+        v4i c0, c1;
+        int e;
+        quant_block32(&st[4 * f], c0, c1, e);
+        *reinterpret_cast<v4i*>(act + row * ldA_ + cb * 32) = c0;
+        *reinterpret_cast<v4i*>(act + row * ldA_ + cb * 32 + 16) = c1;
+        scl[row * ldS_ + cb] = (uint8_t)(e + 127);
+        if (tg == 0) {
+          uint8_t* qo = p.a_q + (int64_t)row * K + col0 + cb * 32;
+          *reinterpret_cast<v4i*>(qo) = c0;
+          *reinterpret_cast<v4i*>(qo + 16) = c1;
+          p.a_s[((int64_t)row * K + col0 + cb * 32) >> 5] = (uint8_t)(e + 127);
+        }
       }
     }
   };
@@ -960,7 +970,7 @@ int device_cus() {
 template <int MB, int T, int SPW, bool FQ>
 hipError_t launch_2d(const GemmArgs& a, hipStream_t stream) {
   constexpr int CHM = (MB * 16 * 16 * 8 + kM16Waves * 64 - 1) / (kM16Waves * 64);
-  constexpr int CHL = FQ ? 4 : CHM;                      // staging registers per chunk (v4i)
+  constexpr int CHL = FQ ? 4 * MB : CHM;                 // staging registers per chunk (v4i)
   constexpr int NCH = (SPW + T - 1) / T;
   // The whole part's activations in registers (then in LDS at once) while
   // they fit beside the weight slots; otherwise chunk by chunk.
@@ -1017,13 +1027,14 @@ hipError_t launch_2d_t(const GemmArgs& a, int T, int spw, hipStream_t stream) {
   return launch_2d_spw<MB, 4, FQ>(a, spw, stream);
 }
 
-// With BF16 input only for M <= 16 (larger row counts would spill the
+// With BF16 input only for M <= 32 (larger row counts would spill the
 // staging registers); the caller quantizes the others first.
 template <bool FQ>
 hipError_t launch_2d_mb(const GemmArgs& a, int T, int spw, hipStream_t stream) {
   const int mb = a.M > kRowBlock ? kRowBlock / 16 : (a.M + 15) / 16;
   if (mb == 1) return launch_2d_t<1, FQ>(a, T, spw, stream);
   if constexpr (FQ) {
+    if (mb == 2) return launch_2d_t<2, FQ>(a, T, spw, stream);
     return hipErrorInvalidValue;
   } else {
     if (mb == 2) return launch_2d_t<2, FQ>(a, T, spw, stream);
@@ -1232,7 +1243,7 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
     return launch_gemm(b, stream);
   }
   // Otherwise the 2D kernel.  BF16 input is quantized while staging when
-  // M <= 16 and a workgroup's share is small (M * Sp <= 1024: at most four
+  // M <= 32 and a workgroup's share is small (M * Sp <= 1024: at most four
   // 32-blocks per thread over its K part), else by its own launch first.
   if (pl.T == 0) return hipErrorInvalidValue;
   GemmArgs b = a;
@@ -1241,11 +1252,11 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
   if (pl.P > 1 && (b.ctr == nullptr || b.part == nullptr)) return hipErrorInvalidValue;
   // (Only where the kernel holds the whole part's BF16 blocks in registers:
   // chunk by chunk, the in-kernel quantize measured no faster.)
-  const int nch_fq = (pl.SPW + pl.T - 1) / pl.T;
-  const bool fq_regs = nch_fq * 16 + pl.SPW * 9 + 4 <= 120 &&
+  const int nch_fq = (pl.SPW + pl.T - 1) / pl.T, mb_fq = (a.M + 15) / 16;
+  const bool fq_regs = nch_fq * 16 * mb_fq + pl.SPW * 9 + 4 * mb_fq <= 120 &&
                        (size_t)a.M * (pl.Sp * 128 + 16) + (size_t)a.M * (pl.Sp * 4 + 4) <=
                            160 * 1024 - 64;
-  if (fq && a.M <= 16 && a.M * pl.Sp <= 1024 && fq_regs)
+  if (fq && a.M <= 32 && a.M * pl.Sp <= 1024 && fq_regs)
     return launch_2d_mb<true>(b, pl.T, pl.SPW, stream);
   if (fq) {
     hipError_t e = launch_quantize(a.x, a.M, a.K, a.ld_x, a.a_q, a.a_s, stream);

@@ -445,6 +445,17 @@ def test_every_2d_plan(M, plan, monkeypatch):
     run_case(M, 512, 2048, seed=M + len(plan))
 
 
+@pytest.mark.parametrize("plan", ["1,1", "2,1", "4,1", "2,2", "4,2", "1,4", "4,4", "2,8"])
+@pytest.mark.parametrize("M", [9, 17, 32])
+def test_every_2d_plan_bf16_input(M, plan, monkeypatch):
+    # BF16 input on the 2D kernel: quantized while staging (one or two
+    # 32-blocks per thread) where the plan's part fits, else by a quantize
+    # launch first; the codes the kernel writes out are checked bit for bit.
+    monkeypatch.setenv("MXG_DIRECT_KERNEL", "2d")
+    monkeypatch.setenv("MXG_PLAN", plan)
+    run_case(M, 512, 2048, seed=M + 3 * len(plan), fused=True)
+
+
 @pytest.mark.parametrize("rsplit", ["1", "2", "4"])
 @pytest.mark.parametrize("M,N,K,fused", [(1, 256, 1024, False), (5, 1024, 2048, True),
                                          (16, 2048, 5120, False), (4, 2048, 5120, True),
