@@ -72,12 +72,21 @@ int chain_direct(const mxg_chain& c, hipStream_t stream) {
   GemmArgs a{nullptr, 0, const_cast<uint8_t*>(c.a_q), const_cast<uint8_t*>(c.a_s), c.wA.q, c.wA.s,
              c.out_a, M, (int)c.wA.N, (int)c.wA.K};
   set_ksplit(a, c.workspace, mxg::kGemmPartOffset);
-  hipError_t e = mxg::launch_gemm(a, stream);
-  if (e != hipSuccess) return MXG_ERR_DEVICE;
-  GemmArgs b{c.out_a, c.wA.N, c.b_q, c.b_s, c.wB.q, c.wB.s, c.out_b, M, (int)c.wB.N, (int)c.wB.K};
-  // B quantizes A's leading columns while staging them (RMS-normalising
-  // them first when a gain is given), or launches that step on its own
+  // A writes the MXFP8 of its leading wB.K columns itself where its kernel
+  // can (each 32-column block in one workgroup's epilogue); otherwise B
+  // quantizes them while staging them (RMS-normalising them first when a
+  // gain is given, which needs whole rows), or launches that step on its own
   // first where its kernel cannot.
+  if (!c.norm_weight) {
+    a.out_q = c.b_q;
+    a.out_s = c.b_s;
+    a.qn = (int)c.wB.K;
+  }
+  bool a_quantized = false;
+  hipError_t e = mxg::launch_gemm(a, stream, &a_quantized);
+  if (e != hipSuccess) return MXG_ERR_DEVICE;
+  GemmArgs b{a_quantized ? nullptr : c.out_a, c.wA.N, c.b_q, c.b_s, c.wB.q, c.wB.s, c.out_b, M,
+             (int)c.wB.N, (int)c.wB.K};
   b.norm_w = c.norm_weight;
   b.norm_eps = c.norm_eps;
   b.norm_y = c.b_bf16;

@@ -26,6 +26,7 @@
 //     badly): a workgroup takes 1, 2 or 4 weight tiles over one K part, the
 //     activations go through LDS in 2048-wide K chunks, and K parts are
 //     summed across workgroups in part order by the last to arrive.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -690,6 +691,30 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) s_red[(wave * MB + mb) * 64 + lane] = acc[mb];
   __syncthreads();
+  // Output MXFP8 (out_q): the tile group's BF16 outputs are also put in an
+  // LDS tile [16 MB rows][16 T columns] beside the partial tiles and, after
+  // a barrier, quantized per 32 columns, one block per thread.
+  const bool qz = T >= 2 && p.out_q != nullptr && 16 * T * tg < p.qn;   // workgroup-uniform
+  uint16_t* s_q = reinterpret_cast<uint16_t*>(smem + kM16Waves * MB * 64 * 16);
+  auto q_put = [&](int m, int n, uint2 o) {
+    *reinterpret_cast<uint2*>(s_q + m * (16 * T) + (n - 16 * T * tg)) = o;
+  };
+  auto q_flush = [&]() {
+    __syncthreads();
+    constexpr int BPR = T / 2 > 0 ? T / 2 : 1;          // 32-column blocks per row
+    const int row = tid / BPR, cb = tid - row * BPR, col = 16 * T * tg + 32 * cb;
+    if (row < M && col < p.qn) {
+      const v4i* v = reinterpret_cast<const v4i*>(s_q + row * (16 * T) + 32 * cb);
+      v4i blk[4] = {v[0], v[1], v[2], v[3]};
+      v4i c0, c1;
+      int e;
+      quant_block32(blk, c0, c1, e);
+      uint8_t* qo = p.out_q + (int64_t)row * p.qn + col;
+      *reinterpret_cast<v4i*>(qo) = c0;
+      *reinterpret_cast<v4i*>(qo + 16) = c1;
+      p.out_s[(int64_t)row * (p.qn >> 5) + (col >> 5)] = (uint8_t)(e + 127);
+    }
+  };
   if (P == 1 && T * MB <= kM16Waves / 4) {
     // Few units: each spread over four waves (one of its 256 sums per thread).
     const int u = wave >> 2, t4 = tid & 255, l = t4 >> 2;
@@ -699,9 +724,12 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
       uint2 o;
       if (quad_bf16(sum_slices(reinterpret_cast<const float*>(s_red) + u * 256, WPT, T * MB * 256, t4),
                     t4, o) &&
-          m < M)
+          m < M) {
         *reinterpret_cast<uint2*>(p.out + (int64_t)m * p.N + n) = o;
+        if (qz) q_put(m, n, o);
+      }
     }
+    if (qz) q_flush();
     return;
   }
   // Otherwise wave tt * MB + mb sums tile tt's row block mb.
@@ -721,7 +749,9 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
       o.x = f32_to_bf16(sum[0]) | (f32_to_bf16(sum[1]) << 16);
       o.y = f32_to_bf16(sum[2]) | (f32_to_bf16(sum[3]) << 16);
       *reinterpret_cast<uint2*>(p.out + (int64_t)m * p.N + n) = o;
+      if (qz) q_put(m, n, o);
     }
+    if (qz) q_flush();
     return;
   }
   // K split: FP32 tile sums to the workspace (device-coherent), then one
@@ -752,9 +782,11 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
       o.x = f32_to_bf16(tot[0]) | (f32_to_bf16(tot[1]) << 16);
       o.y = f32_to_bf16(tot[2]) | (f32_to_bf16(tot[3]) << 16);
       *reinterpret_cast<uint2*>(p.out + (int64_t)m * p.N + n) = o;
+      if (qz) q_put(m, n, o);
     }
   }
   if (tid == 0) __hip_atomic_store(p.ctr + tg * kCtrStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (qz) q_flush();
 }
 
 // ------------------------------------------------------------------ launch
@@ -979,6 +1011,9 @@ hipError_t launch_2d(const GemmArgs& a, hipStream_t stream) {
   const size_t whole_lds = (size_t)Mb * (a.Sp * 128 + 16) + (size_t)Mb * (a.Sp * 4 + 4);
   const bool whole = kRegs && NCH > 1 && whole_lds <= 160 * 1024 - 64;
   const dim3 grid((a.N / 16 / T) * a.P * ((a.M + kRowBlock - 1) / kRowBlock));
+  // with out_q: the partial tiles, then the BF16 output tile of 16 MB x 16 T
+  size_t lds_min = gemm_2d_lds_bytes(Mb, MB);
+  if (a.out_q) lds_min = std::max(lds_min, (size_t)kM16Waves * MB * 64 * 16 + (size_t)512 * MB * T);
   if (whole) {
     auto kern = gemm_2d_kernel<MB, T, SPW, (kRegs ? NCH : 1), CHM, FQ>;
     static bool configured = false;
@@ -990,7 +1025,7 @@ hipError_t launch_2d(const GemmArgs& a, hipStream_t stream) {
       if (e != hipSuccess) return e;
       configured = true;
     }
-    size_t lds = gemm_2d_lds_bytes(Mb, MB);
+    size_t lds = lds_min;
     if (whole_lds > lds) lds = (whole_lds + 15) & ~(size_t)15;
     hipLaunchKernelGGL(kern, grid, dim3(kM16Waves * 64), lds, stream, a);
   } else {
@@ -1003,7 +1038,7 @@ hipError_t launch_2d(const GemmArgs& a, hipStream_t stream) {
       if (e != hipSuccess) return e;
       configured = true;
     }
-    hipLaunchKernelGGL(kern, grid, dim3(kM16Waves * 64), gemm_2d_lds_bytes(Mb, MB), stream, a);
+    hipLaunchKernelGGL(kern, grid, dim3(kM16Waves * 64), lds_min, stream, a);
   }
   return hipGetLastError();
 }
@@ -1131,7 +1166,8 @@ bool m16_half_tiles_wide(int M, int N, int K, bool fq) {
   return !fq && M <= 4 && K >= 4096 && tiles > G && 2 * (tiles - G) <= G;
 }
 
-hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
+hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream, bool* quantized_out) {
+  if (quantized_out) *quantized_out = false;
   GemmArgs a = args;
   if (a.lda == 0) a.lda = a.K;
   const bool fq = a.x != nullptr;
@@ -1142,6 +1178,7 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
     // 64 rows), MXFP8 input (BF16 input is quantized by its own launch
     // first).
     if (a.group_tiles != 0) return hipErrorInvalidValue;
+    a.out_q = a.out_s = nullptr;                         // not on row blocks
     if (fq) {
       hipError_t e = launch_quantize(a.x, a.M, a.K, a.ld_x, a.a_q, a.a_s, stream);
       if (e != hipSuccess) return e;
@@ -1186,7 +1223,7 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
     GemmArgs b = a;
     b.x = nullptr;
     b.norm_w = nullptr;
-    return launch_gemm(b, stream);
+    return launch_gemm(b, stream, quantized_out);
   }
   // A weight of G < tiles <= 1.5 G tiles with BF16 input: one tile per CU
   // plus half a leftover tile for some, no sum across workgroups.  A read of
@@ -1240,7 +1277,7 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
     if (e != hipSuccess) return e;
     GemmArgs b = a;
     b.x = nullptr;
-    return launch_gemm(b, stream);
+    return launch_gemm(b, stream, quantized_out);
   }
   // Otherwise the 2D kernel.  BF16 input is quantized while staging when
   // M <= 32 and a workgroup's share is small (M * Sp <= 1024: at most four
@@ -1256,14 +1293,21 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
   const bool fq_regs = nch_fq * 16 * mb_fq + pl.SPW * 9 + 4 * mb_fq <= 120 &&
                        (size_t)a.M * (pl.Sp * 128 + 16) + (size_t)a.M * (pl.Sp * 4 + 4) <=
                            160 * 1024 - 64;
-  if (fq && a.M <= 32 && a.M * pl.Sp <= 1024 && fq_regs)
-    return launch_2d_mb<true>(b, pl.T, pl.SPW, stream);
-  if (fq) {
-    hipError_t e = launch_quantize(a.x, a.M, a.K, a.ld_x, a.a_q, a.a_s, stream);
-    if (e != hipSuccess) return e;
+  // The output's MXFP8 in the epilogue where a workgroup holds whole 32-column
+  // blocks (two or more weight tiles).
+  const bool qz = b.out_q && pl.T >= 2 && b.qn > 0 && b.qn % 32 == 0 && b.qn <= b.N;
+  if (!qz) b.out_q = b.out_s = nullptr;
+  hipError_t e;
+  if (fq && a.M <= 32 && a.M * pl.Sp <= 1024 && fq_regs) {
+    e = launch_2d_mb<true>(b, pl.T, pl.SPW, stream);
+  } else {
+    if (fq && (e = launch_quantize(a.x, a.M, a.K, a.ld_x, a.a_q, a.a_s, stream)) != hipSuccess)
+      return e;
+    b.x = nullptr;
+    e = launch_2d_mb<false>(b, pl.T, pl.SPW, stream);
   }
-  b.x = nullptr;
-  return launch_2d_mb<false>(b, pl.T, pl.SPW, stream);
+  if (e == hipSuccess && qz && quantized_out) *quantized_out = true;
+  return e;
 }
 
 }  // namespace mxg

@@ -42,6 +42,14 @@ struct GemmArgs {
   const uint16_t* norm_w = nullptr;
   float norm_eps = 0.f;
   uint16_t* norm_y = nullptr;
+  // Also write the MXFP8 of output columns [0, qn) (qn % 32 == 0, qn <= N),
+  // quantized from the BF16 outputs as launch_quantize would: codes to
+  // out_q [M, qn], scale bytes to out_s [M, qn / 32].  Only the 2D kernel
+  // with two or more weight tiles per workgroup and at most 64 rows does it;
+  // launch_gemm reports whether the call did.
+  uint8_t* out_q = nullptr;
+  uint8_t* out_s = nullptr;
+  int qn = 0;
 };
 
 // Bytes of FP32 partials the GEMM of this shape needs (0: no K split).
@@ -63,7 +71,8 @@ constexpr size_t kGemmPartOffset = kCtrRegionBytes;
 hipError_t launch_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
                            uint8_t* q, uint8_t* s, hipStream_t stream);
 
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+// *quantized_out (when given) is set to whether out_q / out_s were written.
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream, bool* quantized_out = nullptr);
 
 // 64 x 64-tile GEMM for more than 64 rows (gemm_big.hip): MXFP8 input,
 // N % 64 == 0, row-major activation scales.

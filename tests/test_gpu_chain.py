@@ -80,6 +80,17 @@ def test_chain_small(M, chain_path):
     run_chain(M, dims=SMALL, seed=M)
 
 
+@pytest.mark.parametrize("plan", ["2,1", "4,1", "2,2", "4,4", "2,8"])
+@pytest.mark.parametrize("M", [3, 17, 48])
+def test_chain_plans(M, plan, chain_path, monkeypatch):
+    # Every GEMM of the chain on the 2D kernel with a forced (tiles, K parts)
+    # plan: A then writes B's MXFP8 input in its epilogue (one or several K
+    # parts), which must be exactly the quantization of A's BF16 output.
+    monkeypatch.setenv("MXG_DIRECT_KERNEL", "2d")
+    monkeypatch.setenv("MXG_PLAN", plan)
+    run_chain(M, dims=SMALL, seed=M + 7 * len(plan))
+
+
 @pytest.mark.parametrize("M", [1, 8, 32])
 def test_chain_full_size(M, chain_path):
     run_chain(M)
