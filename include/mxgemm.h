@@ -285,6 +285,9 @@ typedef struct {
  * The stages run as three launches in stream order (each stage's weight
  * read starts when the previous launch ends): on MI355X a dependency between
  * workgroups of one persistent launch measured slower than a launch boundary.
+ * The requantize runs inside one of them: in A's epilogue where A's kernel
+ * holds whole 32-column blocks of its output per workgroup, otherwise in B's
+ * activation staging.
  *
  * Shapes: 1 <= M <= 48; each weight N % 16 == 0, K % 128 == 0; wB.K <= wA.N,
  * wB.K % 128 == 0.  out_a/out_b/out_c are BF16 [M, N] row-major, b_q/b_s
@@ -296,7 +299,8 @@ typedef struct {
  * aligned; norm_eps >= 0), out_a[:, 0:wB.K] is RMS-normalised as
  * mxfp8_rmsnorm_quantize does and the BF16 result is what is requantized;
  * it is also written to b_bf16 ([M, wB.K] BF16) when that is non-NULL.
- * This takes one more launch between A and B.  norm_weight NULL: the plain
+ * B normalises the rows while staging them up to 16 rows; above that the
+ * norm takes one more launch between A and B.  norm_weight NULL: the plain
  * requantize.
  */
 typedef struct {
