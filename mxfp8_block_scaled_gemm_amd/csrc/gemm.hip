@@ -295,12 +295,12 @@ void gemm_m16_kernel(GemmArgs p) {
         }
       }
       __syncthreads();
-      if (wave < M) {
+      for (int row = wave; row < M; row += W) {               // W waves, up to 16 rows
         float t = 0.f;
-        for (int b = lane; b < KB; b += 64) t = t + s_ss[wave * KB + b];
+        for (int b = lane; b < KB; b += 64) t = t + s_ss[row * KB + b];
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) t = t + __shfl_xor(t, o);
-        if (lane == 0) s_r[wave] = 1.0f / __builtin_sqrtf(t / (float)K + p.norm_eps);
+        if (lane == 0) s_r[row] = 1.0f / __builtin_sqrtf(t / (float)K + p.norm_eps);
       }
       __syncthreads();
 #pragma unroll
@@ -428,7 +428,7 @@ constexpr int kCtrStride = 32;
 // tile are summed through LDS in wave order; with P > 1 the FP32 tile sums
 // go to the workspace and the last of the P workgroups of a tile group to
 // arrive adds them in part order (deterministic) and stores BF16.
-template <int MB, int T, int SPW, int NB, int CHM, bool FQ>
+template <int MB, int T, int SPW, int NB, int CHM, bool FQ, bool NRM = false>
 __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
   // Row block y: rows [64 y, 64 y + 64) of the activations and the output,
   // with their own K-split partials and tile counters (a GEMM of more than
@@ -465,6 +465,7 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
   constexpr int FQB = FQ ? MB : 0;                      // BF16 blocks per thread per chunk
   constexpr int CHL = FQ ? 4 * FQB : CHM;
   static_assert(!FQ || MB <= 2, "BF16 staging serves up to 32 rows");
+  static_assert(!NRM || (FQ && NB == 1), "the norm runs in the BF16 staging of one chunk");
   constexpr int W = kM16Waves, kT = W * 64, WPT = W / T;  // waves per tile
   constexpr int kLdA = 16 * 128 + 16;                   // LDS bytes per code row of a chunk
   constexpr int kLdS = 16 * 4 + 4;                      // LDS bytes per scale row of a chunk
@@ -572,7 +573,8 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
     }
   };
 
-  // 1. Activations (chunk 0, or all chunks) ahead of the weight stream.
+  // 1. Activations (chunk 0, or all chunks) ahead of the weight stream; with
+  //    the norm, its gain too (one 16-byte piece per thread, K <= 2048).
   v4i st[NB][CHL];
   uint32_t sc[NB];
 #pragma unroll
@@ -584,6 +586,10 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
         stage_load(c, st[c], sc[c]);
     }
   }
+  v4i gst = {0, 0, 0, 0};
+  if constexpr (NRM)
+    gst = buf_ld16(make_rsrc(p.norm_w, (uint32_t)(K * 2)),
+                   tid < (K >> 3) ? (uint32_t)(tid * 16) : kOutOfRange);
   __builtin_amdgcn_sched_barrier(0);
 
   // 2. The weight stream: slot j = step wi + WPT j of my tile.
@@ -655,6 +661,69 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     if (c < nch) {                                      // uniform
+      if constexpr (NRM) {
+        // RMSNorm of the staged rows (the part is all of K, one chunk): as in
+        // the M <= 16 kernel, block sums of squares (each product and sum
+        // rounded on its own) to LDS, then a wave per row adds its blocks in
+        // block order (lane l: block l, then a fixed butterfly), then
+        // y = BF16((x * r) * w) replaces the staged values.
+        const int KB = K >> 5;
+        float* s_ss = reinterpret_cast<float*>(smem + ((M * kLdA + M * kLdS + 15) & ~15));
+        float* s_r = s_ss + M * KB;
+        uint8_t* s_gain = reinterpret_cast<uint8_t*>(s_r + ((M + 3) & ~3));
+        if (tid < (K >> 3)) *reinterpret_cast<v4i*>(s_gain + tid * 16) = gst;
+#pragma unroll
+        for (int f = 0; f < FQB; ++f) {
+          const int blk = tid + f * kT;                 // row blk / KB, block blk % KB
+          if (blk < M * KB) {
+            float ss = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+              for (int h = 0; h < 4; ++h) {
+                const uint32_t u = (uint32_t)st[0][4 * f + k][h];
+                const float a = bf16_lo(u), b = bf16_hi(u);
+                ss = ss + a * a;
+                ss = ss + b * b;
+              }
+            s_ss[blk] = ss;
+          }
+        }
+        __syncthreads();
+        for (int row = wave; row < M; row += kM16Waves) {
+          float t = 0.f;
+          for (int b = lane; b < KB; b += 64) t = t + s_ss[row * KB + b];
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1) t = t + __shfl_xor(t, o);
+          if (lane == 0) s_r[row] = 1.0f / __builtin_sqrtf(t / (float)K + p.norm_eps);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int f = 0; f < FQB; ++f) {
+          const int blk = tid + f * kT;
+          if (blk < M * KB) {
+            const int row = blk / KB, cb = blk - row * KB;
+            const float rr = s_r[row];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const v4i gk = *reinterpret_cast<const v4i*>(s_gain + cb * 64 + 16 * k);
+#pragma unroll
+              for (int h = 0; h < 4; ++h) {
+                const uint32_t xu = (uint32_t)st[0][4 * f + k][h], wu = (uint32_t)gk[h];
+                const float lo = (bf16_lo(xu) * rr) * bf16_lo(wu);
+                const float hi = (bf16_hi(xu) * rr) * bf16_hi(wu);
+                st[0][4 * f + k][h] = (int)(f32_to_bf16(lo) | (f32_to_bf16(hi) << 16));
+              }
+            }
+            if (tg == 0 && p.norm_y) {
+#pragma unroll
+              for (int k = 0; k < 4; ++k)
+                *reinterpret_cast<v4i*>(p.norm_y + (int64_t)row * K + cb * 32 + 8 * k) =
+                    st[0][4 * f + k];
+            }
+          }
+        }
+      }
       if constexpr (FQ)
         park_bf16(c, st[NB > 1 ? c : 0], s_act, kLdA, s_scl, kLdS);
       else
@@ -1062,6 +1131,49 @@ hipError_t launch_2d_t(const GemmArgs& a, int T, int spw, hipStream_t stream) {
   return launch_2d_spw<MB, 4, FQ>(a, spw, stream);
 }
 
+// The RMSNorm in the 2D kernel's BF16 staging: two weight tiles per
+// workgroup, no K split, the part one staging chunk (K <= 2048), at most 32
+// rows.  LDS: the chunk's codes and scales, then the norm's block sums [M][K/32],
+// row factors [M] and gain [K].
+size_t gemm_2d_norm_lds_bytes(int M, int K) {
+  const size_t chunk = ((size_t)M * (16 * 128 + 16) + (size_t)M * (16 * 4 + 4) + 15) & ~(size_t)15;
+  return chunk + (size_t)M * (K / 32) * 4 + (size_t)((M + 3) & ~3) * 4 + (size_t)K * 2;
+}
+
+bool gemm_2d_norm_fits(const GemmArgs& a) {
+  return a.x && a.norm_w && a.M <= 32 && a.K <= 2048 && (a.N / 16) % 2 == 0 && a.group_tiles == 0 &&
+         (a.lda == 0 || a.lda == a.K) &&
+         std::max(gemm_2d_lds_bytes(a.M, (a.M + 15) / 16), gemm_2d_norm_lds_bytes(a.M, a.K)) <=
+             160 * 1024 - 64;
+}
+
+template <int MB, int SPW>
+hipError_t launch_2d_norm_k(const GemmArgs& a, hipStream_t stream) {
+  constexpr int CHM = (MB * 16 * 16 * 8 + kM16Waves * 64 - 1) / (kM16Waves * 64);
+  auto kern = gemm_2d_kernel<MB, 2, SPW, 1, CHM, true, true>;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 64);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  const size_t lds = std::max(gemm_2d_lds_bytes(a.M, MB), gemm_2d_norm_lds_bytes(a.M, a.K));
+  hipLaunchKernelGGL(kern, dim3(a.N / 32), dim3(kM16Waves * 64), lds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_2d_norm(const GemmArgs& args, hipStream_t stream) {
+  GemmArgs a = args;
+  const int S = a.K / 128;
+  a.P = 1;
+  a.Sp = S;
+  a.out_q = a.out_s = nullptr;
+  const bool one = (2 * S + 15) / 16 <= 1;               // weight slots per wave: 1 or 2
+  if (a.M <= 16) return one ? launch_2d_norm_k<1, 1>(a, stream) : launch_2d_norm_k<1, 2>(a, stream);
+  return one ? launch_2d_norm_k<2, 1>(a, stream) : launch_2d_norm_k<2, 2>(a, stream);
+}
+
 // With BF16 input only for M <= 32 (larger row counts would spill the
 // staging registers); the caller quantizes the others first.
 template <bool FQ>
@@ -1202,16 +1314,32 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream, bool* quantized
   const int S = a.K / 128;
   int force = forced_kernel();                             // tests: 1 = M <= 16, 2 = 2D, 3 = HALF
   if (a.norm_w) {
-    // The norm runs in the M <= 16 kernel's BF16 staging when that kernel
-    // takes the shape with the quantize inside (16 waves, at most two
-    // 32-blocks per thread and M * K <= 65536 per CU round); otherwise
-    // RMSNorm + MXFP8 runs as its own launch and the GEMM reads the codes.
+    // Where the norm runs (every workgroup normalises the rows it stages, so
+    // its vector work grows with the rows and the workgroups; measured on
+    // MI355X, the chain at N 8192, K 1536 for B):
+    //   * M <= 4: in the M <= 16 kernel's BF16 staging (M = 1: 20.0 us for
+    //     the chain against 20.2 in the 2D kernel, 22.0 with a launch);
+    //   * 5 <= M <= 16: in the 2D kernel's staging, two tiles per workgroup,
+    //     no K split (M = 8 / 12 / 16: 23.5 / 24.8 / 26.4 us against 24.0 /
+    //     26.5 / 28.3 in the M <= 16 kernel and 25.0 / 25.5 / 26.8 with a
+    //     launch);
+    //   * above 16 rows, or where neither form takes the shape: RMSNorm +
+    //     MXFP8 as its own launch, and the GEMM reads the codes (M = 32:
+    //     32.3 us against 34.7 in the 2D kernel).
+    // MXG_NORM_KERNEL=2d|m16|launch forces the form where it takes the shape
+    // (tests and sweeps).
+    const char* nk = std::getenv("MXG_NORM_KERNEL");
+    const int nforce = !nk ? 0 : std::strcmp(nk, "2d") == 0 ? 1 : std::strcmp(nk, "m16") == 0 ? 2
+                                 : std::strcmp(nk, "launch") == 0 ? 3 : 0;
+    const bool norm2d = gemm_2d_norm_fits(a) && force != 1 && force != 3 &&
+                        (nforce == 1 || (nforce == 0 && (force == 2 || (a.M > 4 && a.M <= 16))));
+    if (norm2d) return launch_2d_norm(a, stream);
     constexpr int NW = kNormWaves, NT = NW * 64;
     const int per_cu = (a.N / 16 + device_cus() - 1) / device_cus();
     const bool inline_ok = a.x && a.M <= 16 && (a.M * a.K / 32) * per_cu <= 2048 &&
                            a.M * a.K / 32 <= 2 * NT && a.K <= 8 * NT && (S + NW - 1) / NW <= 4 &&
                            gemm_m16_lds_bytes(a.M, a.K, NW) + (size_t)a.K * 2 <= 160 * 1024 &&
-                           force != 2 && force != 3;
+                           force != 2 && force != 3 && nforce != 1 && nforce != 3;
     if (inline_ok) {
       GemmArgs b = a;
       b.rsplit = m16_row_split(a.N, a.K, true);

@@ -168,12 +168,21 @@ def run_chain_norm(M, dims=None, seed=0):
     assert 1.0 - np.mean(gq == ref.b_q) < 0.02
 
 
-@pytest.mark.parametrize("M", [1, 17, 48])
-def test_chain_with_norm_small(M, chain_path):
-    # with a norm the three-launch form runs on either path selection
+@pytest.mark.parametrize("form", [None, "2d", "m16", "launch"])
+@pytest.mark.parametrize("M", [1, 5, 9, 16, 17, 32, 48])
+def test_chain_with_norm_small(M, form, chain_path, monkeypatch):
+    # The norm inside B's staging on the 2D kernel (up to 32 rows) or on the
+    # M <= 16 kernel (up to 16), or as a launch of its own: routed, and each
+    # form forced (MXG_NORM_KERNEL; a form that does not take the shape
+    # leaves it to the next).
+    if form:
+        monkeypatch.setenv("MXG_NORM_KERNEL", form)
     run_chain_norm(M, dims=SMALL, seed=M)
 
 
-@pytest.mark.parametrize("M", [1, 8, 32])
-def test_chain_with_norm_full_size(M):
+@pytest.mark.parametrize("form", [None, "2d", "m16"])
+@pytest.mark.parametrize("M", [1, 8, 16, 32])
+def test_chain_with_norm_full_size(M, form, monkeypatch):
+    if form:
+        monkeypatch.setenv("MXG_NORM_KERNEL", form)
     run_chain_norm(M)
