@@ -428,7 +428,7 @@ constexpr int kCtrStride = 32;
 // tile are summed through LDS in wave order; with P > 1 the FP32 tile sums
 // go to the workspace and the last of the P workgroups of a tile group to
 // arrive adds them in part order (deterministic) and stores BF16.
-template <int MB, int T, int SPW, int NB, int CHM, bool FQ, bool NRM = false>
+template <int MB, int T, int SPW, int NB, int CHM, bool FQ, bool NRM = false, bool WL = false>
 __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
   // Row block y: rows [64 y, 64 y + 64) of the activations and the output,
   // with their own K-split partials and tile counters (a GEMM of more than
@@ -466,6 +466,10 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
   constexpr int CHL = FQ ? 4 * FQB : CHM;
   static_assert(!FQ || MB <= 2, "BF16 staging serves up to 32 rows");
   static_assert(!NRM || (FQ && NB == 1), "the norm runs in the BF16 staging of one chunk");
+  static_assert(!WL || (!FQ && !NRM && NB == 1 && T * MB <= 8), "wave-local: MXFP8 input");
+  // Partial tiles each wave parks for the sums: its tile's row tiles, or
+  // (wave-local) every tile's.
+  constexpr int RU = WL ? T * MB : MB;
   constexpr int W = kM16Waves, kT = W * 64, WPT = W / T;  // waves per tile
   constexpr int kLdA = 16 * 128 + 16;                   // LDS bytes per code row of a chunk
   constexpr int kLdS = 16 * 4 + 4;                      // LDS bytes per scale row of a chunk
@@ -579,11 +583,34 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
   uint32_t sc[NB];
 #pragma unroll
   for (int c = 0; c < NB; ++c) {
-    if (c < nch) {
+    if (!WL && c < nch) {
       if constexpr (FQ)
         load_bf16(c, st[c]);
       else
         stage_load(c, st[c], sc[c]);
+    }
+  }
+  // Wave-local: no staging.  Wave w takes steps w + 16 j (j < SPW) of every
+  // tile of the group and loads the MFMA B operands of those steps itself
+  // (row 16 mb + r's 32 code bytes and scale byte, rows past M clamped to
+  // row M - 1, whose outputs are never stored), each used for T MFMAs.
+  v4i blo[WL ? SPW : 1][MB], bhi[WL ? SPW : 1][MB];
+  uint32_t bsc[WL ? SPW : 1][MB];
+  if constexpr (WL) {
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      const int stp = wave + kM16Waves * j;
+      const bool ok = stp < ns;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int m = min(16 * mb + r, M - 1);
+        const uint32_t off = (uint32_t)(m * lda + (k0 + stp) * 128 + 16 * g);
+        blo[j][mb] = buf_ld16(ra, ok ? off : kOutOfRange);
+        bhi[j][mb] = buf_ld16(ra, ok ? off + 64 : kOutOfRange);
+        bsc[j][mb] = buf_ld8(
+            rs, ok ? (uint32_t)(act_scale_dword(srow0 + m, k0 + stp, ldas, p.a_sf128, S) + g)
+                   : kOutOfRange);
+      }
     }
   }
   v4i gst = {0, 0, 0, 0};
@@ -595,13 +622,16 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
   // 2. The weight stream: slot j = step wi + WPT j of my tile.
   const auto rw = make_rsrc(p.w_q, (uint32_t)((p.N >> 4) * S * 2048));
   const auto rws = make_rsrc(p.w_s, (uint32_t)((p.N >> 4) * S * 64));
-  v4i wlo[SPW], whi[SPW];
-  uint32_t wsc[SPW];
+  constexpr int NW = WL ? SPW * T : SPW;                // weight slots per wave
+  v4i wlo[NW], whi[NW];
+  uint32_t wsc[NW];
 #pragma unroll
-  for (int j = 0; j < SPW; ++j) {
-    const int stp = wi + WPT * j;
+  for (int j = 0; j < NW; ++j) {
+    // wave-local: slot j = step wave + 16 (j / T) of tile j % T
+    const int stp = WL ? wave + kM16Waves * (j / T) : wi + WPT * j;
+    const int wt = WL ? tg * T + j % T : tile;
     const bool ok = stp < ns;
-    const uint32_t chunk = (uint32_t)(tile * S + k0 + stp);
+    const uint32_t chunk = (uint32_t)(wt * S + k0 + stp);
     wlo[j] = buf_ld16_nt(rw, ok ? chunk * 2048 + lane * 16 : kOutOfRange);
     whi[j] = buf_ld16_nt(rw, ok ? chunk * 2048 + 1024 + lane * 16 : kOutOfRange);
     wsc[j] = buf_ld8(rws, ok ? chunk * 64 + lane : kOutOfRange);
@@ -612,11 +642,24 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
   //    When every chunk is in registers and the part fits LDS, all chunks
   //    are parked side by side behind one barrier and each wave then runs
   //    its MFMAs as its own weights land.
-  v4f acc[MB];
+  v4f acc[RU];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < RU; ++u) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
   constexpr int NCH = (SPW + T - 1) / T;
-  if constexpr (NB == NCH && NB > 1) {
+  if constexpr (WL) {
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      if (wave + kM16Waves * j < ns) {                  // wave-uniform
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            acc[t * MB + mb] = mfma_mx16(cat8(wlo[j * T + t], whi[j * T + t]),
+                                         cat8(blo[j][mb], bhi[j][mb]), acc[t * MB + mb],
+                                         (int)wsc[j * T + t], (int)bsc[j][mb]);
+      }
+    }
+  } else if constexpr (NB == NCH && NB > 1) {
     const int ldA = Sp * 128 + 16, ldS = Sp * 4 + 4;
     uint8_t* w_scl = smem + M * ldA;
 #pragma unroll
@@ -757,14 +800,18 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
   }
 
   // 4. Per (tile, row block) unit: sum its WPT partial tiles in wave order.
+  // Unit u = (tile t, row tile mb), t * MB + mb, has NSL partial tiles
+  // (slices) in wave order, slice i of unit u at s_red[(u + T MB i) * 64]:
+  // WPT waves per tile, or every wave when wave-local.
+  constexpr int NSL = WL ? kM16Waves : WPT;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) s_red[(wave * MB + mb) * 64 + lane] = acc[mb];
+  for (int u = 0; u < RU; ++u) s_red[(wave * RU + u) * 64 + lane] = acc[u];
   __syncthreads();
   // Output MXFP8 (out_q): the tile group's BF16 outputs are also put in an
   // LDS tile [16 MB rows][16 T columns] beside the partial tiles and, after
   // a barrier, quantized per 32 columns, one block per thread.
   const bool qz = T >= 2 && p.out_q != nullptr && 16 * T * tg < p.qn;   // workgroup-uniform
-  uint16_t* s_q = reinterpret_cast<uint16_t*>(smem + kM16Waves * MB * 64 * 16);
+  uint16_t* s_q = reinterpret_cast<uint16_t*>(smem + kM16Waves * RU * 64 * 16);
   auto q_put = [&](int m, int n, uint2 o) {
     *reinterpret_cast<uint2*>(s_q + m * (16 * T) + (n - 16 * T * tg)) = o;
   };
@@ -791,7 +838,7 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
       const int rt = u / MB, rmb = u - rt * MB;
       const int m = 16 * rmb + (l & 15), n = 16 * (tg * T + rt) + 4 * (l >> 4);
       uint2 o;
-      if (quad_bf16(sum_slices(reinterpret_cast<const float*>(s_red) + u * 256, WPT, T * MB * 256, t4),
+      if (quad_bf16(sum_slices(reinterpret_cast<const float*>(s_red) + u * 256, NSL, T * MB * 256, t4),
                     t4, o) &&
           m < M) {
         *reinterpret_cast<uint2*>(p.out + (int64_t)m * p.N + n) = o;
@@ -808,7 +855,7 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
   if (red) {
     sum = s_red[(rt * MB + rmb) * 64 + lane];
 #pragma unroll
-    for (int i = 1; i < WPT; ++i) sum += s_red[((rt + T * i) * MB + rmb) * 64 + lane];
+    for (int i = 1; i < NSL; ++i) sum += s_red[((rt + T * i) * MB + rmb) * 64 + lane];
   }
   const int otile = tg * T + rt;
   const int m = 16 * rmb + (lane & 15), n = 16 * otile + 4 * (lane >> 4);
@@ -1066,6 +1113,56 @@ int device_cus() {
       return 256;
   }
   return cached;
+}
+
+// Wave-local form (MXFP8 input, at most 64 rows, T * MB <= 8): SL steps
+// per wave.
+template <int MB, int T, int SL>
+hipError_t launch_2d_wl(const GemmArgs& a, hipStream_t stream) {
+  constexpr int CHM = (MB * 16 * 16 * 8 + kM16Waves * 64 - 1) / (kM16Waves * 64);
+  auto kern = gemm_2d_kernel<MB, T, SL, 1, CHM, false, false, true>;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 64);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  size_t lds = (size_t)kM16Waves * T * MB * 64 * 16;
+  if (a.out_q) lds += (size_t)512 * MB * T;
+  hipLaunchKernelGGL(kern, dim3((a.N / 16 / T) * a.P), dim3(kM16Waves * 64), lds, stream, a);
+  return hipGetLastError();
+}
+
+template <int MB, int T>
+hipError_t launch_2d_wl_sl(const GemmArgs& a, int sl, hipStream_t stream) {
+  if (sl <= 1) return launch_2d_wl<MB, T, 1>(a, stream);
+  if (sl <= 2) return launch_2d_wl<MB, T, 2>(a, stream);
+  return launch_2d_wl<MB, T, 3>(a, stream);
+}
+
+// Whether the wave-local form takes the plan: MXFP8 input, one row block,
+// T * MB <= 8, at most 3 steps per wave.
+bool wl_fits(const GemmArgs& a, int T, int Sp) {
+  const int MB = (a.M + 15) / 16, sl = (Sp + 15) / 16;
+  if (sl == 3 && ((MB == 1 && T == 4) || (MB == 2 && T == 4) || (MB == 3 && T == 2))) return false;
+  return a.x == nullptr && a.M <= 48 && T * MB <= 8 && sl <= 3;
+}
+
+hipError_t launch_2d_wave_local(const GemmArgs& a, int T, hipStream_t stream) {
+  const int MB = (a.M + 15) / 16, sl = (a.Sp + 15) / 16;
+  if (MB == 1) {
+    if (T == 1) return launch_2d_wl_sl<1, 1>(a, sl, stream);
+    if (T == 2) return launch_2d_wl_sl<1, 2>(a, sl, stream);
+    return launch_2d_wl_sl<1, 4>(a, sl, stream);
+  }
+  if (MB == 2) {
+    if (T == 1) return launch_2d_wl_sl<2, 1>(a, sl, stream);
+    if (T == 2) return launch_2d_wl_sl<2, 2>(a, sl, stream);
+    return launch_2d_wl_sl<2, 4>(a, sl, stream);
+  }
+  if (T == 1) return launch_2d_wl_sl<3, 1>(a, sl, stream);
+  return launch_2d_wl_sl<3, 2>(a, sl, stream);
 }
 
 template <int MB, int T, int SPW, bool FQ>
@@ -1432,7 +1529,24 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream, bool* quantized
     if (fq && (e = launch_quantize(a.x, a.M, a.K, a.ld_x, a.a_q, a.a_s, stream)) != hipSuccess)
       return e;
     b.x = nullptr;
-    e = launch_2d_mb<false>(b, pl.T, pl.SPW, stream);
+    // The wave-local form where every wave has a step of the part (Sp >= 12
+    // of 16 waves) and each B operand feeds two or more weight tiles; with a
+    // shorter part its idle waves leave fewer loads in flight than the
+    // staged form, and one tile per workgroup gains nothing.  Measured on
+    // MI355X (MXFP8 input, M = 17 / 24 / 32, staged -> wave-local, us):
+    // N 8192 K 1536, plan (2, 1): 5.29 / 5.50 / 5.68 -> 4.91 / 5.20 / 5.36;
+    // N 5120 K 8192, (4, 3): 13.65 / 14.09 / 13.88 -> 12.45 / 12.83 / 13.31;
+    // N 8192 K 4096, (2, 1): 11.17 / 11.85 / 12.22 -> 10.35 / 11.20 / 11.97;
+    // and the other way at N 4096 K 5120, (4, 4), Sp = 10: 8.70 / 8.80 ->
+    // 8.79 / 8.99, and N 2048 K 5120, (4, 8), Sp = 5: 7.8 -> 8.4.
+    // MXG_WAVE_LOCAL=1|0 forces the form on (where it takes the plan) or off.
+    const char* wle = std::getenv("MXG_WAVE_LOCAL");
+    const bool wl = wl_fits(b, pl.T, pl.Sp) &&
+                    (wle ? wle[0] == '1' : pl.T >= 2 && pl.Sp >= 12);
+    if (wl)
+      e = launch_2d_wave_local(b, pl.T, stream);
+    else
+      e = launch_2d_mb<false>(b, pl.T, pl.SPW, stream);
   }
   if (e == hipSuccess && qz && quantized_out) *quantized_out = true;
   return e;

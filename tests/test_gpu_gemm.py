@@ -17,15 +17,21 @@ from helpers import check_gemm, dev_bf16, dev_u8, host_bits, host_u8, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=["direct", "direct-m16", "direct-2d"])
+@pytest.fixture(params=["direct", "direct-m16", "direct-2d", "direct-2d-wl"])
 def path(request, monkeypatch):
     """Run a test through the direct kernels: as routed, and with the M <= 16
-    kernel or the 2D-tiled kernel forced wherever it applies."""
+    kernel, the 2D kernel (staged) or the 2D kernel's wave-local form forced
+    wherever it applies."""
     kind, _, kernel = request.param.partition("-")
-    if kernel:
+    monkeypatch.delenv("MXG_DIRECT_KERNEL", raising=False)
+    monkeypatch.delenv("MXG_WAVE_LOCAL", raising=False)
+    if kernel == "2d-wl":
+        monkeypatch.setenv("MXG_DIRECT_KERNEL", "2d")
+        monkeypatch.setenv("MXG_WAVE_LOCAL", "1")
+    elif kernel:
         monkeypatch.setenv("MXG_DIRECT_KERNEL", kernel)
-    else:
-        monkeypatch.delenv("MXG_DIRECT_KERNEL", raising=False)
+        if kernel == "2d":
+            monkeypatch.setenv("MXG_WAVE_LOCAL", "0")
     return request.param
 
 _wcache = {}
@@ -443,6 +449,17 @@ def test_every_2d_plan(M, plan, monkeypatch):
     monkeypatch.setenv("MXG_DIRECT_KERNEL", "2d")
     monkeypatch.setenv("MXG_PLAN", plan)
     run_case(M, 512, 2048, seed=M + len(plan))
+
+
+@pytest.mark.parametrize("plan", ["1,1", "2,1", "4,1", "1,2", "2,2", "4,2", "2,3", "4,4"])
+@pytest.mark.parametrize("M", [9, 17, 32, 48])
+def test_every_2d_plan_wave_local(M, plan, monkeypatch):
+    # The wave-local form (each wave loads its own B operands) on every plan
+    # it takes, K parts of 1..3 steps per wave included.
+    monkeypatch.setenv("MXG_DIRECT_KERNEL", "2d")
+    monkeypatch.setenv("MXG_WAVE_LOCAL", "1")
+    monkeypatch.setenv("MXG_PLAN", plan)
+    run_case(M, 512, 4096, seed=M + 5 * len(plan))
 
 
 @pytest.mark.parametrize("plan", ["1,1", "2,1", "4,1", "2,2", "4,2", "1,4", "4,4", "2,8"])
