@@ -118,9 +118,11 @@ def gemm_bytes(M: int, N: int, K: int, bf16_in: bool) -> int:
     return mx_bytes(N, K) + act + 2 * M * N
 
 
-def weight_copies(N: int, K: int, dev):
-    """Identical MXFP8 weight copies, enough to cycle ROTATE_BYTES."""
-    w = mx.PackedWeight.from_bf16(synth.gemm_case(1, N, K, seed=0)["w"].to(dev))
+def weight_copies(N: int, K: int, dev, row_major: bool = False):
+    """Identical MXFP8 weight copies, enough to cycle ROTATE_BYTES (packed, or
+    [N, K] / [N, K/32] as quantized with row_major)."""
+    q, s = mx.mxfp8_quantize(synth.gemm_case(1, N, K, seed=0)["w"].to(dev))
+    w = mx.RowMajorWeight(q, s) if row_major else mx.PackedWeight.from_rows(q, s)
     n = max(2, math.ceil(ROTATE_BYTES / mx_bytes(N, K)))
     return [w.clone() for _ in range(n)]
 
@@ -391,6 +393,7 @@ def case_names():
     for (N, K) in ((4096, 5120), (5120, 8192), (8192, 1536)):
         names += [f"M{M} N{N} K{K}" for M in (16, 32, 48)]
     names += [f"rows above 48: M{M} N4096 K5120" for M in (64, 128, 256)]
+    names += [f"row-major weights: M{M} N4096 K5120" for M in (1, 8, 48)]
     names += [f"chain M{M}" for M in (1, 8, 32)]
     names += [f"chain+norm M{M}" for M in (1, 8, 32)]
     names += [f"rmsnorm+quantize M{M} K{K}" for M in (1, 8, 48) for K in (1536, 5120)]
@@ -400,8 +403,9 @@ def case_names():
 
 def extra_cases(dev, stream, floor_us, only=None, reps=None):
     """Latency of every other configuration: single GEMMs with MXFP8 inputs
-    (config 0, the wide tiles with outliers, rows above 48), the chain with
-    and without the norm, RMSNorm + MXFP8, WO-A + wo_b.  `only`: run the
+    (M 4 at N 1024, K 2048; the wide tiles with outliers; rows above 48; the
+    weight read row-major without a repack), the chain with and without the
+    norm, RMSNorm + MXFP8, WO-A + wo_b.  `only`: run the
     cases whose name contains it (profiling one case at a time)."""
     prof = profiled_cases()
     out = {}
@@ -409,17 +413,20 @@ def extra_cases(dev, stream, floor_us, only=None, reps=None):
     exact = only in case_names()
     want = lambda name: only is None or (name == only if exact else only in name)
     r = lambda default: reps or default
-    specs = [("single M4 N1024 K2048", 4, 1024, 2048, False)]
+    specs = [("single M4 N1024 K2048", 4, 1024, 2048, False, False)]
     for (N, K) in ((4096, 5120), (5120, 8192), (8192, 1536)):
-        specs += [(f"M{M} N{N} K{K}", M, N, K, True) for M in (16, 32, 48)]
-    specs += [(f"rows above 48: M{M} N4096 K5120", M, 4096, 5120, False) for M in (64, 128, 256)]
+        specs += [(f"M{M} N{N} K{K}", M, N, K, True, False) for M in (16, 32, 48)]
+    specs += [(f"rows above 48: M{M} N4096 K5120", M, 4096, 5120, False, False)
+              for M in (64, 128, 256)]
+    specs += [(f"row-major weights: M{M} N4096 K5120", M, 4096, 5120, False, True)
+              for M in (1, 8, 48)]
     by_weight = {}
     for spec in specs:
         if want(spec[0]):
-            by_weight.setdefault((spec[2], spec[3]), []).append(spec)
-    for (N, K), group in by_weight.items():
-        copies = weight_copies(N, K, dev)
-        for (name, M, _, _, outliers) in group:
+            by_weight.setdefault((spec[2], spec[3], spec[5]), []).append(spec)
+    for (N, K, row_major), group in by_weight.items():
+        copies = weight_copies(N, K, dev, row_major)
+        for (name, M, _, _, outliers, _) in group:
             u = gemm_case_timing(dev, stream, copies, M, N, K, outliers, r(400 if M <= 48 else 200))
             extra = {}
             if M > 48:

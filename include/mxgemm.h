@@ -16,10 +16,12 @@
  *                 operands, Float8E8M0FNU scales, sf_vec_size 32.)
  *   weights       a column-major K x N matrix on the [mxfp8] page
  *                 (launch_low_latency), i.e. N rows of K contiguous codes:
- *                 w_q [N, K], w_s [N, K/32] here.  The GEMM entry points take
- *                 the weight once repacked by mxfp8_pack_weights into the
- *                 order its kernels stream (see there), as a layer
- *                 preprocesses its weights once for its GEMM backend.
+ *                 w_q [N, K], w_s [N, K/32] here (MXG_WEIGHTS_ROW_MAJOR).
+ *                 The GEMMs read that layout as it is, or the same bytes
+ *                 once repacked by mxfp8_pack_weights into the order their
+ *                 kernels stream (MXG_WEIGHTS_PACKED, the default), as a
+ *                 layer preprocesses its weights once for its GEMM backend.
+ *                 On MI355X the packed layout streams 25-40 % faster.
  *   BF16          uint16_t bit patterns.  Outputs are BF16 [M, N] row-major,
  *                 each element the FP32-accumulated sum rounded to nearest even,
  *                 with no scale and no bias ([mxfp8] compile_low_latency).
@@ -34,7 +36,8 @@
  *     on any error nothing is launched and no output is written.
  *   - Device pointers must be 16-byte aligned, and row strides must keep every
  *     row 16-byte aligned ([mxfp8] launch_low_latency passes 16-byte aligned
- *     operand pointers).
+ *     operand pointers, and a 32-byte aligned weight scale pointer, which
+ *     meets this).
  *   - Row counts: 1 <= M <= MXG_MAX_ROWS for the chain and WO-A ([mxfp8]:
  *     the low-latency kernel covers up to 48 rows with 16-, 32- or 48-row
  *     activation tiles; more rows go to another kernel), and up to
@@ -113,6 +116,16 @@ int mxg_hbm_read_probe(const uint8_t *w_q, const uint8_t *w_s, int64_t N, int64_
  */
 int mxfp8_quantize(const uint16_t *x, int64_t M, int64_t K, int64_t ld_x,
                    uint8_t *q, uint8_t *s, void *stream);
+
+/*
+ * Layouts of an MXFP8 weight's bytes (mxg_weight.layout, mxfp8_gemm_ex).
+ * Both hold the same N*K code bytes and N*K/32 scale bytes, and give results
+ * equal bit for bit.  A 16-row x 128-K step of the row-major layout is 16
+ * rows of 128 bytes, so each of a wave's two 16-byte-per-lane code loads
+ * reads 64 bytes of 16 rows, where a packed step is 2 KiB in lane order.
+ */
+#define MXG_WEIGHTS_PACKED 0    /* mxfp8_pack_weights order (fastest)   */
+#define MXG_WEIGHTS_ROW_MAJOR 1 /* [N, K] codes, [N, K/32] scales       */
 
 /* Layouts of MXFP8 scale bytes written by mxfp8_rmsnorm_quantize. */
 #define MXG_SCALES_ROW_MAJOR 0 /* [M, K/32], row-major                          */
@@ -197,6 +210,7 @@ int mxfp8_pack_weights(const uint8_t *w_q, const uint8_t *w_s, int64_t N, int64_
  *   ld_x      row stride of x_bf16 in elements (ignored when x_bf16 is NULL)
  *   a_q, a_s  MXFP8 activations [M, K] / [M, K/32]
  *   w_q, w_s  MXFP8 weight [N, K] / [N, K/32], packed by mxfp8_pack_weights
+ *             (mxfp8_gemm_ex also reads it unpacked)
  *   out       BF16 [M, N]
  *   workspace, workspace_bytes
  *             caller-owned device scratch of at least mxg_gemm_workspace_bytes()
@@ -243,30 +257,45 @@ int mxfp8_gemm_noalloc(int64_t M, int64_t N, int64_t K, const uint16_t *x_bf16,
                        const uint8_t *w_s, uint16_t *out, void *stream);
 
 /*
- * mxfp8_gemm_ex -- mxfp8_gemm on MXFP8 activations whose scale bytes come in
- * the given layout ([mxfp8] module text: the low-latency and cute-dsl
- * backends read the same F8_128x4 activation scales), so a tensor written by
- * mxfp8_rmsnorm_quantize with MXG_SCALES_128X4, or by another producer of
- * that layout, needs no repack.
- *   a_s              MXG_SCALES_ROW_MAJOR: [M, K/32], exactly as mxfp8_gemm;
- *                    MXG_SCALES_128X4: mxg_scale_bytes_128x4(M, K) bytes in
- *                    128 x 4 tiles (offsets as in mxfp8_rmsnorm_quantize)
- *   other arguments  as mxfp8_gemm with x_bf16 = NULL (a_q is [M, K])
- * With MXG_SCALES_ROW_MAJOR this is mxfp8_gemm.  With MXG_SCALES_128X4 the
- * direct kernels always serve the call, and the result equals mxfp8_gemm's
- * on the same scales in row-major order, bit for bit.  Status as above.
+ * mxfp8_gemm_ex -- mxfp8_gemm with the layouts of the activation scales and
+ * of the weight given by the caller.
+ *   a_scale_layout   MXG_SCALES_ROW_MAJOR: a_s is [M, K/32], as in mxfp8_gemm;
+ *                    MXG_SCALES_128X4: a_s is mxg_scale_bytes_128x4(M, K)
+ *                    bytes in 128 x 4 tiles (offsets as in
+ *                    mxfp8_rmsnorm_quantize), MXFP8 input only (x_bf16 NULL).
+ *                    ([mxfp8] module text: the low-latency and cute-dsl
+ *                    backends read the same F8_128x4 activation scales, so a
+ *                    tensor from mxfp8_rmsnorm_quantize with MXG_SCALES_128X4,
+ *                    or another producer of that layout, needs no repack.)
+ *   w_layout         MXG_WEIGHTS_PACKED: w_q/w_s from mxfp8_pack_weights, as
+ *                    in mxfp8_gemm; MXG_WEIGHTS_ROW_MAJOR: w_q [N, K] and
+ *                    w_s [N, K/32] as the [mxfp8] page's launch_low_latency
+ *                    takes them (a column-major [K, N] weight), read without
+ *                    a repack.
+ *   other arguments  as mxfp8_gemm.
+ * The kernels, plans and summation order do not depend on either layout, so
+ * results equal mxfp8_gemm's on the same values bit for bit.  With
+ * MXG_SCALES_128X4 the direct kernels (up to 48 rows) or the 64-row blocks
+ * of the 2D kernel serve the call.  An unknown layout, or 128 x 4 scales with
+ * BF16 input, is MXG_ERR_SHAPE; other status as above.
  */
-int mxfp8_gemm_ex(int64_t M, int64_t N, int64_t K, const uint8_t *a_q, const uint8_t *a_s,
-                  int32_t a_scale_layout, const uint8_t *w_q, const uint8_t *w_s, uint16_t *out,
-                  void *workspace, size_t workspace_bytes, void *stream);
+int mxfp8_gemm_ex(int64_t M, int64_t N, int64_t K, const uint16_t *x_bf16, int64_t ld_x,
+                  uint8_t *a_q, uint8_t *a_s, int32_t a_scale_layout, const uint8_t *w_q,
+                  const uint8_t *w_s, int32_t w_layout, uint16_t *out, void *workspace,
+                  size_t workspace_bytes, void *stream);
 
 /*
- * A packed MXFP8 weight (mxfp8_pack_weights order) and its shape [N, K].
+ * An MXFP8 weight of shape [N, K] and the layout of its bytes:
+ *   MXG_WEIGHTS_PACKED     (0, the default of a zero-initialised field) q and
+ *                          s as mxfp8_pack_weights writes them;
+ *   MXG_WEIGHTS_ROW_MAJOR  q [N, K] codes, s [N, K/32] scale bytes, row-major.
+ * Any other layout value is rejected with MXG_ERR_SHAPE.
  */
 typedef struct {
-  const uint8_t *q; /* N*K packed codes   */
-  const uint8_t *s; /* N*K/32 packed scales */
+  const uint8_t *q; /* N*K codes      */
+  const uint8_t *s; /* N*K/32 scales  */
   int64_t N, K;
+  int32_t layout;   /* MXG_WEIGHTS_* */
 } mxg_weight;
 
 /*
@@ -358,11 +387,11 @@ size_t mxg_chain_workspace_bytes(const mxg_chain *chain);
  *   n_heads H, head_dim D, nope_dim, n_groups G
  *               H % G == 0, H/G <= 8, D and nope multiples of 32,
  *               0 < nope < D (rope = D - nope)
- *   wa          packed MXFP8 weight (mxfp8_pack_weights) with N = G*R rows,
+ *   wa          MXFP8 weight (either layout) with N = G*R rows,
  *               group g = rows [g*R, g*R + R), and K = hpg*D; R % 128 == 0
  *   z           optional out: BF16 [M, G*R] (NULL: kept in the workspace)
  *   z_q, z_s    out: MXFP8 of z, [M, G*R] codes, [M, G*R/32] scale bytes
- *   wb, out     optional wo_b: packed weight with K = G*R, N % 16 == 0, and
+ *   wb, out     optional wo_b: a weight with K = G*R, N % 16 == 0, and
  *               its BF16 output [M, wb.N]; wb.q == NULL skips step 5
  *   workspace, workspace_bytes
  *               at least mxg_wo_a_workspace_bytes() bytes, zero-filled once

@@ -26,7 +26,7 @@ _lib = None
 
 class MxgWeight(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("s", ctypes.c_void_p),
-                ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("layout", ctypes.c_int32)]
 
 
 class MxgChain(ctypes.Structure):
@@ -93,7 +93,8 @@ def lib() -> ctypes.CDLL:
         L.mxfp8_gemm.restype = ctypes.c_int
         L.mxfp8_gemm_noalloc.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp]
         L.mxfp8_gemm_noalloc.restype = ctypes.c_int
-        L.mxfp8_gemm_ex.argtypes = [i64, i64, i64, vp, vp, ctypes.c_int32, vp, vp, vp, vp, sz, vp]
+        L.mxfp8_gemm_ex.argtypes = [i64, i64, i64, vp, i64, vp, vp, ctypes.c_int32, vp, vp,
+                                    ctypes.c_int32, vp, vp, sz, vp]
         L.mxfp8_gemm_ex.restype = ctypes.c_int
         L.mxg_gemm_workspace_bytes.argtypes = [i64, i64, i64]
         L.mxg_gemm_workspace_bytes.restype = sz
@@ -190,6 +191,8 @@ def mxfp8_quantize(x: torch.Tensor, K: int | None = None, q: torch.Tensor | None
 
 SCALES_ROW_MAJOR = 0   # [M, K/32]
 SCALES_128X4 = 1       # 128 x 4 scale tiles (mxg_scale_bytes_128x4 bytes)
+WEIGHTS_PACKED = 0     # mxfp8_pack_weights order (MXG_WEIGHTS_PACKED)
+WEIGHTS_ROW_MAJOR = 1  # [N, K] codes, [N, K/32] scales (MXG_WEIGHTS_ROW_MAJOR)
 
 
 def scale_bytes_128x4(M: int, K: int) -> int:
@@ -255,6 +258,8 @@ def mxfp8_pack_weights(w_q: torch.Tensor, w_s: torch.Tensor, wp_q: torch.Tensor 
 class PackedWeight:
     """An MXFP8 weight in the GEMM's streaming order, with its shape."""
 
+    layout = WEIGHTS_PACKED
+
     def __init__(self, q: torch.Tensor, s: torch.Tensor, N: int, K: int):
         self.q, self.s, self.N, self.K = q, s, N, K
 
@@ -273,22 +278,60 @@ class PackedWeight:
         return PackedWeight(self.q.clone(), self.s.clone(), self.N, self.K)
 
 
-def mxfp8_gemm(a_q: torch.Tensor, a_s: torch.Tensor, w: PackedWeight,
+class RowMajorWeight:
+    """An MXFP8 weight as a layer holds it, [N, K] codes and [N, K/32] scale
+    bytes, which the GEMMs read without a repack (slower to stream than a
+    PackedWeight of the same values; results are equal bit for bit)."""
+
+    layout = WEIGHTS_ROW_MAJOR
+
+    def __init__(self, q: torch.Tensor, s: torch.Tensor):
+        N, K = q.shape
+        _expect(q, torch.uint8, "q", (N, K))
+        _expect(s, torch.uint8, "s", (N, K // 32))
+        self.q, self.s, self.N, self.K = q, s, N, K
+
+    @classmethod
+    def from_bf16(cls, w: torch.Tensor, stream=None) -> "RowMajorWeight":
+        """Quantize a BF16 [N, K] weight (same rule as the activations)."""
+        return cls(*mxfp8_quantize(w, stream=stream))
+
+    def clone(self) -> "RowMajorWeight":
+        return RowMajorWeight(self.q.clone(), self.s.clone())
+
+
+# Either weight class: every GEMM entry takes both.
+Weight = "PackedWeight | RowMajorWeight"
+
+
+def _expect_weight(w: Weight) -> None:
+    if w.layout == WEIGHTS_PACKED:
+        _expect(w.q, torch.uint8, "w.q", (w.N * w.K,))
+        _expect(w.s, torch.uint8, "w.s", (w.N * w.K // 32,))
+    else:
+        _expect(w.q, torch.uint8, "w.q", (w.N, w.K))
+        _expect(w.s, torch.uint8, "w.s", (w.N, w.K // 32))
+
+
+def mxfp8_gemm(a_q: torch.Tensor, a_s: torch.Tensor, w: Weight,
                out: torch.Tensor | None = None, x: torch.Tensor | None = None,
                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """out[M, N] (BF16) = dequant(a) . dequant(w)^T for a PackedWeight w.
+    """out[M, N] (BF16) = dequant(a) . dequant(w)^T for a PackedWeight or a
+    RowMajorWeight w (the latter through the C call mxfp8_gemm_ex).
 
     With ``x`` (BF16 [M, >=K]) the kernel quantizes x itself and writes its
     codes/scales into ``a_q``/``a_s`` (which must then be allocated by the
     caller); otherwise ``a_q``/``a_s`` are the MXFP8 inputs."""
+    if w.layout != WEIGHTS_PACKED:
+        return mxfp8_gemm_ex(a_q, a_s, w, SCALES_ROW_MAJOR, out=out, x=x, workspace=workspace,
+                             stream=stream)
     M, K = a_q.shape
     N = w.N
     if w.K != K:
         raise ValueError(f"weight K {w.K} != activation K {K}")
     _expect(a_q, torch.uint8, "a_q", (M, K))
     _expect(a_s, torch.uint8, "a_s", (M, K // 32))
-    _expect(w.q, torch.uint8, "w.q", (N * K,))
-    _expect(w.s, torch.uint8, "w.s", (N * K // 32,))
+    _expect_weight(w)
     if out is None:
         out = torch.empty(M, N, dtype=torch.bfloat16, device=a_q.device)
     _expect(out, torch.bfloat16, "out", (M, N))
@@ -311,15 +354,16 @@ def mxfp8_gemm_noalloc(a_q: torch.Tensor, a_s: torch.Tensor, w: PackedWeight,
                        stream=None) -> torch.Tensor:
     """mxfp8_gemm without a workspace: the library keeps the K-split state in
     its own per-GPU device scratch (calls on one GPU must not overlap).  With
-    ``out`` given, nothing is allocated on this path."""
+    ``out`` given, nothing is allocated on this path.  Packed weights only."""
     M, K = a_q.shape
     N = w.N
     if w.K != K:
         raise ValueError(f"weight K {w.K} != activation K {K}")
+    if w.layout != WEIGHTS_PACKED:
+        raise TypeError("mxfp8_gemm_noalloc takes a PackedWeight")
     _expect(a_q, torch.uint8, "a_q", (M, K))
     _expect(a_s, torch.uint8, "a_s", (M, K // 32))
-    _expect(w.q, torch.uint8, "w.q", (N * K,))
-    _expect(w.s, torch.uint8, "w.s", (N * K // 32,))
+    _expect_weight(w)
     if out is None:
         out = torch.empty(M, N, dtype=torch.bfloat16, device=a_q.device)
     _expect(out, torch.bfloat16, "out", (M, N))
@@ -333,12 +377,13 @@ def mxfp8_gemm_noalloc(a_q: torch.Tensor, a_s: torch.Tensor, w: PackedWeight,
     return out
 
 
-def mxfp8_gemm_ex(a_q: torch.Tensor, a_s: torch.Tensor, w: PackedWeight, a_scale_layout: int,
-                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                  stream=None) -> torch.Tensor:
-    """mxfp8_gemm on MXFP8 activations a_q [M, K] whose scales a_s are
-    row-major [M, K/32] (SCALES_ROW_MAJOR) or a flat buffer of
-    scale_bytes_128x4(M, K) bytes in 128 x 4 tiles (SCALES_128X4)."""
+def mxfp8_gemm_ex(a_q: torch.Tensor, a_s: torch.Tensor, w: Weight, a_scale_layout: int,
+                  out: torch.Tensor | None = None, x: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """mxfp8_gemm with the activation scales a_s row-major [M, K/32]
+    (SCALES_ROW_MAJOR) or a flat buffer of scale_bytes_128x4(M, K) bytes in
+    128 x 4 tiles (SCALES_128X4, MXFP8 input only), and the weight w a
+    PackedWeight or a RowMajorWeight.  ``x`` as in mxfp8_gemm."""
     M, K = a_q.shape
     N = w.N
     if w.K != K:
@@ -350,24 +395,32 @@ def mxfp8_gemm_ex(a_q: torch.Tensor, a_s: torch.Tensor, w: PackedWeight, a_scale
             raise ValueError("a_s holds fewer than scale_bytes_128x4(M, K) bytes")
     else:
         _expect(a_s, torch.uint8, "a_s", (M, K // 32))
+    _expect_weight(w)
     if out is None:
         out = torch.empty(M, N, dtype=torch.bfloat16, device=a_q.device)
     _expect(out, torch.bfloat16, "out", (M, N))
+    ld_x = 0
+    if x is not None:
+        if x.dim() != 2 or x.dtype != torch.bfloat16 or x.stride(1) != 1 or x.shape[0] != M:
+            raise TypeError("x must be a bfloat16 [M, >=K] tensor with unit stride along K")
+        ld_x = x.stride(0)
     ws_bytes = int(lib().mxg_gemm_workspace_bytes(M, N, K))
     if workspace is None:
         workspace = get_workspace(a_q.device, ws_bytes)
     wsz = workspace.numel() * workspace.element_size()
-    _check(lib().mxfp8_gemm_ex(M, N, K, _ptr(a_q), _ptr(a_s), int(a_scale_layout), _ptr(w.q),
-                               _ptr(w.s), _ptr(out), _ptr(workspace), wsz, _stream(stream)))
+    _check(lib().mxfp8_gemm_ex(M, N, K, _ptr(x), ld_x, _ptr(a_q), _ptr(a_s), int(a_scale_layout),
+                               _ptr(w.q), _ptr(w.s), int(w.layout), _ptr(out), _ptr(workspace),
+                               wsz, _stream(stream)))
     return out
 
 
-def _w(w: PackedWeight) -> MxgWeight:
-    return MxgWeight(w.q.data_ptr(), w.s.data_ptr(), w.N, w.K)
+def _w(w: Weight) -> MxgWeight:
+    _expect_weight(w)
+    return MxgWeight(w.q.data_ptr(), w.s.data_ptr(), w.N, w.K, w.layout)
 
 
-def mxfp8_proj_chain(a_q: torch.Tensor, a_s: torch.Tensor, wA: PackedWeight, wB: PackedWeight,
-                     c_q: torch.Tensor, c_s: torch.Tensor, wC: PackedWeight, outs=None,
+def mxfp8_proj_chain(a_q: torch.Tensor, a_s: torch.Tensor, wA: Weight, wB: Weight,
+                     c_q: torch.Tensor, c_s: torch.Tensor, wC: Weight, outs=None,
                      workspace: torch.Tensor | None = None, norm_weight: torch.Tensor | None = None,
                      norm_eps: float = 0.0, b_bf16: torch.Tensor | None = None, stream=None):
     """Three projections back to back: A on (a_q, a_s); the leading wB.K
@@ -424,15 +477,15 @@ def wo_a_rotary_codes(workspace: torch.Tensor, M: int, HD: int):
 
 
 def wo_a_fused_quantize(o: torch.Tensor, positions: torch.Tensor, cos_sin: torch.Tensor,
-                        wa: PackedWeight, *, n_groups: int, nope_dim: int,
-                        wb: PackedWeight | None = None, outs=None, keep_z: bool = True,
+                        wa: Weight, *, n_groups: int, nope_dim: int,
+                        wb: Weight | None = None, outs=None, keep_z: bool = True,
                         workspace: torch.Tensor | None = None, stream=None):
     """Grouped WO-A with rotary in front and MXFP8 of its output behind,
     optionally followed by wo_b.
 
     ``o``: BF16 [M, H, D] (any row and head strides, D contiguous);
     ``positions``: int64 [M]; ``cos_sin``: float32 [max_pos, D - nope_dim];
-    ``wa``: packed [G*R, (H/G)*D].  Returns (z or None, z_q, z_s, out or None)."""
+    ``wa``: [G*R, (H/G)*D], packed or row-major.  Returns (z or None, z_q, z_s, out or None)."""
     if o.dim() != 3 or o.dtype != torch.bfloat16 or not o.is_cuda or o.stride(2) != 1:
         raise ValueError("o must be a BF16 [M, H, D] device tensor with contiguous last dim")
     M, H, D = o.shape
@@ -455,7 +508,7 @@ def wo_a_fused_quantize(o: torch.Tensor, positions: torch.Tensor, cos_sin: torch
     p = MxgWoA(M, o.data_ptr(), o.stride(0), o.stride(1), positions.data_ptr(),
                cos_sin.data_ptr(), cos_sin.shape[0], H, D, nope_dim, n_groups, _w(wa),
                z.data_ptr() if z is not None else None, z_q.data_ptr(), z_s.data_ptr(),
-               _w(wb) if wb is not None else MxgWeight(None, None, 0, 0),
+               _w(wb) if wb is not None else MxgWeight(None, None, 0, 0, 0),
                out.data_ptr() if wb is not None else None, None, 0)
     need = int(lib().mxg_wo_a_workspace_bytes(ctypes.byref(p)))
     if workspace is None:

@@ -71,6 +71,7 @@ int chain_direct(const mxg_chain& c, hipStream_t stream) {
   const int M = (int)c.M;
   GemmArgs a{nullptr, 0, const_cast<uint8_t*>(c.a_q), const_cast<uint8_t*>(c.a_s), c.wA.q, c.wA.s,
              c.out_a, M, (int)c.wA.N, (int)c.wA.K};
+  a.w_rm = c.wA.layout == MXG_WEIGHTS_ROW_MAJOR;
   set_ksplit(a, c.workspace, mxg::kGemmPartOffset);
   // A writes the MXFP8 of its leading wB.K columns itself where its kernel
   // can (each 32-column block in one workgroup's epilogue); otherwise B
@@ -87,6 +88,7 @@ int chain_direct(const mxg_chain& c, hipStream_t stream) {
   if (e != hipSuccess) return MXG_ERR_DEVICE;
   GemmArgs b{a_quantized ? nullptr : c.out_a, c.wA.N, c.b_q, c.b_s, c.wB.q, c.wB.s, c.out_b, M,
              (int)c.wB.N, (int)c.wB.K};
+  b.w_rm = c.wB.layout == MXG_WEIGHTS_ROW_MAJOR;
   b.norm_w = c.norm_weight;
   b.norm_eps = c.norm_eps;
   b.norm_y = c.b_bf16;
@@ -94,6 +96,7 @@ int chain_direct(const mxg_chain& c, hipStream_t stream) {
   if ((e = mxg::launch_gemm(b, stream)) != hipSuccess) return MXG_ERR_DEVICE;
   GemmArgs cc{nullptr, 0, const_cast<uint8_t*>(c.c_q), const_cast<uint8_t*>(c.c_s), c.wC.q,
               c.wC.s, c.out_c, M, (int)c.wC.N, (int)c.wC.K};
+  cc.w_rm = c.wC.layout == MXG_WEIGHTS_ROW_MAJOR;
   set_ksplit(cc, c.workspace, mxg::kGemmPartOffset);
   return launched(mxg::launch_gemm(cc, stream));
 }
@@ -155,11 +158,13 @@ int wo_a_run(const mxg_wo_a& p, hipStream_t stream) {
   ga.lda = HD;
   ga.group_tiles = R / 16;
   ga.a_group = Kg;
+  ga.w_rm = p.wa.layout == MXG_WEIGHTS_ROW_MAJOR;
   set_ksplit(ga, p.workspace, l.end);
   if ((e = mxg::launch_gemm(ga, stream)) != hipSuccess) return MXG_ERR_DEVICE;
   // 4-5. MXFP8 of z, written by wo_b's GEMM when there is one.
   if (p.wb.q) {
     GemmArgs gb{z, GR, p.z_q, p.z_s, p.wb.q, p.wb.s, p.out, M, (int)p.wb.N, (int)p.wb.K};
+    gb.w_rm = p.wb.layout == MXG_WEIGHTS_ROW_MAJOR;
     set_ksplit(gb, p.workspace, l.end);
     return launched(mxg::launch_gemm(gb, stream));
   }
@@ -273,20 +278,19 @@ int mxfp8_gemm_noalloc(int64_t M, int64_t N, int64_t K, const uint16_t* x_bf16, 
   return launched(mxg::launch_gemm(a, (hipStream_t)stream));
 }
 
-int mxfp8_gemm_ex(int64_t M, int64_t N, int64_t K, const uint8_t* a_q, const uint8_t* a_s,
-                  int32_t a_scale_layout, const uint8_t* w_q, const uint8_t* w_s, uint16_t* out,
-                  void* workspace, size_t workspace_bytes, void* stream) {
-  if (a_scale_layout == MXG_SCALES_ROW_MAJOR)
-    return mxfp8_gemm(M, N, K, nullptr, 0, const_cast<uint8_t*>(a_q), const_cast<uint8_t*>(a_s),
-                      w_q, w_s, out, workspace, workspace_bytes, stream);
-  if (a_scale_layout != MXG_SCALES_128X4) return MXG_ERR_SHAPE;
-  int st = validate_gemm(M, N, K, nullptr, 0, a_q, a_s, w_q, w_s, out, workspace_bytes,
-                         workspace);
+int mxfp8_gemm_ex(int64_t M, int64_t N, int64_t K, const uint16_t* x_bf16, int64_t ld_x,
+                  uint8_t* a_q, uint8_t* a_s, int32_t a_scale_layout, const uint8_t* w_q,
+                  const uint8_t* w_s, int32_t w_layout, uint16_t* out, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  int st = check::gemm_layouts(a_scale_layout, w_layout, x_bf16);
   if (st != MXG_OK) return st;
+  if ((st = validate_gemm(M, N, K, x_bf16, ld_x, a_q, a_s, w_q, w_s, out, workspace_bytes,
+                          workspace)) != MXG_OK)
+    return st;
   if ((st = check_device()) != MXG_OK) return st;
-  GemmArgs a{nullptr, 0, const_cast<uint8_t*>(a_q), const_cast<uint8_t*>(a_s), w_q, w_s, out,
-             (int)M, (int)N, (int)K};
-  a.a_sf128 = true;
+  GemmArgs a{x_bf16, ld_x, a_q, a_s, w_q, w_s, out, (int)M, (int)N, (int)K};
+  a.a_sf128 = a_scale_layout == MXG_SCALES_128X4;
+  a.w_rm = w_layout == MXG_WEIGHTS_ROW_MAJOR;
   set_ksplit(a, workspace, mxg::kGemmPartOffset);
   return launched(mxg::launch_gemm(a, (hipStream_t)stream));
 }

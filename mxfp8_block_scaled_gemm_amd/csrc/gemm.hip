@@ -230,6 +230,7 @@ void gemm_m16_kernel(GemmArgs p) {
   const auto rws = make_rsrc(p.w_s + (int64_t)t * S * 64, (uint32_t)(S * 64));
   const auto rwh = make_rsrc(p.w_q + (int64_t)th * S * 2048, has_half ? (uint32_t)(S * 2048) : 0u);
   const auto rwsh = make_rsrc(p.w_s + (int64_t)th * S * 64, has_half ? (uint32_t)(S * 64) : 0u);
+  const WeightLane wl = weight_lane(p.w_rm, K, lane);
   v4i wlo[SPW], whi[SPW];
   uint32_t wsc[SPW];
 #pragma unroll
@@ -240,9 +241,10 @@ void gemm_m16_kernel(GemmArgs p) {
     const bool ok = jj < my && (full ? mine : mine_h);
     const auto rq = full ? rw : rwh;
     const auto rsc = full ? rws : rwsh;
-    wlo[j] = buf_ld16_nt(rq, ok ? (uint32_t)(s * 2048 + lane * 16) : kOutOfRange);
-    whi[j] = buf_ld16_nt(rq, ok ? (uint32_t)(s * 2048 + 1024 + lane * 16) : kOutOfRange);
-    wsc[j] = buf_ld8(rsc, ok ? (uint32_t)(s * 64 + lane) : kOutOfRange);
+    const uint32_t lo = s * wl.step_q + wl.lane_q;
+    wlo[j] = buf_ld16_nt(rq, ok ? lo : kOutOfRange);
+    whi[j] = buf_ld16_nt(rq, ok ? lo + wl.half_q : kOutOfRange);
+    wsc[j] = buf_ld8(rsc, ok ? s * wl.step_s + wl.lane_s : kOutOfRange);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -623,6 +625,7 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
   const auto rw = make_rsrc(p.w_q, (uint32_t)((p.N >> 4) * S * 2048));
   const auto rws = make_rsrc(p.w_s, (uint32_t)((p.N >> 4) * S * 64));
   constexpr int NW = WL ? SPW * T : SPW;                // weight slots per wave
+  const WeightLane wl = weight_lane(p.w_rm, K, lane);
   v4i wlo[NW], whi[NW];
   uint32_t wsc[NW];
 #pragma unroll
@@ -631,10 +634,12 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
     const int stp = WL ? wave + kM16Waves * (j / T) : wi + WPT * j;
     const int wt = WL ? tg * T + j % T : tile;
     const bool ok = stp < ns;
-    const uint32_t chunk = (uint32_t)(wt * S + k0 + stp);
-    wlo[j] = buf_ld16_nt(rw, ok ? chunk * 2048 + lane * 16 : kOutOfRange);
-    whi[j] = buf_ld16_nt(rw, ok ? chunk * 2048 + 1024 + lane * 16 : kOutOfRange);
-    wsc[j] = buf_ld8(rws, ok ? chunk * 64 + lane : kOutOfRange);
+    const uint32_t ks = (uint32_t)(k0 + stp);
+    const uint32_t lo = (uint32_t)wt * (uint32_t)(16 * K) + ks * wl.step_q + wl.lane_q;
+    wlo[j] = buf_ld16_nt(rw, ok ? lo : kOutOfRange);
+    whi[j] = buf_ld16_nt(rw, ok ? lo + wl.half_q : kOutOfRange);
+    wsc[j] = buf_ld8(rws, ok ? (uint32_t)wt * (uint32_t)(K / 2) + ks * wl.step_s + wl.lane_s
+                             : kOutOfRange);
   }
   __builtin_amdgcn_sched_barrier(0);
 

@@ -111,6 +111,7 @@ __global__ __launch_bounds__(WV * 64) void gemm_big_kernel(GemmArgs p) {
 
   // Weight steps of chunk c for this wave's tile, in register set W.
   constexpr int kHS = kCS / kHalves;                 // my steps per chunk
+  const WeightLane wl = weight_lane(p.w_rm, K, lane);
   v4i wlo[2][kHS], whi[2][kHS];
   uint32_t wsc[2][kHS];
   auto weight_load = [&](auto set_tag, int c) {
@@ -119,9 +120,10 @@ __global__ __launch_bounds__(WV * 64) void gemm_big_kernel(GemmArgs p) {
     for (int jj = 0; jj < kHS; ++jj) {
       const int s = kCS * c + kHalves * jj + kh;
       const bool ok = s < S;
-      wlo[W][jj] = buf_ld16_nt(rw, ok ? (uint32_t)(s * 2048 + lane * 16) : kOutOfRange);
-      whi[W][jj] = buf_ld16_nt(rw, ok ? (uint32_t)(s * 2048 + 1024 + lane * 16) : kOutOfRange);
-      wsc[W][jj] = buf_ld8(rws, ok ? (uint32_t)(s * 64 + lane) : kOutOfRange);
+      const uint32_t lo = s * wl.step_q + wl.lane_q;
+      wlo[W][jj] = buf_ld16_nt(rw, ok ? lo : kOutOfRange);
+      whi[W][jj] = buf_ld16_nt(rw, ok ? lo + wl.half_q : kOutOfRange);
+      wsc[W][jj] = buf_ld8(rws, ok ? s * wl.step_s + wl.lane_s : kOutOfRange);
     }
   };
 

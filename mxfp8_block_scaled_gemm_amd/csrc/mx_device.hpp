@@ -125,6 +125,26 @@ __device__ __forceinline__ v8i cat8(v4i lo, v4i hi) {
 __device__ __forceinline__ v4i ld16(const void* p) { return *reinterpret_cast<const v4i*>(p); }
 __device__ __forceinline__ void st16(void* p, v4i v) { *reinterpret_cast<v4i*>(p) = v; }
 
+// ------------------------------------------------------- weight layouts
+//
+// A 16-row weight tile t holds codes [16tK, 16(t+1)K) and scale bytes
+// [tK/2, (t+1)K/2) both in the row-major layout ([N, K] codes, [N, K/32]
+// scales) and in the packed one (pack.hip); only the order inside the tile
+// differs.  For the 128-wide K step s, lane l of a scaled 16x16x128 MFMA
+// (A row r = l % 16, K group g = l / 16) takes codes K[16g, 16g+16) ("lo")
+// and K[64+16g, 64+16g+16) ("hi") of row r, and the scale of row r over
+// block K[32g, 32g+32).  Inside the tile they sit at
+//   lo: s * step_q + lane_q,   hi: lo + half_q,   scale: s * step_s + lane_s.
+struct WeightLane {
+  uint32_t step_q, half_q, lane_q, step_s, lane_s;
+};
+__device__ __forceinline__ WeightLane weight_lane(bool row_major, int K, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  if (row_major)
+    return {128u, 64u, (uint32_t)(r * K + 16 * g), 4u, (uint32_t)(r * (K >> 5) + g)};
+  return {2048u, 1024u, (uint32_t)(16 * lane), 64u, (uint32_t)lane};
+}
+
 // ------------------------------------------------------- buffer loads
 //
 // Raw buffer loads with a byte range: an access at or beyond `bytes` returns

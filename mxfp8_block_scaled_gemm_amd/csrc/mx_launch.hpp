@@ -12,8 +12,8 @@ struct GemmArgs {
   int64_t ld_x;          // row stride of x (elements)
   uint8_t* a_q;          // MXFP8 activation codes [M, K]  (written when x != nullptr)
   uint8_t* a_s;          // activation scale bytes [M, K/32] (written when x != nullptr)
-  const uint8_t* w_q;    // packed weight codes (pack.hip order), N*K bytes
-  const uint8_t* w_s;    // packed weight scale bytes, N*K/32 bytes
+  const uint8_t* w_q;    // weight codes, N*K bytes (packed, or row-major with w_rm)
+  const uint8_t* w_s;    // weight scale bytes, N*K/32 bytes
   uint16_t* out;         // BF16 [M, N]
   int M, N, K;
   // MXFP8 activations read with row stride lda bytes (scales: lda / 32).
@@ -32,6 +32,8 @@ struct GemmArgs {
   // Activation scales in 128 x 4 tiles instead of row-major (MXFP8 input,
   // no grouping, lda == K).
   bool a_sf128 = false;
+  // Weights row-major ([N, K] codes, [N, K/32] scales) instead of packed.
+  bool w_rm = false;
   // M <= 16 kernel: workgroups per 16-row weight tile (1, 2 or 4; set by the
   // launcher).
   int rsplit = 1;

@@ -47,7 +47,7 @@ int gemm(int64_t M, int64_t N, int64_t K, const uint16_t* x, int64_t ld_x, const
 }
 
 bool weight(const mxg_weight& w) {
-  return w.N >= 16 && w.N % 16 == 0 && w.K >= 128 && w.K % 128 == 0 && w.N <= ((int64_t)1 << 24) &&
+  return (w.layout == MXG_WEIGHTS_PACKED || w.layout == MXG_WEIGHTS_ROW_MAJOR) && w.N >= 16 && w.N % 16 == 0 && w.K >= 128 && w.K % 128 == 0 && w.N <= ((int64_t)1 << 24) &&
          w.K <= MXG_MAX_K && w.N * w.K <= ((int64_t)1 << 31) - 1;
 }
 
@@ -99,6 +99,14 @@ int wo_a(const mxg_wo_a* p) {
   if (p->z && !aligned16(p->z)) return MXG_ERR_ALIGN;
   if (p->wb.q && (!aligned16(p->wb.q) || !aligned16(p->wb.s) || !aligned16(p->out)))
     return MXG_ERR_ALIGN;
+  return MXG_OK;
+}
+
+int gemm_layouts(int32_t a_scale_layout, int32_t w_layout, const uint16_t* x) {
+  if (a_scale_layout != MXG_SCALES_ROW_MAJOR && a_scale_layout != MXG_SCALES_128X4)
+    return MXG_ERR_SHAPE;
+  if (w_layout != MXG_WEIGHTS_PACKED && w_layout != MXG_WEIGHTS_ROW_MAJOR) return MXG_ERR_SHAPE;
+  if (x && a_scale_layout == MXG_SCALES_128X4) return MXG_ERR_SHAPE;
   return MXG_OK;
 }
 

@@ -23,7 +23,10 @@ int rmsnorm(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x, const uint16_
 bool gemm_shape(int64_t M, int64_t N, int64_t K);
 int gemm(int64_t M, int64_t N, int64_t K, const uint16_t* x, int64_t ld_x, const uint8_t* a_q,
          const uint8_t* a_s, const uint8_t* w_q, const uint8_t* w_s, const uint16_t* out);
+// Weight shape and layout of the chain's and WO-A's weights.
 bool weight(const mxg_weight& w);
+// mxfp8_gemm_ex's layouts: known values, and 128 x 4 scales only on MXFP8 input.
+int gemm_layouts(int32_t a_scale_layout, int32_t w_layout, const uint16_t* x);
 // Chain and WO-A structures, everything but the workspace.
 int chain(const mxg_chain* c);
 bool wo_a_shape(const mxg_wo_a& p);

@@ -155,6 +155,10 @@ def test_chain_rejects_before_launch(lib):
     bad = mx.MxgChain.from_buffer_copy(c)
     bad.wB = w(4, 8192, 4096)                 # requantized width beyond A's output
     assert lib.mxfp8_proj_chain(ctypes.byref(bad), None) == 3
+    for layout in (2, -1):                    # unknown weight layout
+        bad = mx.MxgChain.from_buffer_copy(c)
+        bad.wC.layout = layout
+        assert lib.mxfp8_proj_chain(ctypes.byref(bad), None) == 3
     bad = mx.MxgChain.from_buffer_copy(c)
     bad.a_q = A + 8
     assert lib.mxfp8_proj_chain(ctypes.byref(bad), None) == 2
@@ -233,6 +237,10 @@ def test_wo_a_rejects_weight_shapes(lib):
                    (w(4, 8192, 4096), w(9, 5120, 4096))):     # wb.K != G * R
         p = _wo_a(wa=wa, wb=wb)
         assert lib.wo_a_fused_quantize(ctypes.byref(p), None) == 3
+    for field in ("wa", "wb"):                                 # unknown weight layout
+        p = _wo_a()
+        getattr(p, field).layout = 2
+        assert lib.wo_a_fused_quantize(ctypes.byref(p), None) == 3
 
 
 def test_wo_a_workspace_size(lib):
@@ -271,17 +279,25 @@ def test_scale_bytes_128x4(lib):
     assert lib.mxg_scale_bytes_128x4(0, 1536) == 0
 
 
-def gemm_ex(lib, M=4, N=1024, K=2048, a_q=P(1), a_s=P(2), layout=1, w_q=P(3), w_s=P(4),
-            out=P(5), ws=P(7), ws_bytes=1 << 30):
-    return lib.mxfp8_gemm_ex(M, N, K, a_q, a_s, layout, w_q, w_s, out, ws, ws_bytes, None)
+def gemm_ex(lib, M=4, N=1024, K=2048, x=None, ld_x=0, a_q=P(1), a_s=P(2), layout=1, w_q=P(3),
+            w_s=P(4), w_layout=0, out=P(5), ws=P(7), ws_bytes=1 << 30):
+    return lib.mxfp8_gemm_ex(M, N, K, x, ld_x, a_q, a_s, layout, w_q, w_s, w_layout, out, ws,
+                             ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(a_s=None), 1), (dict(a_q=None), 1), (dict(layout=0, out=None), 1),
+    (dict(w_layout=1, w_s=None), 1),
     (dict(layout=2), 3), (dict(layout=-1), 3), (dict(M=0), 3), (dict(M=257), 3),
     (dict(K=1000), 3), (dict(layout=0, M=257), 3),
+    (dict(w_layout=2), 3), (dict(w_layout=-1), 3), (dict(layout=0, w_layout=2), 3),
+    # 128 x 4 scales take MXFP8 input only; BF16 input needs ld_x >= K
+    (dict(x=P(6), ld_x=2048), 3), (dict(layout=0, x=P(6), ld_x=1024), 3),
     (dict(a_q=ctypes.c_void_p(A + 8)), 2), (dict(a_s=ctypes.c_void_p(A + 4)), 2),
-    (dict(ws=None), 4),
+    (dict(w_layout=1, w_q=ctypes.c_void_p(A + 8)), 2),
+    (dict(layout=0, x=ctypes.c_void_p(A + 2), ld_x=2048), 2),
+    (dict(layout=0, x=P(6), ld_x=2052), 2),
+    (dict(ws=None), 4), (dict(w_layout=1, ws=None), 4),
 ])
 def test_gemm_ex_rejects(lib, kw, status):
     assert gemm_ex(lib, **kw) == status

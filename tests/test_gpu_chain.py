@@ -31,8 +31,10 @@ def chain_path(request, monkeypatch):
     return request.param
 
 
-def _prep(case):
-    """GPU and oracle quantization of every input (must agree bit for bit)."""
+def _prep(case, row_major=()):
+    """GPU and oracle quantization of every input (must agree bit for bit);
+    the weights named in row_major stay [N, K] / [N, K/32], the others are
+    packed."""
     g, o = {}, {}
     for name in ("x_a", "x_c", "w_a", "w_b", "w_c"):
         bits = synth.bits(case[name])
@@ -40,17 +42,20 @@ def _prep(case):
         q, s = mx.mxfp8_quantize(dev_bf16(bits))
         torch.cuda.synchronize()
         assert np.array_equal(host_u8(q), o[name][0]) and np.array_equal(host_u8(s), o[name][1]), name
-        g[name] = (q, s) if name.startswith("x") else mx.PackedWeight.from_rows(q, s)
+        if name.startswith("x"):
+            g[name] = (q, s)
+        else:
+            g[name] = mx.RowMajorWeight(q, s) if name in row_major else mx.PackedWeight.from_rows(q, s)
     return g, o
 
 
-def run_chain(M, dims=None, seed=0):
+def run_chain(M, dims=None, seed=0, row_major=()):
     case = synth.chain_case(M, seed=seed, dims=dims)
     d = case["dims"]
     b_cols = d["B"][1]
-    g, o = _prep(case)
+    g, o = _prep(case, row_major)
     ref = oracle.chain(*o["x_a"], o["w_a"], b_cols, o["w_b"], *o["x_c"], o["w_c"])
-    say(f"chain M={M} dims={d} seed={seed} path={os.environ.get('MXG_CHAIN_PATH')}")
+    say(f"chain M={M} dims={d} seed={seed} row_major={row_major}")
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
     out_a, b_q, b_s, out_b, out_c = mx.mxfp8_proj_chain(*g["x_a"], g["w_a"], g["w_b"], *g["x_c"],
                                                          g["w_c"], workspace=ws)
@@ -94,6 +99,18 @@ def test_chain_plans(M, plan, chain_path, monkeypatch):
 @pytest.mark.parametrize("M", [1, 8, 32])
 def test_chain_full_size(M, chain_path):
     run_chain(M)
+
+
+@pytest.mark.parametrize("row_major", [("w_a", "w_b", "w_c"), ("w_b",), ("w_a", "w_c")])
+@pytest.mark.parametrize("M,dims", [(1, None), (17, SMALL), (32, None), (48, SMALL)])
+def test_chain_row_major_weights(M, dims, row_major):
+    """Weights read as [N, K] / [N, K/32] (all, or some of them): within
+    tolerance of the oracle as run_chain checks, and bit for bit the outputs
+    of the same chain on packed weights."""
+    g, outs, _ = run_chain(M, dims=dims, seed=M + 3, row_major=row_major)
+    _, ref_outs, _ = run_chain(M, dims=dims, seed=M + 3)
+    for name, a, b in zip(("out_a", "b_q", "b_s", "out_b", "out_c"), outs, ref_outs):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
 
 
 @pytest.mark.parametrize("M", [8, 32])

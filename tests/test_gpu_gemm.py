@@ -51,16 +51,19 @@ def _weights(N, K, seed):
     return _wcache[key]
 
 
-def run_case(M, N, K, seed=0, outliers=False, fused=False):
+def run_case(M, N, K, seed=0, outliers=False, fused=False, row_major=False):
+    """One GEMM against the oracle; row_major: the weight as [N, K] codes and
+    [N, K/32] scales, read without a repack."""
     case = synth.gemm_case(M, N, K, seed=seed, outliers=outliers)
     x_bits = synth.bits(case["x"])
     w_bits = synth.bits(case["w"])
     ow_q, ow_s = oracle.quantize(w_bits)
     oa_q, oa_s = oracle.quantize(x_bits)
     ref = oracle.gemm(oa_q, oa_s, ow_q, ow_s)
-    say(f"gemm M={M} N={N} K={K} seed={seed} outliers={outliers} fused={fused}")
+    say(f"gemm M={M} N={N} K={K} seed={seed} outliers={outliers} fused={fused} "
+        f"row_major={row_major}")
     w_q, w_s = mx.mxfp8_quantize(dev_bf16(w_bits))
-    w = mx.PackedWeight.from_rows(w_q, w_s)
+    w = mx.RowMajorWeight(w_q, w_s) if row_major else mx.PackedWeight.from_rows(w_q, w_s)
     x = dev_bf16(x_bits)
     if fused:
         a_q = torch.full((M, K), 0x55, dtype=torch.uint8, device="cuda")
@@ -495,3 +498,63 @@ def test_big_tile_kernel(M, N, K, monkeypatch):
     # (8 waves each) and beyond (4 waves each).
     monkeypatch.delenv("MXG_DIRECT_KERNEL", raising=False)
     run_case(M, N, K, seed=M + K, outliers=True)
+
+
+# ------------------------------------------------------ row-major weights
+#
+# The weight as a layer holds it ([N, K] codes, [N, K/32] scales), read
+# without a repack: only the offsets of each lane's bytes change, so every
+# kernel form, plan and summation order is that of the packed weight and the
+# outputs must be equal bit for bit, besides lying within tolerance of the
+# oracle.
+
+def run_layouts(M, N, K, seed=0, fused=False, outliers=False, a_sf128=False):
+    case = synth.gemm_case(M, N, K, seed=seed, outliers=outliers)
+    x_bits, w_bits = synth.bits(case["x"]), synth.bits(case["w"])
+    ow_q, ow_s = oracle.quantize(w_bits)
+    oa_q, oa_s = oracle.quantize(x_bits)
+    ref = oracle.gemm(oa_q, oa_s, ow_q, ow_s)
+    say(f"gemm layouts M={M} N={N} K={K} seed={seed} fused={fused} outliers={outliers} "
+        f"a_sf128={a_sf128}")
+    w_q, w_s = dev_u8(ow_q), dev_u8(ow_s)
+    outs = []
+    for w in (mx.RowMajorWeight(w_q, w_s), mx.PackedWeight.from_rows(w_q, w_s)):
+        if fused:
+            a_q = torch.full((M, K), 0x55, dtype=torch.uint8, device="cuda")
+            a_s = torch.full((M, K // 32), 0x55, dtype=torch.uint8, device="cuda")
+            out = mx.mxfp8_gemm(a_q, a_s, w, x=dev_bf16(x_bits))
+        elif a_sf128:
+            a_q, a_s = dev_u8(oa_q), dev_u8(oracle.scales_to_128x4(oa_s))
+            out = mx.mxfp8_gemm_ex(a_q, a_s, w, mx.SCALES_128X4)
+        else:
+            a_q, a_s = dev_u8(oa_q), dev_u8(oa_s)
+            out = mx.mxfp8_gemm(a_q, a_s, w)
+        torch.cuda.synchronize()
+        if fused:
+            assert np.array_equal(host_u8(a_q), oa_q) and np.array_equal(host_u8(a_s), oa_s)
+        outs.append(out)
+    check_gemm(outs[0], ref, f"row-major M={M} N={N} K={K}")
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), "layouts differ"
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 8, 16, 17, 32, 33, 48])
+@pytest.mark.parametrize("fused", [False, True])
+def test_row_major_weights_rows_sweep(M, fused, path):
+    run_layouts(M, 256, 1024, seed=M + 100, fused=fused)
+
+
+@pytest.mark.parametrize("M,N,K,fused", [
+    (1, 4096, 5120, True), (4, 4096, 5120, True), (8, 4096, 5120, True),   # decode bucket
+    (16, 4096, 5120, False), (48, 4096, 5120, False), (32, 5120, 8192, False),
+    (48, 8192, 1536, False),                                                # wide tiles
+    (4, 5120, 8192, True), (3, 4112, 1024, False),                          # half tiles
+    (17, 512, 16384, True), (1, 16, 128, False),                            # edges of K and N
+    (64, 4096, 5120, False), (200, 4096, 5120, False), (256, 2048, 8192, True),  # rows above 48
+])
+def test_row_major_weights_shapes(M, N, K, fused):
+    run_layouts(M, N, K, seed=N + M, fused=fused, outliers=not fused)
+
+
+@pytest.mark.parametrize("M", [3, 20, 48, 100])
+def test_row_major_weights_with_128x4_scales(M):
+    run_layouts(M, 1024, 2048, seed=M + 5, a_sf128=True)

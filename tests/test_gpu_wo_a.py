@@ -109,6 +109,30 @@ def test_wo_a_full_size(M):
     run_wo_a(case, w, M)
 
 
+def _row_major(w):
+    """The same weights as [N, K] codes and [N, K/32] scales (no repack)."""
+    (wa_q, wa_s, (wb_q, wb_s)), _ = w
+    GR = wa_q.shape[0] * wa_q.shape[1]
+    wa = mx.RowMajorWeight(dev_u8(np.ascontiguousarray(wa_q.reshape(GR, -1))),
+                           dev_u8(np.ascontiguousarray(wa_s.reshape(GR, -1))))
+    return w[0], (wa, mx.RowMajorWeight(dev_u8(wb_q), dev_u8(wb_s)))
+
+
+@pytest.mark.parametrize("M,full", [(3, False), (17, False), (4, True)])
+def test_wo_a_row_major_weights(M, full):
+    """W_a and W_b read as [N, K] / [N, K/32]: within tolerance of the oracle
+    as run_wo_a checks, and bit for bit the outputs on packed weights."""
+    if full:
+        case, w = full_case()
+    else:
+        case = synth.wo_a_case(M, seed=M + 9, dims=SMALL)
+        w = _weights(case)
+    got, _ = run_wo_a(case, _row_major(w), M)
+    ref, _ = run_wo_a(case, w, M)
+    for name, a, b in zip(("z", "z_q", "z_s", "out"), got, ref):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), name
+
+
 def test_wo_a_without_wo_b_and_without_z():
     case = synth.wo_a_case(5, seed=7, dims=SMALL)
     run_wo_a(case, _weights(case), 5, with_wb=False, keep_z=False)
