@@ -37,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import mxfp8_block_scaled_gemm_amd as mx  # noqa: E402
+from mxfp8_block_scaled_gemm_amd import probe as mxprobe  # noqa: E402
 import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
@@ -243,7 +244,7 @@ def stream_ceiling(dev, stream, reps: int = 600):
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def call(i):
-        mx.hbm_read_probe(copies[i % len(copies)], sink)
+        mxprobe.hbm_read_probe(copies[i % len(copies)], sink)
     with torch.cuda.stream(stream):
         for i in range(20):
             call(i)
@@ -259,7 +260,7 @@ def launch_floor(dev, stream, reps: int = 600):
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def call(i):
-        mx.hbm_read_probe(w, sink)
+        mxprobe.hbm_read_probe(w, sink)
     with torch.cuda.stream(stream):
         for i in range(20):
             call(i)

@@ -79,22 +79,6 @@ const char *mxg_strerror(int status);
 int mxg_version(void);
 
 /*
- * mxg_hbm_read_probe -- a measurement aid, not a step of the method: reads a
- * weight packed by mxfp8_pack_weights (N rows, K columns) exactly as the
- * GEMMs' weight stream reads it (one workgroup of 16 waves per 16-row tile,
- * each wave issuing all of its 128-wide K steps at once) and computes
- * nothing.  Timing it against mxfp8_gemm on the same weight gives the
- * single-launch streaming ceiling the GEMM is measured against.
- *   w_q, w_s    packed weight codes (N*K bytes) and scales (N*K/32 bytes)
- *   N, K        N % 16 == 0, K % 128 == 0, K <= 8192
- *   sink        a device word the kernel writes only for one improbable
- *               folded value of the data (so no load can be optimized away)
- * Status as above; nothing is launched on an error.
- */
-int mxg_hbm_read_probe(const uint8_t *w_q, const uint8_t *w_s, int64_t N, int64_t K,
-                       uint32_t *sink, void *stream);
-
-/*
  * mxfp8_quantize -- BF16 -> MXFP8 ([mxfp8] pinned_mm and wide_mm quantize a
  * BF16 input with mxfp8_e4m3_quantize; [cute] AllReduceMHC's mxfp8_out
  * receives the layer input as MXFP8).

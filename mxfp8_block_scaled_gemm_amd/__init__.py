@@ -78,8 +78,6 @@ def lib() -> ctypes.CDLL:
         L.mxg_strerror.restype = ctypes.c_char_p
         L.mxg_version.argtypes = []
         L.mxg_version.restype = ctypes.c_int
-        L.mxg_hbm_read_probe.argtypes = [vp, vp, i64, i64, vp, vp]
-        L.mxg_hbm_read_probe.restype = ctypes.c_int
         L.mxfp8_quantize.argtypes = [vp, i64, i64, i64, vp, vp, vp]
         L.mxfp8_quantize.restype = ctypes.c_int
         L.mxfp8_rmsnorm_quantize.argtypes = [vp, i64, i64, i64, vp, ctypes.c_float, vp, i64,
@@ -160,15 +158,6 @@ def workspace_error(ws: torch.Tensor) -> int:
     """The error word of a workspace (non-zero: an in-kernel wait expired, or
     for wo_a_fused_quantize bit 1: a position outside the angle table)."""
     return int(ws[20:24].view(torch.int32).item())
-
-
-def hbm_read_probe(w: "PackedWeight", sink: torch.Tensor, stream=None) -> None:
-    """Measurement aid: read the packed weight w as the GEMMs' weight stream
-    does, computing nothing (mxg_hbm_read_probe)."""
-    if not sink.is_cuda or sink.dtype != torch.int32 or sink.numel() < 1:
-        raise ValueError("sink must be a device int32 tensor")
-    _check(lib().mxg_hbm_read_probe(w.q.data_ptr(), w.s.data_ptr(), w.N, w.K, sink.data_ptr(),
-                                     _stream(stream)))
 
 
 def mxfp8_quantize(x: torch.Tensor, K: int | None = None, q: torch.Tensor | None = None,

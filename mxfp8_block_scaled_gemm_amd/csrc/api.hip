@@ -235,15 +235,6 @@ int mxfp8_rmsnorm_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x
                                                scale_layout, (hipStream_t)stream));
 }
 
-int mxg_hbm_read_probe(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K,
-                       uint32_t* sink, void* stream) {
-  int st = check::hbm_probe(w_q, w_s, N, K, sink);
-  if (st != MXG_OK) return st;
-  if ((st = check_device()) != MXG_OK) return st;
-  return launched(
-      mxg::launch_hbm_read(w_q, w_s, (int)(N / 16), (int)(K / 128), sink, (hipStream_t)stream));
-}
-
 int mxfp8_pack_weights(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K,
                        uint8_t* wp_q, uint8_t* wp_s, void* stream) {
   int st = check::pack(w_q, w_s, N, K, wp_q, wp_s);

@@ -101,11 +101,6 @@ struct RopeQuantArgs {
 
 hipError_t launch_rope_quant(const RopeQuantArgs& a, hipStream_t stream);
 
-// Read-only HBM probe (probe.hip): reads a packed weight of `tiles` 16-row
-// tiles and `steps` 128-wide K steps as the GEMM weight stream does.
-hipError_t launch_hbm_read(const uint8_t* w_q, const uint8_t* w_s, int tiles, int steps,
-                           uint32_t* sink, hipStream_t stream);
-
 hipError_t launch_pack(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K,
                        uint8_t* wp_q, uint8_t* wp_s, hipStream_t stream);
 

@@ -121,15 +121,6 @@ int pack(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K, const uin
   return MXG_OK;
 }
 
-int hbm_probe(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K, const uint32_t* sink) {
-  if (!w_q || !w_s || !sink) return MXG_ERR_NULL;
-  if (N < 16 || N % 16 != 0 || N > ((int64_t)1 << 24) || K < 128 || K % 128 != 0 || K > 8192)
-    return MXG_ERR_SHAPE;
-  if (!aligned16(w_q) || !aligned16(w_s) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
-    return MXG_ERR_ALIGN;
-  return MXG_OK;
-}
-
 int workspace(const void* ws, size_t bytes, size_t need) {
   if (need > 0 && (!ws || bytes < need)) return MXG_ERR_WORKSPACE;
   if (ws && !aligned16(ws)) return MXG_ERR_ALIGN;

@@ -33,7 +33,6 @@ bool wo_a_shape(const mxg_wo_a& p);
 int wo_a(const mxg_wo_a* p);
 int pack(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K, const uint8_t* wp_q,
          const uint8_t* wp_s);
-int hbm_probe(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K, const uint32_t* sink);
 // A caller workspace of `bytes` bytes for a call that needs `need`.
 int workspace(const void* ws, size_t bytes, size_t need);
 

@@ -8,8 +8,15 @@
 // words are folded into one value that is stored only when it equals a
 // pattern no weight produces by accident, so no load can be dropped and
 // nothing is written.
+//
+// A measurement aid, built into its own library (libmxprobe.so) beside the
+// GEMM library and not part of its interface.
+#include <cstdlib>
+#include <cstring>
+
 #include "mx_device.hpp"
-#include "mx_launch.hpp"
+#include "mxgemm.h"
+#include "mxprobe.h"
 
 namespace mxg {
 
@@ -45,11 +52,28 @@ __global__ __launch_bounds__(kProbeWaves * 64) void hbm_read_kernel(const uint8_
   if (x == 0x9E3779B9u && acc[0] == 0x7F4A7C15) sink[0] = x;
 }
 
-hipError_t launch_hbm_read(const uint8_t* w_q, const uint8_t* w_s, int tiles, int steps,
-                           uint32_t* sink, hipStream_t stream) {
-  hipLaunchKernelGGL(hbm_read_kernel, dim3(tiles), dim3(kProbeWaves * 64), 0, stream, w_q, w_s,
-                     steps, sink);
-  return hipGetLastError();
-}
-
 }  // namespace mxg
+
+extern "C" int mxg_hbm_read_probe(const uint8_t* w_q, const uint8_t* w_s, int64_t N, int64_t K,
+                                  uint32_t* sink, void* stream) {
+  if (!w_q || !w_s || !sink) return MXG_ERR_NULL;
+  if (N < 16 || N % 16 != 0 || N > ((int64_t)1 << 24) || K < 128 || K % 128 != 0 ||
+      K > 128 * mxg::kProbeWaves * mxg::kProbeSlots)
+    return MXG_ERR_SHAPE;
+  const auto addr = [](const void* p) { return reinterpret_cast<uintptr_t>(p); };
+  if ((addr(w_q) & 15u) || (addr(w_s) & 15u) || (addr(sink) & 3u)) return MXG_ERR_ALIGN;
+  // gfx950 only (MXG_FORCE_ARCH stands in for the device's name in tests)
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MXG_ERR_DEVICE;
+  if (const char* forced = std::getenv("MXG_FORCE_ARCH")) {
+    if (std::strncmp(forced, "gfx950", 6) != 0) return MXG_ERR_DEVICE;
+  } else {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess ||
+        std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+      return MXG_ERR_DEVICE;
+  }
+  hipLaunchKernelGGL(mxg::hbm_read_kernel, dim3((unsigned)(N / 16)), dim3(mxg::kProbeWaves * 64),
+                     0, (hipStream_t)stream, w_q, w_s, (int)(K / 128), sink);
+  return hipGetLastError() == hipSuccess ? MXG_OK : MXG_ERR_DEVICE;
+}

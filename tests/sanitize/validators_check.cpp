@@ -103,10 +103,6 @@ int main() {
   EXPECT(c::pack(aq, as, 4100, 5120, P<uint8_t>(8), P<uint8_t>(9)), MXG_ERR_SHAPE);
   EXPECT(c::pack(aq, as, big, big, P<uint8_t>(8), P<uint8_t>(9)), MXG_ERR_SHAPE);
   EXPECT(c::pack(aq, as, 4096, 5120, Off<uint8_t>(8, 4), P<uint8_t>(9)), MXG_ERR_ALIGN);
-  EXPECT(c::hbm_probe(aq, as, 4096, 5120, P<uint32_t>(2)), MXG_OK);
-  EXPECT(c::hbm_probe(aq, as, 4096, 5120, nullptr), MXG_ERR_NULL);
-  EXPECT(c::hbm_probe(aq, as, 4096, 8192 + 128, P<uint32_t>(2)), MXG_ERR_SHAPE);
-  EXPECT(c::hbm_probe(aq, as, 4096, 5120, Off<uint32_t>(2, 2)), MXG_ERR_ALIGN);
 
   // mxfp8_proj_chain
   mxg_chain ch{};

@@ -22,6 +22,12 @@ def lib():
     return mx.lib()
 
 
+@pytest.fixture(scope="module")
+def probe_lib(lib):
+    from mxfp8_block_scaled_gemm_amd import probe
+    return probe.lib()
+
+
 def declared_functions():
     names = set()
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
@@ -120,18 +126,25 @@ def test_quantize_rejects(lib, args, status):
     ((ctypes.c_void_p(A + 8), P(1), 4096, 5120, P(2)), 2),
     ((P(0), P(1), 4096, 5120, ctypes.c_void_p(A + 2)), 2),
 ])
-def test_hbm_read_probe_rejects(lib, args, status):
-    assert lib.mxg_hbm_read_probe(*args, None) == status
+def test_hbm_read_probe_rejects(probe_lib, args, status):
+    assert probe_lib.mxg_hbm_read_probe(*args, None) == status
 
 
-def test_forced_foreign_arch_is_rejected_before_launch(lib, monkeypatch):
+def test_probe_lives_outside_the_gemm_library(lib, probe_lib):
+    # The read probe is a measurement aid: its own library exports it, the
+    # GEMM library does not.
+    assert hasattr(probe_lib, "mxg_hbm_read_probe")
+    assert not hasattr(lib, "mxg_hbm_read_probe")
+
+
+def test_forced_foreign_arch_is_rejected_before_launch(lib, probe_lib, monkeypatch):
     # A fully valid call on a device that reports another architecture must
     # return MXG_ERR_DEVICE without launching (the pointers are fake).
     monkeypatch.setenv("MXG_FORCE_ARCH", "gfx942")
     assert gemm(lib) == 5
     assert lib.mxfp8_quantize(P(0), 4, 64, 64, P(1), P(2), None) == 5
     assert lib.wo_a_fused_quantize(ctypes.byref(_wo_a()), None) == 5
-    assert lib.mxg_hbm_read_probe(P(0), P(1), 4096, 5120, P(2), None) == 5
+    assert probe_lib.mxg_hbm_read_probe(P(0), P(1), 4096, 5120, P(2), None) == 5
 
 
 def test_workspace_size_is_positive(lib):
