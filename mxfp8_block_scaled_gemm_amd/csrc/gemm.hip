@@ -1398,14 +1398,25 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream, bool* quantized
       if (e != hipSuccess) return e;
       a.x = nullptr;
     }
-    // The 64 x 64-tile kernel above 128 rows, or above 64 rows at K >= 8192,
-    // where it measured faster than the row blocks (or equal): 20.6 against
-    // 28.8 us at M = 256, N 4096, K 5120; 30.7 against 35.5 at M = 128, N
-    // 5120, K 8192.  At 65-128 rows and smaller K its grid covers half the
-    // CUs or less and the row blocks win (M = 128, N 4096, K 5120: 16.5
-    // against 20.4 us).  MXG_DIRECT_KERNEL=2d keeps the row blocks.
-    if (a.M > 64 && (a.M > 128 || a.K >= 8192) && gemm_big_fits(a) && forced_kernel() != 2)
-      return launch_gemm_big(a, device_cus(), stream);
+    // Above 64 rows (measured on MI355X, us, wide / 64 x 64 / row blocks):
+    //   * K >= 4096: the wide form (K split across the waves; 2 or 4 weight
+    //     tiles per workgroup, in one round where a count allows): N 4096,
+    //     K 5120, M = 96 / 256: 11.2 / 15.1 against 15.7 / 16.2 and 15.0 /
+    //     26.7; N 5120, K 8192, M = 128 / 256: 20.2 / 35.8 against 24.3 /
+    //     39.7; N 2048, K 16384, M = 128: 23.5 against 43.5 and 30.5;
+    //   * K < 4096: the 64 x 64 form, whose 4-step chunks suit short K
+    //     better than the wide form's 8 steps (N 8192, K 1536, M = 96 / 256:
+    //     7.4 / 10.3 against 8.2 / 14.7 and 8.5 / 15.5);
+    //   * else (a shape neither takes) the row blocks below.
+    // MXG_BIG_KERNEL=wide|64 forces a form where it takes the shape, and
+    // MXG_DIRECT_KERNEL=2d keeps the row blocks.
+    const char* bk = std::getenv("MXG_BIG_KERNEL");
+    const int bforce = !bk ? 0 : std::strcmp(bk, "wide") == 0 ? 1 : std::strcmp(bk, "64") == 0 ? 2 : 0;
+    if (a.M > 64 && forced_kernel() != 2) {
+      if (gemm_wide_fits(a) && (bforce == 1 || (bforce == 0 && a.K >= 4096)))
+        return launch_gemm_wide(a, device_cus(), stream);
+      if (gemm_big_fits(a) && bforce != 1) return launch_gemm_big(a, device_cus(), stream);
+    }
     const Plan pl = choose_plan(a.M, a.N, a.K, 0, device_cus());
     if (pl.T == 0) return hipErrorInvalidValue;
     a.P = pl.P;

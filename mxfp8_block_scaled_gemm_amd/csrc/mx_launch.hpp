@@ -80,6 +80,12 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream, bool* quantized_ou
 // N % 64 == 0, row-major activation scales.
 bool gemm_big_fits(const GemmArgs& a);
 hipError_t launch_gemm_big(const GemmArgs& a, int cus, hipStream_t stream);
+// The wide form of the same (K split across waves, NT tiles per workgroup):
+// whether it takes the shape, the tile count whose grid fits one round on
+// `cus` CUs (0: none), and the launch (nt 0: that count).
+bool gemm_wide_fits(const GemmArgs& a);
+int gemm_wide_tiles(const GemmArgs& a, int cus);
+hipError_t launch_gemm_wide(const GemmArgs& a, int cus, hipStream_t stream, int nt = 0);
 
 // RMSNorm + MXFP8 of BF16 rows (rmsnorm.hip); layout 1 = 128 x 4 scale tiles.
 hipError_t launch_rmsnorm_quantize(const uint16_t* x, int64_t M, int64_t K, int64_t ld_x,
