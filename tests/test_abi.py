@@ -25,6 +25,9 @@ def lib():
 @pytest.fixture(scope="module")
 def probe_lib(lib):
     from mxfp8_block_scaled_gemm_amd import probe
+    if not os.path.exists(probe.LIB_PATH):
+        from mxfp8_block_scaled_gemm_amd import _build
+        _build.build()
     return probe.lib()
 
 
