@@ -193,6 +193,17 @@ def decode_bucket(dev, steps: int, warmup: int, stream):
         per_m[str(M)] = {"us": round(u["ms"], 3), "us_min": round(u["min"], 3),
                          "us_max": round(u["max"], 3),
                          "GBs": round(gemm_bytes(M, N, K, True) / (u["ms"] * 1e-6) / 1e9, 1)}
+    # Warm cache: the same step on one weight copy, reused by every call, so
+    # the weights come from the 256 MB MALL rather than HBM (labelled as such,
+    # never the headline).
+    def warm_step(i):
+        for M in Ms:
+            x, aq, as_, out = bufs[M]
+            mx.mxfp8_gemm(aq, as_, copies[0], out=out, x=x)
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            warm_step(i)
+    tw = time_graph(warm_step, steps, stream)
     return {
         "ms_per_step": t["ms"] / steps,
         "ms_per_step_min": t["min"] / steps,
@@ -203,6 +214,8 @@ def decode_bucket(dev, steps: int, warmup: int, stream):
         "kernel_us": t["ms"] * 1e3 / (steps * len(Ms)),
         "per_m": per_m,
         "copies": len(copies),
+        "warm": {"ms_per_step": tw["ms"] / steps,
+                 "GBs": step_bytes * steps / (tw["ms"] * 1e-3) / 1e9},
     }
 
 
@@ -581,6 +594,10 @@ def main():
                            "roofline_vs_ceiling": round(roof["GBs"] / ceil["GBs"], 4)},
         "launch_floor_us": round(floor, 3),
         "step_avg_launch_us": round(rec["kernel_us"], 3),
+        "warm_cache": {"note": "the same step with one weight copy reused by every call: the "
+                               "weights are served from the 256 MB MALL, not HBM; not the headline",
+                       "ms_per_step": round(rec["warm"]["ms_per_step"], 5),
+                       "GBs": round(rec["warm"]["GBs"], 1)},
         "cases": cases,
         "cpu_baseline": cpu,
     }
