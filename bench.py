@@ -4,7 +4,7 @@ A step is one pass of the decode-bucket workload: for each batch size M in
 {1, 2, 4, 8}, BF16 activations x [M, 5120] are quantized to MXFP8 and
 multiplied by an MXFP8 weight [4096, 5120] (BF16 out), quantize and GEMM in
 one mxfp8_gemm launch.  Inputs are resident in HBM before the timed region.
-Weights rotate over enough identical copies (>= 512 MB) that no launch finds
+Weights rotate over enough identical copies (>= 1 GB) that no launch finds
 its weight in the 256 MB Infinity Cache.  The K timed steps are captured in
 one HIP graph (torch.cuda.CUDAGraph); the graph is replayed R >= 30 times,
 each replay (exactly K steps) bracketed by HIP events on the launch stream
@@ -42,7 +42,7 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MALL_BYTES = 256 << 20         # Infinity Cache
-ROTATE_BYTES = 512 << 20       # weight bytes cycled through before a copy is reused
+ROTATE_BYTES = 1 << 30         # weight bytes cycled through before a copy is reused (>= 1 GB)
 
 
 REPLAYS = 30                   # graph replays per timing; the median is reported
@@ -124,7 +124,7 @@ def weight_copies(N: int, K: int, dev, row_major: bool = False):
     [N, K] / [N, K/32] as quantized with row_major)."""
     q, s = mx.mxfp8_quantize(synth.gemm_case(1, N, K, seed=0)["w"].to(dev))
     w = mx.RowMajorWeight(q, s) if row_major else mx.PackedWeight.from_rows(q, s)
-    n = max(2, math.ceil(ROTATE_BYTES / mx_bytes(N, K)))
+    n = max(16, math.ceil(ROTATE_BYTES / mx_bytes(N, K)))
     return [w.clone() for _ in range(n)]
 
 
@@ -310,7 +310,7 @@ def chain_case(dev, stream, M: int, reps: int = 200, norm: bool = False):
     case = synth.chain_case(M, seed=0)
     w = {k: mx.PackedWeight.from_bf16(case[k].to(dev)) for k in ("w_a", "w_b", "w_c")}
     per = sum(mx_bytes(v.N, v.K) for v in w.values())
-    n = max(2, math.ceil(ROTATE_BYTES / per))
+    n = max(16, math.ceil(ROTATE_BYTES / per))
     cop = [{k: v.clone() for k, v in w.items()} for _ in range(n)]
     a = mx.mxfp8_quantize(case["x_a"].to(dev))
     c = mx.mxfp8_quantize(case["x_c"].to(dev))
@@ -364,7 +364,7 @@ def wo_a_case(dev, stream, M: int, reps: int = 200):
     wa = mx.PackedWeight.from_bf16(case["w_a"].reshape(G * R, -1).to(dev))
     wb = mx.PackedWeight.from_bf16(case["w_b"].to(dev))
     per = mx_bytes(wa.N, wa.K) + mx_bytes(wb.N, wb.K)
-    n = max(2, math.ceil(ROTATE_BYTES / per))
+    n = max(16, math.ceil(ROTATE_BYTES / per))
     cop = [(wa.clone(), wb.clone()) for _ in range(n)]
     o = case["o"].to(dev)
     pos = case["positions"].to(dev)
