@@ -148,17 +148,21 @@ def test_half_tile_plan(M, N, K, fused, monkeypatch):
 
 
 def _force(monkeypatch, kernel):
-    if kernel:
+    monkeypatch.delenv("MXG_DIRECT_KERNEL", raising=False)
+    monkeypatch.delenv("MXG_BIG_KERNEL", raising=False)
+    if kernel and kernel.startswith("big:"):
+        monkeypatch.setenv("MXG_BIG_KERNEL", kernel[4:])
+    elif kernel:
         monkeypatch.setenv("MXG_DIRECT_KERNEL", kernel)
-    else:
-        monkeypatch.delenv("MXG_DIRECT_KERNEL", raising=False)
 
 
-# Every kernel form: as routed, and the M <= 16 kernel, the 2D kernel and the
-# tile + half-tile form forced where they apply (N 5120 gives G < tiles <=
-# 1.5 G on 256 CUs); M = 130 runs the forms for more than 48 rows.
-KERNEL_FORMS = [None, "m16", "2d", "m16h"]
-BITWISE_SHAPES = [(9, 256, 1024), (9, 5120, 1024), (130, 256, 1024)]
+# Every kernel form: as routed, and the M <= 16 kernel, the 2D kernel, the
+# tile + half-tile form, and above 64 rows the wide and the 64 x 64 forms,
+# forced where they apply (N 5120 gives G < tiles <= 1.5 G on 256 CUs);
+# M = 130 runs the forms for more than 48 rows (routed: the 64 x 64 form at
+# K 1024, the wide form at K 4096).
+KERNEL_FORMS = [None, "m16", "2d", "m16h", "big:wide", "big:64"]
+BITWISE_SHAPES = [(9, 256, 1024), (9, 5120, 1024), (130, 256, 1024), (130, 256, 4096)]
 
 
 @pytest.mark.parametrize("kernel", KERNEL_FORMS)
@@ -183,7 +187,8 @@ def test_one_hot_weights_bitwise(M, N, K, kernel, monkeypatch):
 
 
 @pytest.mark.parametrize("kernel", KERNEL_FORMS)
-@pytest.mark.parametrize("M,N,K", [(6, 512, 2048), (6, 5120, 1024), (130, 512, 1024)])
+@pytest.mark.parametrize("M,N,K", [(6, 512, 2048), (6, 5120, 1024), (130, 512, 1024),
+                                   (130, 512, 4096)])
 def test_weight_scale_plus_one_doubles_output_bitwise(M, N, K, kernel, monkeypatch):
     """Raising every weight scale byte by one doubles every output exactly,
     whatever the kernel's summation order (the sums scale by a power of two)."""
@@ -196,6 +201,22 @@ def test_weight_scale_plus_one_doubles_output_bitwise(M, N, K, kernel, monkeypat
     out2 = mx.mxfp8_gemm(a_q, a_s, mx.PackedWeight.from_rows(w_q, w_s + 1))
     torch.cuda.synchronize()
     assert torch.equal(out2.float(), out1.float() * 2)
+
+
+@pytest.mark.parametrize("form", ["wide", "64"])
+def test_rows_above_64_deterministic(form, monkeypatch):
+    """Both forms above 64 rows sum in a fixed order (wave order through LDS,
+    no cross-workgroup sum): repeated calls give the same bits."""
+    monkeypatch.setenv("MXG_BIG_KERNEL", form)
+    M, N, K = 200, 4096, 5120
+    w, _ = _weights(N, K, 0)
+    a_q, a_s = mx.mxfp8_quantize(synth.gemm_case(M, 16, K, seed=4)["x"].cuda())
+    say(f"gemm repeats M={M} N={N} K={K} form={form}")
+    first = mx.mxfp8_gemm(a_q, a_s, w)
+    for _ in range(10):
+        again = mx.mxfp8_gemm(a_q, a_s, w)
+        torch.cuda.synchronize()
+        assert torch.equal(first.view(torch.int16), again.view(torch.int16))
 
 
 def test_zero_activations_give_positive_zero():
