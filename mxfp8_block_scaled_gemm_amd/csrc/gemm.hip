@@ -1398,20 +1398,28 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream, bool* quantized
       if (e != hipSuccess) return e;
       a.x = nullptr;
     }
-    // Above 64 rows (measured on MI355X, us, wide / 64 x 64 / row blocks):
-    //   * K >= 4096: the wide form (K split across the waves; 2 or 4 weight
+    // Above 48 rows (measured on MI355X, us, wide / 64 x 64 / row blocks):
+    //   * above 64 rows at K >= 4096: the wide form (K split across the waves; 2 or 4 weight
     //     tiles per workgroup, in one round where a count allows): N 4096,
     //     K 5120, M = 96 / 256: 11.2 / 15.1 against 15.7 / 16.2 and 15.0 /
     //     26.7; N 5120, K 8192, M = 128 / 256: 20.2 / 35.8 against 24.3 /
     //     39.7; N 2048, K 16384, M = 128: 23.5 against 43.5 and 30.5;
-    //   * K < 4096: the 64 x 64 form, whose 4-step chunks suit short K
+    //   * above 64 rows at K < 4096: the 64 x 64 form, whose 4-step chunks suit short K
     //     better than the wide form's 8 steps (N 8192, K 1536, M = 96 / 256:
     //     7.4 / 10.3 against 8.2 / 14.7 and 8.5 / 15.5);
+    //   * 49-64 rows: the wide form where two or more weight tiles per
+    //     workgroup fill one round (N 5120, K 8192, M = 56: 15.4 against
+    //     17.9; N 8192, K 1536, M = 64: 6.9 against 7.3), else the row
+    //     blocks, whose K split fills the CUs (N 2048, K 16384, M = 64: 14.7
+    //     against 24.1 in the wide form's 128 workgroups);
     //   * else (a shape neither takes) the row blocks below.
     // MXG_BIG_KERNEL=wide|64 forces a form where it takes the shape, and
     // MXG_DIRECT_KERNEL=2d keeps the row blocks.
     const char* bk = std::getenv("MXG_BIG_KERNEL");
     const int bforce = !bk ? 0 : std::strcmp(bk, "wide") == 0 ? 1 : std::strcmp(bk, "64") == 0 ? 2 : 0;
+    if (a.M <= 64 && forced_kernel() != 2 && gemm_wide_fits(a) &&
+        (bforce == 1 || (bforce == 0 && gemm_wide_tiles(a, device_cus()) >= 2)))
+      return launch_gemm_wide(a, device_cus(), stream);
     if (a.M > 64 && forced_kernel() != 2) {
       if (gemm_wide_fits(a) && (bforce == 1 || (bforce == 0 && a.K >= 4096)))
         return launch_gemm_wide(a, device_cus(), stream);

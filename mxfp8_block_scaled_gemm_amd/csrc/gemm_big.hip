@@ -402,7 +402,7 @@ bool gemm_big_fits(const GemmArgs& a) {
 }
 
 bool gemm_wide_fits(const GemmArgs& a) {
-  return a.M > kBigRows && a.N % 16 == 0 && a.x == nullptr && a.group_tiles == 0 &&
+  return a.M > 48 && a.N % 16 == 0 && a.x == nullptr && a.group_tiles == 0 &&
          (a.lda == 0 || a.lda == a.K) && !a.a_sf128;
 }
 

@@ -513,15 +513,17 @@ def test_weight_tile_row_split(M, N, K, fused, rsplit, monkeypatch):
 @pytest.mark.parametrize("M,N,K", [(129, 64, 128), (129, 512, 1024), (200, 1088, 2048),
                                    (256, 4096, 5120), (100, 5120, 8192), (250, 320, 16384),
                                    (193, 8192, 2048), (200, 5184, 1536), (129, 1040, 4096),
-                                   (160, 8192, 4096)])
+                                   (160, 8192, 4096), (56, 5120, 8192), (64, 8192, 1536),
+                                   (49, 1040, 2048)])
 def test_big_tile_kernel(M, N, K, form, monkeypatch):
-    # Above 64 rows, as routed and with each form forced: the 64 x 64 form
-    # (grids up to one workgroup per CU with 8 waves each, and beyond with 4)
-    # and the wide form (K split across 8 waves; 4, 2 or 1 weight tiles per
-    # workgroup, N = 1040 taking 1; one round of workgroups or, at N 8192 K
-    # 4096 M 160, two).  Ragged row blocks, a single K step (K = 128) and
-    # ragged last chunks, N not a multiple of 512 (no XCD grouping), the
-    # longest K.
+    # Above 48 rows, as routed and with each form forced: the 64 x 64 form
+    # above 64 rows (grids up to one workgroup per CU with 8 waves each, and
+    # beyond with 4) and the wide form (K split across 8 waves; 4, 2 or 1
+    # weight tiles per workgroup, N = 1040 taking 1; one round of workgroups
+    # or, at N 8192 K 4096 M 160, two; at 49-64 rows one row block, routed
+    # there with two tiles per workgroup).  Ragged row blocks, a single K
+    # step (K = 128) and ragged last chunks, N not a multiple of 512 (no XCD
+    # grouping), the longest K.
     monkeypatch.delenv("MXG_DIRECT_KERNEL", raising=False)
     if form:
         monkeypatch.setenv("MXG_BIG_KERNEL", form)
