@@ -125,14 +125,23 @@ __device__ __forceinline__ bool quad_bf16(float v, int t, uint2& o) {
 //
 // NRM (BF16 input, not HALF): the rows of x are RMS-normalised before the
 // quantize.  Every workgroup stages whole rows, so it computes each row's
-// factor 1 / sqrt(mean(x^2) + eps) itself: block sums of squares through LDS,
-// one wave per row adds them in block order, then y = BF16((x * r) * w) is
-// quantized as any BF16 input is.  It runs with 8 waves, built for two
-// workgroups per CU (at most 128 registers per lane): with 16 waves the norm
-// needs more than the 64 registers that two such workgroups per CU allow,
-// and with one workgroup per CU a weight of more tiles than CUs takes a
-// second round.
-template <int W, int SPW, int CH, bool FQ, bool HALF = false, bool NRM = false>
+// factor 1 / sqrt(mean(x^2) + eps) itself, then y = BF16((x * r) * w) is
+// quantized as any BF16 input is.  Two forms, with the same arithmetic in the
+// same order (bit-identical results):
+//   NRM = 1: blocks in thread order; block sums of squares through LDS, one
+//            wave per row adds them in block order, the gain parked in LDS;
+//            two workgroup barriers ahead of the quantize.
+//   NRM = 2: K <= 2048 (at most 64 blocks a row): wave w stages whole rows
+//            w, w + W, ..., lane l block l, and holds its blocks' gains in
+//            registers, so each wave finishes its rows' norm with no barrier
+//            (the barriers cannot pass before every wave has issued its weight
+//            loads, and the norm's work then stood between that point and the
+//            MFMAs).
+// It runs with 8 waves, built for two workgroups per CU (at most 128
+// registers per lane): with 16 waves the norm needs more than the 64
+// registers that two such workgroups per CU allow, and with one workgroup per
+// CU a weight of more tiles than CUs takes a second round.
+template <int W, int SPW, int CH, bool FQ, bool HALF = false, int NRM = 0>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(NRM ? W / 2 : 1)))
 void gemm_m16_kernel(GemmArgs p) {
   static_assert(!NRM || (FQ && !HALF), "the norm runs in the BF16 staging");
@@ -169,6 +178,10 @@ void gemm_m16_kernel(GemmArgs p) {
   uint32_t sc[SCR];
   const int nck = FQ ? (M * K) >> 5 : (M * K) >> 4;        // 32-blocks, or 16-byte chunks
   auto chunk = [&](int i) {                                // chunk id, or -1
+    if constexpr (NRM == 2) {                              // row wave + W i, block lane
+      const int row = wave + W * i;
+      return row < M && lane < KB ? row * KB + lane : -1;
+    }
     const int c = tid + i * kThreads;
     return c < nck ? c : -1;
   };
@@ -212,9 +225,17 @@ void gemm_m16_kernel(GemmArgs p) {
   // threads), staged through LDS so that it holds no registers across the
   // weight stream (two workgroups per CU need at most 64 per lane).
   v4i gst = {0, 0, 0, 0};
-  if constexpr (NRM)
+  if constexpr (NRM == 1)
     gst = buf_ld16(make_rsrc(p.norm_w, (uint32_t)(K * 2)),
                    tid < (K >> 3) ? (uint32_t)(tid * 16) : kOutOfRange);
+  // NRM = 2: the 32 gains of block `lane` (the same for every row).
+  v4i gw[NRM == 2 ? 4 : 1];
+  if constexpr (NRM == 2) {
+    const auto rg = make_rsrc(p.norm_w, (uint32_t)(K * 2));
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      gw[k] = buf_ld16(rg, lane < KB ? (uint32_t)(lane * 64 + 16 * k) : kOutOfRange);
+  }
 
   // Keep the staging loads ahead of the weight stream: the load counter
   // drains in issue order, so the staging data can then be waited for
@@ -272,54 +293,74 @@ void gemm_m16_kernel(GemmArgs p) {
   } else {
     const bool writer = blockIdx.x == 0;   // one workgroup writes the codes out
     if constexpr (NRM) {
-      // Block sums of squares (each product and sum rounded on its own), then
-      // one wave per row adds its blocks in block order: lane l takes blocks
-      // l, l + 64, ... in order, then a fixed butterfly across the lanes.
-      float* s_ss = reinterpret_cast<float*>(s_red);       // [M][KB], then r [M]
-      float* s_r = s_ss + M * KB;
+      // Block sums of squares (each product and sum rounded on its own); a
+      // row's blocks are then added in a fixed order: lane l takes blocks l,
+      // l + 64, ... in order, then wave_sum across the lanes.
+      auto block_ss = [&](int i) {
+        float ss = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const uint32_t u = (uint32_t)st[4 * i + k][h];
+            const float a = bf16_lo(u), b = bf16_hi(u);
+            ss = ss + a * a;
+            ss = ss + b * b;
+          }
+        return ss;
+      };
+      float rr[CH];                                        // each chunk's row factor
       uint8_t* s_gain = reinterpret_cast<uint8_t*>(s_red) + W * 64 * sizeof(v4f);  // [K] BF16
-      if (tid < (K >> 3)) *reinterpret_cast<v4i*>(s_gain + tid * 16) = gst;
+      if constexpr (NRM == 1) {
+        float* s_ss = reinterpret_cast<float*>(s_red);     // [M][KB], then r [M]
+        float* s_r = s_ss + M * KB;
+        if (tid < (K >> 3)) *reinterpret_cast<v4i*>(s_gain + tid * 16) = gst;
 #pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        const int c = chunk(i);
-        if (c >= 0) {
-          float ss = 0.f;
+        for (int i = 0; i < CH; ++i) {
+          const int c = chunk(i);
+          if (c >= 0) s_ss[c] = block_ss(i);               // c = row * KB + block
+        }
+        __syncthreads();
+        for (int row = wave; row < M; row += W) {          // W waves, up to 16 rows
+          float t = 0.f;
+          for (int b = lane; b < KB; b += 64) t = t + s_ss[row * KB + b];
+          t = wave_sum(t);
+          if (lane == 0) s_r[row] = 1.0f / __builtin_sqrtf(t / (float)K + p.norm_eps);
+        }
+        __syncthreads();
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
+        for (int i = 0; i < CH; ++i) {
+          const int c = chunk(i);
+          rr[i] = s_r[c >= 0 ? c / KB : 0];
+        }
+      } else {
+        // One block per lane: the lane's sum is its only term (0 + ss = ss).
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              const uint32_t u = (uint32_t)st[4 * i + k][h];
-              const float a = bf16_lo(u), b = bf16_hi(u);
-              ss = ss + a * a;
-              ss = ss + b * b;
-            }
-          s_ss[c] = ss;                                    // c = row * KB + block
+        for (int i = 0; i < CH; ++i) {
+          rr[i] = 0.f;
+          if (wave + W * i < M) {                          // wave-uniform
+            const float t = wave_sum(chunk(i) >= 0 ? block_ss(i) : 0.f);
+            rr[i] = 1.0f / __builtin_sqrtf(t / (float)K + p.norm_eps);
+          }
         }
       }
-      __syncthreads();
-      for (int row = wave; row < M; row += W) {               // W waves, up to 16 rows
-        float t = 0.f;
-        for (int b = lane; b < KB; b += 64) t = t + s_ss[row * KB + b];
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) t = t + __shfl_xor(t, o);
-        if (lane == 0) s_r[row] = 1.0f / __builtin_sqrtf(t / (float)K + p.norm_eps);
-      }
-      __syncthreads();
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
         const int c = chunk(i);
         if (c >= 0) {
-          const float r = s_r[c / KB];
+          const float r = rr[i];
           const uint8_t* gb = s_gain + (c - (c / KB) * KB) * 64;   // the block's 32 gains
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            const v4i gk = *reinterpret_cast<const v4i*>(gb + 16 * k);
+            v4i gk;
+            if constexpr (NRM == 2) gk = gw[k];
+            else gk = *reinterpret_cast<const v4i*>(gb + 16 * k);
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
               const uint32_t xu = (uint32_t)st[4 * i + k][h], wu = (uint32_t)gk[h];
               const float lo = (bf16_lo(xu) * r) * bf16_lo(wu);
               const float hi = (bf16_hi(xu) * r) * bf16_hi(wu);
-              st[4 * i + k][h] = (int)(f32_to_bf16(lo) | (f32_to_bf16(hi) << 16));
+              st[4 * i + k][h] = (int)pk_bf16(lo, hi);
             }
           }
           if (writer && p.norm_y) {
@@ -536,8 +577,17 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
   };
 
   // BF16 input: the chunk's 32-element blocks (64 per row), FQB whole blocks
-  // per thread (block tid + f * threads), quantized while parked; the first
-  // tile group's workgroups also write the codes out.
+  // per thread, quantized while parked; the first tile group's workgroups
+  // also write the codes out.  Thread block f: block tid + f * threads; with
+  // the norm (one chunk of at most 64 blocks a row), row wave + 16 f, block
+  // lane, so that each wave holds whole rows.  nblk: none.
+  auto blk_of = [&](int f, int bpr, int nblk) {
+    if constexpr (NRM) {
+      const int row = wave + kM16Waves * f;
+      return row < M && lane < bpr ? row * bpr + lane : nblk;
+    }
+    return tid + f * kT;
+  };
   auto load_bf16 = [&](int c, v4i (&st)[CHL]) {
     const int nsc_steps = min(16, ns - 16 * c);
     const int col0 = (k0 + 16 * c) * 128;
@@ -545,7 +595,7 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
     const int bpr = nsc_steps * 4, nblk = M * bpr;
 #pragma unroll
     for (int f = 0; f < FQB; ++f) {
-      const int blk = tid + f * kT;
+      const int blk = blk_of(f, bpr, nblk);
       const int row = blk / bpr, cb = blk - row * bpr;
       const uint32_t off = (uint32_t)(row * p.ld_x + col0 + cb * 32) * 2u;
 #pragma unroll
@@ -560,7 +610,7 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
     const int col0 = (k0 + 16 * c) * 128;
 #pragma unroll
     for (int f = 0; f < FQB; ++f) {
-      const int blk = tid + f * kT;
+      const int blk = blk_of(f, bpr, nblk);
       if (blk < nblk) {
         const int row = blk / bpr, cb = blk - row * bpr;
         v4i c0, c1;
@@ -615,10 +665,14 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
       }
     }
   }
-  v4i gst = {0, 0, 0, 0};
-  if constexpr (NRM)
-    gst = buf_ld16(make_rsrc(p.norm_w, (uint32_t)(K * 2)),
-                   tid < (K >> 3) ? (uint32_t)(tid * 16) : kOutOfRange);
+  // The norm's gain: the 32 values of block `lane` (the same for every row).
+  v4i gw[NRM ? 4 : 1];
+  if constexpr (NRM) {
+    const auto rg = make_rsrc(p.norm_w, (uint32_t)(K * 2));
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      gw[k] = buf_ld16(rg, lane < (K >> 5) ? (uint32_t)(lane * 64 + 16 * k) : kOutOfRange);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // 2. The weight stream: slot j = step wi + WPT j of my tile.
@@ -710,64 +764,48 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
   for (int c = 0; c < NCH; ++c) {
     if (c < nch) {                                      // uniform
       if constexpr (NRM) {
-        // RMSNorm of the staged rows (the part is all of K, one chunk): as in
-        // the M <= 16 kernel, block sums of squares (each product and sum
-        // rounded on its own) to LDS, then a wave per row adds its blocks in
-        // block order (lane l: block l, then a fixed butterfly), then
-        // y = BF16((x * r) * w) replaces the staged values.
+        // RMSNorm of the staged rows (the part is all of K, one chunk, at
+        // most 64 blocks a row): as in the M <= 16 kernel, block sums of
+        // squares (each product and sum rounded on its own), added across
+        // the wave's lanes (lane l: block l) by wave_sum, then
+        // y = BF16((x * r) * w) replaces the staged values.  Each wave holds
+        // whole rows: no barrier.
         const int KB = K >> 5;
-        float* s_ss = reinterpret_cast<float*>(smem + ((M * kLdA + M * kLdS + 15) & ~15));
-        float* s_r = s_ss + M * KB;
-        uint8_t* s_gain = reinterpret_cast<uint8_t*>(s_r + ((M + 3) & ~3));
-        if (tid < (K >> 3)) *reinterpret_cast<v4i*>(s_gain + tid * 16) = gst;
 #pragma unroll
         for (int f = 0; f < FQB; ++f) {
-          const int blk = tid + f * kT;                 // row blk / KB, block blk % KB
-          if (blk < M * KB) {
-            float ss = 0.f;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-#pragma unroll
-              for (int h = 0; h < 4; ++h) {
-                const uint32_t u = (uint32_t)st[0][4 * f + k][h];
-                const float a = bf16_lo(u), b = bf16_hi(u);
-                ss = ss + a * a;
-                ss = ss + b * b;
-              }
-            s_ss[blk] = ss;
-          }
-        }
-        __syncthreads();
-        for (int row = wave; row < M; row += kM16Waves) {
-          float t = 0.f;
-          for (int b = lane; b < KB; b += 64) t = t + s_ss[row * KB + b];
-#pragma unroll
-          for (int o = 32; o >= 1; o >>= 1) t = t + __shfl_xor(t, o);
-          if (lane == 0) s_r[row] = 1.0f / __builtin_sqrtf(t / (float)K + p.norm_eps);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int f = 0; f < FQB; ++f) {
-          const int blk = tid + f * kT;
-          if (blk < M * KB) {
-            const int row = blk / KB, cb = blk - row * KB;
-            const float rr = s_r[row];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const v4i gk = *reinterpret_cast<const v4i*>(s_gain + cb * 64 + 16 * k);
-#pragma unroll
-              for (int h = 0; h < 4; ++h) {
-                const uint32_t xu = (uint32_t)st[0][4 * f + k][h], wu = (uint32_t)gk[h];
-                const float lo = (bf16_lo(xu) * rr) * bf16_lo(wu);
-                const float hi = (bf16_hi(xu) * rr) * bf16_hi(wu);
-                st[0][4 * f + k][h] = (int)(f32_to_bf16(lo) | (f32_to_bf16(hi) << 16));
-              }
-            }
-            if (tg == 0 && p.norm_y) {
+          const int row = wave + kM16Waves * f;
+          if (row < M) {                                // wave-uniform
+            const bool mine = lane < KB;
+            float t = 0.f;
+            if (mine) {
 #pragma unroll
               for (int k = 0; k < 4; ++k)
-                *reinterpret_cast<v4i*>(p.norm_y + (int64_t)row * K + cb * 32 + 8 * k) =
-                    st[0][4 * f + k];
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                  const uint32_t u = (uint32_t)st[0][4 * f + k][h];
+                  const float x0 = bf16_lo(u), x1 = bf16_hi(u);
+                  t = t + x0 * x0;
+                  t = t + x1 * x1;
+                }
+            }
+            t = wave_sum(t);
+            const float rr = 1.0f / __builtin_sqrtf(t / (float)K + p.norm_eps);
+            if (mine) {
+#pragma unroll
+              for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                  const uint32_t xu = (uint32_t)st[0][4 * f + k][h], wu = (uint32_t)gw[k][h];
+                  const float lo = (bf16_lo(xu) * rr) * bf16_lo(wu);
+                  const float hi = (bf16_hi(xu) * rr) * bf16_hi(wu);
+                  st[0][4 * f + k][h] = (int)pk_bf16(lo, hi);
+                }
+              if (tg == 0 && p.norm_y) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                  *reinterpret_cast<v4i*>(p.norm_y + (int64_t)row * K + lane * 32 + 8 * k) =
+                      st[0][4 * f + k];
+              }
             }
           }
         }
@@ -867,8 +905,8 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
   if (P == 1) {
     if (red && m < M) {
       uint2 o;
-      o.x = f32_to_bf16(sum[0]) | (f32_to_bf16(sum[1]) << 16);
-      o.y = f32_to_bf16(sum[2]) | (f32_to_bf16(sum[3]) << 16);
+      o.x = pk_bf16(sum[0], sum[1]);
+      o.y = pk_bf16(sum[2], sum[3]);
       *reinterpret_cast<uint2*>(p.out + (int64_t)m * p.N + n) = o;
       if (qz) q_put(m, n, o);
     }
@@ -900,8 +938,8 @@ __global__ __launch_bounds__(kM16Waves * 64) void gemm_2d_kernel(GemmArgs p0) {
                                          0, 16));
     if (m < M) {
       uint2 o;
-      o.x = f32_to_bf16(tot[0]) | (f32_to_bf16(tot[1]) << 16);
-      o.y = f32_to_bf16(tot[2]) | (f32_to_bf16(tot[3]) << 16);
+      o.x = pk_bf16(tot[0], tot[1]);
+      o.y = pk_bf16(tot[2], tot[3]);
       *reinterpret_cast<uint2*>(p.out + (int64_t)m * p.N + n) = o;
       if (qz) q_put(m, n, o);
     }
@@ -923,12 +961,12 @@ size_t gemm_m16_half_lds_bytes(int M, int K, int W) {
   return act > red ? act : red;
 }
 
-template <int W, int SPW, int CH, bool FQ, bool HALF = false, bool NRM = false>
+template <int W, int SPW, int CH, bool FQ, bool HALF = false, int NRM = 0>
 static hipError_t launch_m16(const GemmArgs& a, int grid, hipStream_t stream) {
   auto kern = gemm_m16_kernel<W, SPW, CH, FQ, HALF, NRM>;
-  const size_t lds = HALF  ? gemm_m16_half_lds_bytes(a.M, a.K, W)
-                     : NRM ? gemm_m16_lds_bytes(a.M, a.K, W) + (size_t)a.K * 2
-                           : gemm_m16_lds_bytes(a.M, a.K, W);
+  const size_t lds = HALF       ? gemm_m16_half_lds_bytes(a.M, a.K, W)
+                     : NRM == 1 ? gemm_m16_lds_bytes(a.M, a.K, W) + (size_t)a.K * 2
+                                : gemm_m16_lds_bytes(a.M, a.K, W);
   static bool configured = false;   // raise the dynamic-LDS limit once per instance
   if (!configured) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -987,20 +1025,26 @@ static hipError_t launch_m16_half(const GemmArgs& a, int G, int sf, int ch, hipS
 
 // The normalising BF16 staging: 8 waves, one workgroup per weight tile
 // (rsplit as chosen), up to two 32-blocks per thread, up to 4 weight steps
-// per wave (K <= 4096).
+// per wave (K <= 4096).  K <= 2048 and M <= 16 take the per-wave form (a
+// wave's rows in one or two staging chunks, at most 2 weight steps a wave).
 constexpr int kNormWaves = 8;
 
-template <int SPW>
+template <int SPW, int NRM>
 static hipError_t launch_m16_norm_ch(const GemmArgs& a, int ch, hipStream_t stream) {
   const int grid = a.N / 16 * a.rsplit;
-  if (ch <= 1) return launch_m16<kNormWaves, SPW, 1, true, false, true>(a, grid, stream);
-  if (ch <= 2) return launch_m16<kNormWaves, SPW, 2, true, false, true>(a, grid, stream);
+  if (ch <= 1) return launch_m16<kNormWaves, SPW, 1, true, false, NRM>(a, grid, stream);
+  if (ch <= 2) return launch_m16<kNormWaves, SPW, 2, true, false, NRM>(a, grid, stream);
   return hipErrorInvalidValue;
 }
 
-static hipError_t launch_m16_norm(const GemmArgs& a, int spw, int ch, hipStream_t stream) {
-  if (spw <= 2) return launch_m16_norm_ch<2>(a, ch, stream);
-  if (spw <= 4) return launch_m16_norm_ch<4>(a, ch, stream);   // more would spill
+bool m16_norm_per_wave(int M, int K) { return K <= 2048 && M <= 2 * kNormWaves; }
+
+static hipError_t launch_m16_norm(const GemmArgs& a, int spw, int ch, bool shared,
+                                  hipStream_t stream) {
+  if (m16_norm_per_wave(a.M, a.K) && !shared)
+    return launch_m16_norm_ch<2, 2>(a, (a.M + kNormWaves - 1) / kNormWaves, stream);
+  if (spw <= 2) return launch_m16_norm_ch<2, 1>(a, ch, stream);
+  if (spw <= 4) return launch_m16_norm_ch<4, 1>(a, ch, stream);   // more would spill
   return hipErrorInvalidValue;
 }
 
@@ -1235,18 +1279,11 @@ hipError_t launch_2d_t(const GemmArgs& a, int T, int spw, hipStream_t stream) {
 
 // The RMSNorm in the 2D kernel's BF16 staging: two weight tiles per
 // workgroup, no K split, the part one staging chunk (K <= 2048), at most 32
-// rows.  LDS: the chunk's codes and scales, then the norm's block sums [M][K/32],
-// row factors [M] and gain [K].
-size_t gemm_2d_norm_lds_bytes(int M, int K) {
-  const size_t chunk = ((size_t)M * (16 * 128 + 16) + (size_t)M * (16 * 4 + 4) + 15) & ~(size_t)15;
-  return chunk + (size_t)M * (K / 32) * 4 + (size_t)((M + 3) & ~3) * 4 + (size_t)K * 2;
-}
-
+// rows (a wave's rows in registers: no LDS beyond the chunk's).
 bool gemm_2d_norm_fits(const GemmArgs& a) {
   return a.x && a.norm_w && a.M <= 32 && a.K <= 2048 && (a.N / 16) % 2 == 0 && a.group_tiles == 0 &&
          (a.lda == 0 || a.lda == a.K) &&
-         std::max(gemm_2d_lds_bytes(a.M, (a.M + 15) / 16), gemm_2d_norm_lds_bytes(a.M, a.K)) <=
-             160 * 1024 - 64;
+         gemm_2d_lds_bytes(a.M, (a.M + 15) / 16) <= 160 * 1024 - 64;
 }
 
 template <int MB, int SPW>
@@ -1260,7 +1297,7 @@ hipError_t launch_2d_norm_k(const GemmArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     configured = true;
   }
-  const size_t lds = std::max(gemm_2d_lds_bytes(a.M, MB), gemm_2d_norm_lds_bytes(a.M, a.K));
+  const size_t lds = gemm_2d_lds_bytes(a.M, MB);
   hipLaunchKernelGGL(kern, dim3(a.N / 32), dim3(kM16Waves * 64), lds, stream, a);
   return hipGetLastError();
 }
@@ -1438,20 +1475,24 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream, bool* quantized
     // Where the norm runs (every workgroup normalises the rows it stages, so
     // its vector work grows with the rows and the workgroups; measured on
     // MI355X, the chain at N 8192, K 1536 for B):
-    //   * M <= 4: in the M <= 16 kernel's BF16 staging (M = 1: 20.0 us for
-    //     the chain against 20.2 in the 2D kernel, 22.0 with a launch);
+    //   * M <= 4: in the M <= 16 kernel's BF16 staging (M = 1 / 2 / 4: 19.6 /
+    //     19.8 / 20.5 us for the chain against 19.9 / 20.2 / 20.7 in the 2D
+    //     kernel, 22.8 / 23.0 / 23.4 with a launch; 19.5 / 19.5 / 20.0
+    //     without the norm);
     //   * 5 <= M <= 16: in the 2D kernel's staging, two tiles per workgroup,
-    //     no K split (M = 8 / 12 / 16: 23.5 / 24.8 / 26.4 us against 24.0 /
-    //     26.5 / 28.3 in the M <= 16 kernel and 25.0 / 25.5 / 26.8 with a
+    //     no K split (M = 8 / 12 / 16: 22.8 / 24.2 / 25.2 us against 23.2 /
+    //     25.8 / 27.8 in the M <= 16 kernel and 24.9 / 25.6 / 26.0 with a
     //     launch);
     //   * above 16 rows, or where neither form takes the shape: RMSNorm +
     //     MXFP8 as its own launch, and the GEMM reads the codes (M = 32:
     //     32.3 us against 34.7 in the 2D kernel).
     // MXG_NORM_KERNEL=2d|m16|launch forces the form where it takes the shape
-    // (tests and sweeps).
+    // (tests and sweeps); m16lds forces the M <= 16 kernel's shared (NRM = 1)
+    // form where the per-wave one would run.
     const char* nk = std::getenv("MXG_NORM_KERNEL");
     const int nforce = !nk ? 0 : std::strcmp(nk, "2d") == 0 ? 1 : std::strcmp(nk, "m16") == 0 ? 2
-                                 : std::strcmp(nk, "launch") == 0 ? 3 : 0;
+                                 : std::strcmp(nk, "launch") == 0 ? 3
+                                 : std::strcmp(nk, "m16lds") == 0 ? 4 : 0;
     const bool norm2d = gemm_2d_norm_fits(a) && force != 1 && force != 3 &&
                         (nforce == 1 || (nforce == 0 && (force == 2 || (a.M > 4 && a.M <= 16))));
     if (norm2d) return launch_2d_norm(a, stream);
@@ -1464,7 +1505,8 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream, bool* quantized
     if (inline_ok) {
       GemmArgs b = a;
       b.rsplit = m16_row_split(a.N, a.K, true);
-      return launch_m16_norm(b, (S + NW - 1) / NW, (a.M * a.K / 32 + NT - 1) / NT, stream);
+      return launch_m16_norm(b, (S + NW - 1) / NW, (a.M * a.K / 32 + NT - 1) / NT, nforce == 4,
+                             stream);
     }
     hipError_t e = launch_rmsnorm_quantize(a.x, a.M, a.K, a.ld_x, a.norm_w, a.norm_eps, a.norm_y,
                                            a.K, a.a_q, a.a_s, 0, stream);

@@ -196,8 +196,8 @@ __global__ __launch_bounds__(WV * 64) void gemm_big_kernel(GemmArgs p) {
     const int m = 16 * mt + r;
     if (m < Mb) {
       uint2 o;
-      o.x = f32_to_bf16(acc[mt][0]) | (f32_to_bf16(acc[mt][1]) << 16);
-      o.y = f32_to_bf16(acc[mt][2]) | (f32_to_bf16(acc[mt][3]) << 16);
+      o.x = pk_bf16(acc[mt][0], acc[mt][1]);
+      o.y = pk_bf16(acc[mt][2], acc[mt][3]);
       *reinterpret_cast<uint2*>(p.out + (int64_t)(row0 + m) * N + n) = o;
     }
   }
@@ -387,8 +387,8 @@ __global__ __launch_bounds__(kWThreads) void gemm_wide_kernel(GemmArgs p) {
     const int m = 16 * mt + (l & 15), n = 16 * (NT * bx + t) + 4 * (l >> 4);
     if (m < Mb) {
       uint2 o;
-      o.x = f32_to_bf16(sum[0]) | (f32_to_bf16(sum[1]) << 16);
-      o.y = f32_to_bf16(sum[2]) | (f32_to_bf16(sum[3]) << 16);
+      o.x = pk_bf16(sum[0], sum[1]);
+      o.y = pk_bf16(sum[2], sum[3]);
       *reinterpret_cast<uint2*>(p.out + (int64_t)(row0 + m) * N + n) = o;
     }
   }

@@ -27,6 +27,39 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// Two FP32 values -> packed BF16 (lo in bits 0-15, hi in 16-31), round to
+// nearest, ties to even, in one instruction (v_cvt_pk_bf16_f32): for every
+// finite input the same bits as f32_to_bf16, and a NaN stays a NaN.
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  const v2f v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, v2bf16));
+}
+
+// Sum over a wave's 64 lanes, the same value in every lane, with no LDS
+// round trip: DPP adds within each row of 16 lanes with partners l ^ 1 and
+// l ^ 2 (quad permutes), then 7 - l and 15 - l within the half row and the
+// row (mirrors; after the steps before them these add the same values as
+// partners l ^ 4 and l ^ 8 would), then the four row sums, read from lanes
+// 0, 16, 32 and 48, added as (r0 + r1) + (r2 + r3).  All 64 lanes must be
+// active.
+template <int CTRL>
+__device__ __forceinline__ float add_dpp(float t) {
+  return t + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(t), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum(float t) {
+  t = add_dpp<0xB1>(t);    // quad_perm [1, 0, 3, 2]
+  t = add_dpp<0x4E>(t);    // quad_perm [2, 3, 0, 1]
+  t = add_dpp<0x141>(t);   // row_half_mirror
+  t = add_dpp<0x140>(t);   // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // Maximum over the 4 lanes of each aligned lane quad (DPP quad permutes:
 // no LDS round trip).
 __device__ __forceinline__ uint32_t quad_max(uint32_t a) {

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
         const uint32_t xu = (uint32_t)xv[i][k][h], wu = (uint32_t)wv[i][k][h];
         const float lo = (bf16_lo(xu) * r) * bf16_lo(wu);
         const float hi = (bf16_hi(xu) * r) * bf16_hi(wu);
-        yw[4 * k + h] = f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+        yw[4 * k + h] = pk_bf16(lo, hi);
       }
     uint32_t amax = 0;
 #pragma unroll

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_quant_kernel(RopeQuantArgs 
         const float x1 = bf16_lo((uint32_t)v[k]), x2 = bf16_hi((uint32_t)v[k]);
         const float y1 = x1 * c[k] - x2 * s[k];
         const float y2 = x2 * c[k] + x1 * s[k];
-        v[k] = (int)(f32_to_bf16(y1) | (f32_to_bf16(y2) << 16));
+        v[k] = (int)pk_bf16(y1, y2);
       }
     }
     uint32_t a = halves_max(bf16x2_absmax2(bf16x2_absmax2((uint32_t)v[0], (uint32_t)v[1]),

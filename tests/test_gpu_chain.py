@@ -185,21 +185,58 @@ def run_chain_norm(M, dims=None, seed=0):
     assert 1.0 - np.mean(gq == ref.b_q) < 0.02
 
 
-@pytest.mark.parametrize("form", [None, "2d", "m16", "launch"])
+@pytest.mark.parametrize("form", [None, "2d", "m16", "m16lds", "launch"])
 @pytest.mark.parametrize("M", [1, 5, 9, 16, 17, 32, 48])
 def test_chain_with_norm_small(M, form, chain_path, monkeypatch):
     # The norm inside B's staging on the 2D kernel (up to 32 rows) or on the
-    # M <= 16 kernel (up to 16), or as a launch of its own: routed, and each
-    # form forced (MXG_NORM_KERNEL; a form that does not take the shape
-    # leaves it to the next).
+    # M <= 16 kernel (up to 16; per-wave rows, or m16lds: the block sums
+    # through LDS), or as a launch of its own: routed, and each form forced
+    # (MXG_NORM_KERNEL; a form that does not take the shape leaves it to the
+    # next).
     if form:
         monkeypatch.setenv("MXG_NORM_KERNEL", form)
     run_chain_norm(M, dims=SMALL, seed=M)
 
 
-@pytest.mark.parametrize("form", [None, "2d", "m16"])
+@pytest.mark.parametrize("form", [None, "2d", "m16", "m16lds"])
 @pytest.mark.parametrize("M", [1, 8, 16, 32])
 def test_chain_with_norm_full_size(M, form, monkeypatch):
     if form:
         monkeypatch.setenv("MXG_NORM_KERNEL", form)
     run_chain_norm(M)
+
+
+# B's K above 2048 (more than 64 blocks a row): the M <= 16 kernel's norm
+# takes its LDS form (lanes add several blocks each).
+WIDE_B = {"A": (2560, 256), "B": (256, 2560), "C": (128, 256)}
+
+
+@pytest.mark.parametrize("form", [None, "m16"])
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_chain_with_norm_wide_k(M, form, monkeypatch):
+    if form:
+        monkeypatch.setenv("MXG_NORM_KERNEL", form)
+    run_chain_norm(M, dims=WIDE_B, seed=100 + M)
+
+
+@pytest.mark.parametrize("M", [1, 3, 8, 12, 16])
+def test_chain_norm_forms_bitwise(M, monkeypatch):
+    # The M <= 16 kernel's two norm forms add the same terms in the same
+    # order: the normalised row, its codes and B's output agree bit for bit.
+    case = synth.chain_case(M, seed=7)
+    nc = synth.rmsnorm_case(1, case["dims"]["B"][1], seed=8)
+    g, _ = _prep(case)
+    got = {}
+    for form in ("m16", "m16lds"):
+        monkeypatch.setenv("MXG_NORM_KERNEL", form)
+        say(f"chain+norm M={M} form={form}")
+        ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+        y = torch.empty(M, case["dims"]["B"][1], dtype=torch.bfloat16, device="cuda")
+        outs = mx.mxfp8_proj_chain(*g["x_a"], g["w_a"], g["w_b"], *g["x_c"], g["w_c"], workspace=ws,
+                                   norm_weight=dev_bf16(synth.bits(nc["w"])), norm_eps=nc["eps"],
+                                   b_bf16=y)
+        torch.cuda.synchronize()
+        got[form] = [host_bits(y)] + [host_u8(t) if t.dtype == torch.uint8 else host_bits(t)
+                                      for t in outs]
+    for a, b in zip(got["m16"], got["m16lds"]):
+        assert np.array_equal(a, b)
