@@ -59,8 +59,7 @@ __global__ __launch_bounds__(kNormThreads) void rmsnorm_quant_kernel(
         ss = ss + a * a;
         ss = ss + c * c;
       }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ss = ss + __shfl_xor(ss, o);
+  ss = wave_sum(ss);
   if (lane == 0) s_sum[wave] = ss;
   __syncthreads();
   float tot = s_sum[0];
