@@ -1533,7 +1533,24 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream, bool* quantized
     return launch_m16_half<true>(h, device_cus(), sf, (a.M * a.K / 32 + 1023) / 1024, stream);
   }
   if (force == 3) force = 0;                               // HALF does not take the shape
-  const Plan pl = choose_plan(a.M, a.N, a.K, a.group_tiles, device_cus());
+  Plan pl = choose_plan(a.M, a.N, a.K, a.group_tiles, device_cus());
+  // BF16 input, at most 12 weight steps (K <= 1536) and at least two weight
+  // tiles per CU: T = 2 or 4 tiles per workgroup in the 2D kernel, no K
+  // split, so that each CU quantizes the rows once instead of once per tile.
+  // Measured on MI355X (us, the M <= 16 kernel -> this plan): N 8192, K 1536
+  // (T = 2), M = 1 / 4 / 8 / 16: 4.87 / 4.91 / 5.08 / 5.97 -> 4.77 / 4.82 /
+  // 4.92 / 5.37; N 16384, K 1536 (T = 4), M = 1 / 4 / 8: 7.85 / 7.84 / 8.09
+  // -> 6.53 / 6.54 / 6.62.  With a longer K the M <= 16 kernel's weight
+  // stream wins (N 8192, K 4096, M = 1: 8.74 against 9.78 with T = 2).
+  {
+    const int tiles = a.N / 16, cus = device_cus();
+    const int T = tiles >= 4 * cus ? 4 : 2;
+    if (force == 0 && fq && a.M <= 16 && a.K <= 1536 && a.group_tiles == 0 && tiles >= 2 * cus &&
+        tiles % T == 0) {
+      pl = Plan{T, 1, S, round_slots((T * S + 15) / 16), 0.0};
+      force = 2;                                           // the 2D kernel below
+    }
+  }
   // One full-K tile per workgroup with the whole activation in LDS unless
   // the model gives a 2D plan at most 3/4 of its time: the M <= 16 kernel
   // keeps more loads in flight per CU (two workgroups share a CU when their
