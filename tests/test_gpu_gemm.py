@@ -92,6 +92,18 @@ def test_shapes(N, K, fused, path):
         run_case(M, N, K, seed=N + K, fused=fused)
 
 
+# BF16 input over short K with at least two weight tiles per CU: the 2D
+# kernel with two (N 8192) or four (N 16384) tiles per workgroup and no K
+# split; the M <= 16 kernel forced for comparison.
+@pytest.mark.parametrize("N,K", [(8192, 1536), (16384, 1536), (8192, 512)])
+@pytest.mark.parametrize("kernel", [None, "m16"])
+def test_bf16_short_k_many_tiles(N, K, kernel, monkeypatch):
+    if kernel:
+        monkeypatch.setenv("MXG_DIRECT_KERNEL", kernel)
+    for M in (1, 7, 16):
+        run_case(M, N, K, seed=N + K + M, fused=True)
+
+
 @pytest.mark.parametrize("M", [1, 16, 17, 48])
 @pytest.mark.parametrize("fused", [False, True])
 def test_largest_contraction(M, fused, path):
