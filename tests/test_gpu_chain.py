@@ -219,6 +219,18 @@ def test_chain_with_norm_wide_k(M, form, monkeypatch):
     run_chain_norm(M, dims=WIDE_B, seed=100 + M)
 
 
+# B's K at the per-wave forms' limit (64 blocks a row: every lane of a wave
+# holds a block) and one step above it (the M <= 16 kernel's LDS form; the
+# 2D form does not take it and leaves it to the next).
+@pytest.mark.parametrize("bk", [2048, 2176])
+@pytest.mark.parametrize("form", [None, "m16", "m16lds", "2d"])
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_chain_with_norm_k_boundary(M, form, bk, monkeypatch):
+    if form:
+        monkeypatch.setenv("MXG_NORM_KERNEL", form)
+    run_chain_norm(M, dims={"A": (bk, 256), "B": (256, bk), "C": (128, 256)}, seed=200 + M)
+
+
 @pytest.mark.parametrize("M", [1, 3, 8, 12, 16])
 def test_chain_norm_forms_bitwise(M, monkeypatch):
     # The M <= 16 kernel's two norm forms add the same terms in the same
