@@ -1098,18 +1098,25 @@ int round_slots(int spw) {
 
 // The time model of a plan: the busiest workgroup's bytes, weights at its
 // share of HBM bandwidth and activations at the rate one CU pulls them from
-// L2, plus the cross-workgroup sum of a K split.  Rates from measurements on
+// L2, plus the cross-workgroup sum of a K split: a fixed 1.2 us and the last
+// arriving workgroup's read of the other P - 1 parts' FP32 tiles (1 KiB per
+// weight tile and 16-row tile) at 60 GB/s.  Rates from measurements on
 // MI355X (about 6.5 TB/s of weights streamed chip-wide; about 46 GB/s of
-// activations into one CU while every CU reads the same lines).  T = P = 1
-// also models the M <= 16 kernel (one full-K tile per workgroup).
+// activations into one CU while every CU reads the same lines); the split's
+// terms were fitted to every plan timed at 17 / 24 / 32 / 48 rows on N x K =
+// 2048 x 5120, 4096 x 5120, 5120 x 8192 and 8192 x 1536, where the chosen
+// plan is then within 0.2 us of the fastest (a flat 1.5 us picked (4, 8) at
+// 2048 x 5120, up to 1.1 us slower than (2, 4)).  T = P = 1 also models the
+// M <= 16 kernel (one full-K tile per workgroup).
 double plan_cost(int M, int N, int K, int T, int P, int cus, int rb = 1) {
-  const int tiles = N / 16, S = K / 128;
+  const int tiles = N / 16, S = K / 128, MB = (M + 15) / 16;
   const int Sp = (S + P - 1) / P;
   const int groups = tiles / T, wgs = groups * P * rb;
   const int rounds = (wgs + cus - 1) / cus;
   const int active = wgs < cus ? wgs : cus;
   const double wb = (double)T * Sp * 2112.0, ab = (double)M * Sp * 132.0;
-  return rounds * (wb / (6.5e12 / active) + ab / 46e9) + (P > 1 ? 1.5e-6 : 0.0);
+  const double split = P > 1 ? 1.2e-6 + (double)(P - 1) * T * MB * 1024.0 / 60e9 : 0.0;
+  return rounds * (wb / (6.5e12 / active) + ab / 46e9) + split;
 }
 
 // The 2D plan of least modelled time.
