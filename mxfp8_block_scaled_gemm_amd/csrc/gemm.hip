@@ -1558,6 +1558,28 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream, bool* quantized
       force = 2;                                           // the 2D kernel below
     }
   }
+  // MXFP8 input, at most 16 rows, on at least two tiles per CU where the
+  // M <= 16 kernel's LDS (the whole activation) admits one workgroup per CU,
+  // so its tiles take a second round: the 2D kernel with one tile per
+  // workgroup and no K split
+  // stages the activation in 2048-column chunks, and two of its workgroups
+  // share a CU.  Measured on MI355X (N 8192, K 4096, M = 16): 9.66 us in the
+  // M <= 16 kernel, 9.00 in this plan (9.51 in the model's (2, 1)); at 8 and
+  // 12 rows, where two M <= 16 workgroups fit a CU, that kernel stays faster
+  // (7.97 / 8.15 against 8.43 / 8.61).
+  {
+    const int tiles = a.N / 16, cus = device_cus();
+    const size_t lds_cu = 160 * 1024;
+    if (force == 0 && !fq && a.M <= 16 && tiles >= 2 * cus &&
+        2 * gemm_m16_lds_bytes(a.M, a.K, 16) > lds_cu &&
+        2 * gemm_2d_lds_bytes(a.M, (a.M + 15) / 16) <= lds_cu) {
+      const int spw = round_slots((S + 15) / 16);
+      if (spw) {
+        pl = Plan{1, 1, S, spw, 0.0};
+        force = 2;
+      }
+    }
+  }
   // One full-K tile per workgroup with the whole activation in LDS unless
   // the model gives a 2D plan at most 3/4 of its time: the M <= 16 kernel
   // keeps more loads in flight per CU (two workgroups share a CU when their

@@ -104,6 +104,17 @@ def test_bf16_short_k_many_tiles(N, K, kernel, monkeypatch):
         run_case(M, N, K, seed=N + K + M, fused=True)
 
 
+# MXFP8 input on two tiles per CU where the M <= 16 kernel holds one
+# workgroup per CU (16 rows of K 4096): the 2D kernel, one tile per
+# workgroup; 12 rows stay on the M <= 16 kernel; both forced for comparison.
+@pytest.mark.parametrize("kernel", [None, "m16", "2d"])
+def test_two_tiles_per_cu_mxfp8(kernel, monkeypatch):
+    if kernel:
+        monkeypatch.setenv("MXG_DIRECT_KERNEL", kernel)
+    for M in (12, 16):
+        run_case(M, 8192, 4096, seed=M + 77, fused=False)
+
+
 @pytest.mark.parametrize("M", [1, 16, 17, 48])
 @pytest.mark.parametrize("fused", [False, True])
 def test_largest_contraction(M, fused, path):
