@@ -1037,7 +1037,7 @@ static hipError_t launch_m16_norm_ch(const GemmArgs& a, int ch, hipStream_t stre
   return hipErrorInvalidValue;
 }
 
-bool m16_norm_per_wave(int M, int K) { return K <= 2048 && M <= 2 * kNormWaves; }
+static bool m16_norm_per_wave(int M, int K) { return K <= 2048 && M <= 2 * kNormWaves; }
 
 static hipError_t launch_m16_norm(const GemmArgs& a, int spw, int ch, bool shared,
                                   hipStream_t stream) {
@@ -1561,12 +1561,11 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream, bool* quantized
   // MXFP8 input, at most 16 rows, on at least two tiles per CU where the
   // M <= 16 kernel's LDS (the whole activation) admits one workgroup per CU,
   // so its tiles take a second round: the 2D kernel with one tile per
-  // workgroup and no K split
-  // stages the activation in 2048-column chunks, and two of its workgroups
-  // share a CU.  Measured on MI355X (N 8192, K 4096, M = 16): 9.66 us in the
-  // M <= 16 kernel, 9.00 in this plan (9.51 in the model's (2, 1)); at 8 and
-  // 12 rows, where two M <= 16 workgroups fit a CU, that kernel stays faster
-  // (7.97 / 8.15 against 8.43 / 8.61).
+  // workgroup and no K split stages the activation in 2048-column chunks,
+  // and two of its workgroups share a CU.  Measured on MI355X (N 8192,
+  // K 4096, M = 16): 9.66 us in the M <= 16 kernel, 9.00 in this plan (9.51
+  // in the model's (2, 1)); at 8 and 12 rows, where two M <= 16 workgroups
+  // fit a CU, that kernel stays faster (7.97 / 8.15 against 8.43 / 8.61).
   {
     const int tiles = a.N / 16, cus = device_cus();
     const size_t lds_cu = 160 * 1024;
